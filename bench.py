@@ -1,0 +1,251 @@
+#!/usr/bin/env python3
+"""Benchmark of one optimizer step (Muon over every 2-D hidden weight + AdamW
+over the rest) on a transformer-shaped parameter set, on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--config llama_8b]
+
+A step is one mu_muon_step over the whole Muon list (momentum, normalisation,
+five Newton-Schulz steps, update) plus one mu_adamw_step over the whole AdamW
+list, with every input resident in HBM. W untimed steps, then K timed steps
+between two device synchronisations. Per-kernel durations come from HIP events
+the library records around each launch on its launch stream during the timed
+steps. Prints one JSON line.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "Muon step ms per param set; NS TFLOP/s (% MFMA peak); AdamW GB/s"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3        # MI355X fp32 matrix
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="llama_8b")
+    ap.add_argument("--ns-steps", type=int, default=5)
+    ap.add_argument("--precision", default="bf16", choices=["bf16", "f32"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="run a plain device copy of this many MiB first (counter calibration)")
+    return ap.parse_args()
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for f in ("ns_gemm.hip", "elementwise.hip", "common.hpp"):
+        with open(os.path.join(ROOT, "newton_schulz_orthogonalized_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(kernel: str):
+    """HBM bytes per launch from committed counter summaries, if they were taken
+    on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_llama_8b.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("source_digest") != source_digest():
+        return None
+    return d.get("bytes_per_launch")
+
+
+def build_set(ps, set_index, device, torch):
+    from workloads import device_normal, seed_for
+    dt = torch.bfloat16 if ps.dtype == "bf16" else torch.float32
+    mu = {"p": [], "g": [], "m": [], "heads": []}
+    for j, e in enumerate(ps.muon):
+        s = seed_for(set_index, j)
+        mu["p"].append(device_normal(e.shape, s, ps.weight_std, dt, device))
+        mu["g"].append(device_normal(e.shape, s + 500000, ps.grad_std, dt, device))
+        mu["m"].append(device_normal(e.shape, s + 900000, ps.mom_std, torch.float32, device))
+        mu["heads"].append(e.heads)
+    aw = {"p": [], "g": [], "m": [], "v": []}
+    for j, e in enumerate(ps.adamw):
+        s = seed_for(set_index, 100 + j)
+        aw["p"].append(device_normal(e.shape, s, ps.weight_std, dt, device))
+        aw["g"].append(device_normal(e.shape, s + 500000, ps.grad_std, dt, device))
+        aw["m"].append(torch.zeros(e.shape, dtype=torch.float32, device=device))
+        aw["v"].append(torch.zeros(e.shape, dtype=torch.float32, device=device))
+    return mu, aw
+
+
+def cpu_baseline(ps, set_index, ns_steps):
+    """The CPU oracle, as it stands, on a bounded sample of the same workload,
+    scaled to one whole parameter set by algorithmic work."""
+    import numpy as np
+    from oracle import muon_oracle as O
+    from workloads import host_normal
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([int(i.get("num_threads", 1)) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    # sample: the Muon matrices of layer 0 that the oracle finishes in seconds
+    # (the set's smallest distinct shapes, at most two) + 8M AdamW elements
+    shapes, picked = [], []
+    for e in ps.muon:
+        key = (e.shape, e.heads)
+        if key not in shapes:
+            shapes.append(key)
+            picked.append(e)
+    picked.sort(key=lambda e: e.shape[0] * e.shape[1] * min(e.shape) // e.heads)
+    picked = picked[:2]
+    from workloads import MuonEntry, ParamSet
+    sample = ParamSet("sample", [MuonEntry(e.name, e.shape, e.heads) for e in picked])
+    t_muon = 0.0
+    for k, e in enumerate(picked):
+        w = host_normal(e.shape, 777 + k, ps.weight_std)
+        g = host_normal(e.shape, 778 + k, ps.grad_std)
+        m = host_normal(e.shape, 779 + k, ps.mom_std)
+        t0 = time.perf_counter()
+        O.muon_step_ref(w, g, m, lr=0.02, weight_decay=0.01, heads=e.heads, coeffs=O.default_coeffs(ns_steps))
+        t_muon += time.perf_counter() - t0
+    n_aw = min(8 << 20, max(1, ps.adamw_elems()))
+    t_aw = 0.0
+    if ps.adamw:
+        p, g = host_normal(n_aw, 1, 0.02), host_normal(n_aw, 2, 1e-3)
+        z = np.zeros(n_aw)
+        t0 = time.perf_counter()
+        O.adamw_ref(p, g, z, z, lr=0.02, weight_decay=0.01, beta1=0.9, beta2=0.95, eps=1e-8, step=1)
+        t_aw = time.perf_counter() - t0
+    muon_scale = ps.ns_flops(ns_steps) / sample.ns_flops(ns_steps)
+    aw_scale = ps.adamw_elems() / n_aw if ps.adamw else 0.0
+    est_ms = 1e3 * (t_muon * muon_scale + t_aw * aw_scale)
+    desc = ", ".join(f"{e.shape[0]}x{e.shape[1]}" + (f"/{e.heads}h" if e.heads > 1 else "") for e in picked)
+    return {"value": est_ms, "unit": "ms", "cores": cores, "kind": "oracle",
+            "sample": (f"float64 numpy oracle on Muon matrices [{desc}] ({t_muon:.2f} s) scaled by Newton-Schulz "
+                       f"flops x{muon_scale:.1f}, plus AdamW on {n_aw} elements ({t_aw:.2f} s) scaled by "
+                       f"element count x{aw_scale:.1f}; measured {t_muon + t_aw:.1f} s of CPU work")}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; multi-GPU runs are not supported",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(2)
+    import newton_schulz_orthogonalized_amd as nso
+    from newton_schulz_orthogonalized_amd import _lib
+    from workloads import PARAM_SETS
+
+    device = torch.device("cuda", 0)
+    torch.cuda.set_device(device)
+    set_index = list(PARAM_SETS).index(args.config)
+    ps = PARAM_SETS[args.config]()
+    precision = args.precision if ps.dtype == "bf16" else "f32"
+    print(f"[bench] building {args.config}: {len(ps.muon)} Muon matrices ({ps.muon_elems()} elems), "
+          f"{len(ps.adamw)} AdamW tensors ({ps.adamw_elems()} elems)", file=sys.stderr, flush=True)
+    mu, aw = build_set(ps, set_index, device, torch)
+    ws_bytes = nso.muon_workspace_bytes(mu["p"], mu["g"], mu["m"], heads=mu["heads"], ns_steps=args.ns_steps,
+                                        precision=precision)
+    ws = _lib.workspace(ws_bytes, device)
+    aw_ws = _lib.workspace(_lib.mu_adamw_workspace_size(len(aw["p"])), device)
+    torch.cuda.synchronize()
+    print(f"[bench] workspace {ws_bytes / 2**30:.1f} GiB, allocated {torch.cuda.memory_allocated() / 2**30:.1f} GiB",
+          file=sys.stderr, flush=True)
+
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib << 20
+        a = torch.empty(n, dtype=torch.uint8, device=device)
+        b = torch.empty_like(a)
+        a.fill_(1)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    state = {"t": 0}
+
+    def step():
+        state["t"] += 1
+        nso.muon_step(mu["p"], mu["g"], mu["m"], lr=0.02, weight_decay=0.01, heads=mu["heads"],
+                      ns_steps=args.ns_steps, precision=precision, workspace=ws)
+        if aw["p"]:
+            nso.adamw_step(aw["p"], aw["g"], aw["m"], aw["v"], lr=0.02, weight_decay=0.01, beta1=0.9,
+                           beta2=0.95, eps=1e-8, step=state["t"], workspace=aw_ws)
+
+    for i in range(args.warmup):
+        step()
+        torch.cuda.synchronize()
+        print(f"[bench] warmup step {i + 1}/{args.warmup} done", file=sys.stderr, flush=True)
+
+    _lib.mu_profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    _lib.mu_profile_enable(False)
+    prof = {_lib.mu_kernel_name(k): _lib.mu_profile_read(k) for k in range(_lib.MU_K_COUNT)}
+    print(f"[bench] {args.steps} timed steps in {elapsed:.3f} s", file=sys.stderr, flush=True)
+
+    ms_step = 1e3 * elapsed / max(1, args.steps)
+    K = max(1, args.steps)
+    ns_ms = (prof["gram"]["ms"] + prof["gram2"]["ms"] + prof["apply"]["ms"]) / K
+    ns_flops = (prof["gram"]["flops"] + prof["gram2"]["flops"] + prof["apply"]["flops"]) / K
+    peak = PEAK_BF16_TFLOPS if precision == "bf16" else PEAK_F32_TFLOPS
+    ns_tflops = ns_flops / (ns_ms * 1e-3) / 1e12 if ns_ms > 0 else 0.0
+    adamw_gbs = prof["adamw"]["bytes"] / (prof["adamw"]["ms"] * 1e-3) / 1e9 if prof["adamw"]["ms"] > 0 else None
+    prep_gbs = prof["prep"]["bytes"] / (prof["prep"]["ms"] * 1e-3) / 1e9 if prof["prep"]["ms"] > 0 else None
+    kernels = {k: {"ms_per_launch": (v["ms"] / v["launches"]) if v["launches"] else None,
+                   "launches_per_step": v["launches"] / K, "ms_per_step": v["ms"] / K} for k, v in prof.items()}
+    # dominant kernel: the class with the most time
+    dom = max(("gram", "apply", "gram2", "prep", "adamw"), key=lambda k: prof[k]["ms"])
+    d = prof[dom]
+    if dom in ("gram", "apply", "gram2"):
+        achieved = d["flops"] / (d["ms"] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak}
+    else:
+        achieved = d["bytes"] / (d["ms"] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": achieved / PEAK_HBM_GBS}
+    roof["kernel"] = dom
+    roof["ms_per_launch"] = d["ms"] / max(1, d["launches"])
+    roof["traffic"] = traffic_from_profiles(dom)
+
+    out = {
+        "metric": METRIC, "value": ms_step, "unit": "ms", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": False, "scaling": "weak",
+        "vs_baseline": None, "dtype": precision, "data": "synthetic",
+        "config": {"workload": f"{args.config}: Muon over {len(ps.muon)} matrices ({ps.muon_elems()} elements), "
+                               f"AdamW over {len(ps.adamw)} tensors ({ps.adamw_elems()} elements)",
+                   "muon_matrices": len(ps.muon), "adamw_tensors": len(ps.adamw),
+                   "ns_steps": args.ns_steps, "ns_precision": precision, "parallelism": "single-gpu"},
+        "muon_ms_per_step": sum(prof[k]["ms"] for k in ("prep", "norm", "gram", "gram2", "apply", "finish")) / K,
+        "adamw_ms_per_step": prof["adamw"]["ms"] / K,
+        "ns_ms_per_step": ns_ms, "ns_tflops": ns_tflops, "ns_frac_peak": ns_tflops / peak,
+        "adamw_gbs": adamw_gbs, "adamw_frac_hbm": (adamw_gbs / PEAK_HBM_GBS) if adamw_gbs else None,
+        "prep_gbs": prep_gbs, "prep_frac_hbm": (prep_gbs / PEAK_HBM_GBS) if prep_gbs else None,
+        "kernels": kernels, "roofline": roof, "source_digest": source_digest(),
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(ps, set_index, args.ns_steps)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

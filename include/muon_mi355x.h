@@ -1,0 +1,205 @@
+/*
+ * muon_mi355x.h - C ABI of the MI355X (gfx950) Muon + AdamW optimizer step.
+ *
+ * The library updates optimizer state and parameters that the caller owns, on
+ * the caller's HIP stream, with hand-written CDNA4 kernels. It never allocates
+ * or frees device memory inside a step; scratch memory is a caller-provided
+ * workspace whose size the *_workspace_size queries return. The only memory it
+ * owns is a small pinned host staging area for the per-call descriptor tables
+ * (allocated on first use) and, while profiling is on, a pool of HIP events.
+ *
+ * Layout rules common to every entry point:
+ *   - every tensor is dense, row-major, with no padding between rows;
+ *   - parameter, gradient and state buffers of one entry must not overlap each
+ *     other or any other entry's buffers;
+ *   - bfloat16 buffers are 2-byte aligned, float32 buffers 4-byte aligned (16-
+ *     byte alignment and a column count divisible by 4 select the vector path);
+ *   - the workspace is 256-byte aligned.
+ * Every list is validated as a whole before the first HIP call: any error
+ * returns before anything is enqueued, so on error nothing has been modified.
+ * A device fault inside a kernel is asynchronous and surfaces at the caller's
+ * next synchronisation. Calls that share a workspace must not overlap in time.
+ * Streams are passed as void* and must be hipStream_t values (0 = null stream).
+ */
+#ifndef MUON_MI355X_H
+#define MUON_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MU_API_VERSION 1
+
+/* element types */
+#define MU_F32 0
+#define MU_BF16 1
+
+/* arithmetic of the Newton-Schulz products: float32 MFMA on float32 operands,
+ * or bfloat16 MFMA operands with float32 accumulation */
+#define MU_NS_F32 0
+#define MU_NS_BF16 1
+
+/* status codes */
+#define MU_OK 0
+#define MU_ERR_INVALID_ARG 1 /* null pointer, n < 0, bad size, heads do not divide rows, steps < 0, t < 1 */
+#define MU_ERR_DTYPE 2       /* unknown dtype or precision */
+#define MU_ERR_LAYOUT 3      /* misaligned buffer, or overlapping buffers */
+#define MU_ERR_WORKSPACE 4   /* workspace null, too small, or misaligned */
+#define MU_ERR_HIP 5         /* a HIP call failed; detail in mu_last_error() */
+
+/*
+ * One 2-D weight under the Muon rule.
+ *
+ * Muon step, four stages (MuonClip Optimizer page, sections "Momentum" and
+ * "Newton-Schulz Orthogonalization"; Qwen training-details page, "Confirmed",
+ * for per-head orthogonalisation):
+ *   M <- mu*M + (1-mu)*G;  U = nesterov ? (1-mu)*G + mu*M : M
+ *   for each head h (rows h*rows/num_heads ... (h+1)*rows/num_heads - 1):
+ *       X = U_h / (||U_h||_F + norm_eps), transposed when the block is taller
+ *       than wide; ns_steps times: X <- a_k X + b_k (X X^T) X + c_k (X X^T)^2 X
+ *   W <- W - lr*weight_decay*W - lr*scale*O       (O = X, untransposed)
+ *
+ * param    [rows, cols] dtype, updated in place (float32 math, bf16 stores
+ *          round to nearest even)
+ * grad     [rows, cols] same dtype as param, read only
+ * momentum [rows, cols] float32, updated in place
+ * num_heads >= 1 and divides rows; each head block is its own matrix
+ * scale    multiplies the direction in the update (the caller derives it from
+ *          the global matrix shape, as the NeMo AutoModel muown_triton page's
+ *          _finish contract says); 1.0 is plain Muon
+ * norm_out optional float32 [num_heads] device buffer receiving ||U_h||_F
+ * ortho_out optional float32 [rows, cols] device buffer receiving O (the
+ *          direction before lr and scale), for inspection; NULL to skip
+ */
+typedef struct mu_matrix {
+    void* param;
+    const void* grad;
+    float* momentum;
+    int64_t rows;
+    int64_t cols;
+    int32_t dtype;
+    int32_t num_heads;
+    float scale;
+    float* norm_out;
+    float* ortho_out;
+} mu_matrix;
+
+/*
+ * Hyper-parameters of one Muon call (one value for every matrix in the list).
+ * coeffs: host pointer to ns_steps rows of (a, b, c); NULL means the pages'
+ * cubic step (1.5, -0.5, 0) every time. ns_steps = 0 applies the normalised U.
+ */
+typedef struct mu_muon_hparams {
+    float lr;
+    float weight_decay;
+    float mu;
+    int32_t nesterov;
+    float norm_eps;
+    int32_t ns_steps;
+    const float* coeffs;
+    int32_t ns_precision;
+} mu_muon_hparams;
+
+/*
+ * Normalise + Newton-Schulz only, for one 2-D input (no momentum, no update):
+ * output = O computed from U = input exactly as in mu_muon_step. input and
+ * output share dtype and shape and must not overlap.
+ */
+typedef struct mu_ortho {
+    const void* input;
+    void* output;
+    int64_t rows;
+    int64_t cols;
+    int32_t dtype;
+    int32_t num_heads;
+    float* norm_out;
+} mu_ortho;
+
+/*
+ * One tensor under the AdamW rule (nanochat optimizer page, "Parameter
+ * Grouping Strategy" and "AdamW Step Implementation"; bias corrections are
+ * runtime scalars as on the NeMo AutoModel muown_triton page):
+ *   m <- b1 m + (1-b1) g;  v <- b2 v + (1-b2) g^2
+ *   p <- p - lr*wd*p - lr * (m/(1-b1^t)) / (sqrt(v/(1-b2^t)) + eps)
+ * param [numel] dtype, updated in place; grad [numel] same dtype, read only;
+ * exp_avg, exp_avg_sq [numel] float32, updated in place. lr and weight_decay
+ * are per tensor so parameter groups with different rates share one launch.
+ */
+typedef struct mu_tensor {
+    void* param;
+    const void* grad;
+    float* exp_avg;
+    float* exp_avg_sq;
+    int64_t numel;
+    int32_t dtype;
+    float lr;
+    float weight_decay;
+} mu_tensor;
+
+/* step is t >= 1, the number of this AdamW step */
+typedef struct mu_adamw_hparams {
+    float beta1;
+    float beta2;
+    float eps;
+    int64_t step;
+} mu_adamw_hparams;
+
+/* Workspace bytes mu_muon_step needs for this list (n == 0 gives 0). */
+int mu_muon_workspace_size(const mu_matrix* mats, int32_t n, const mu_muon_hparams* hp, size_t* bytes);
+
+/* One Muon step over the whole list, enqueued on `stream`. No host sync. */
+int mu_muon_step(const mu_matrix* mats, int32_t n, const mu_muon_hparams* hp,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes mu_muon_orthogonalize needs for this list. */
+int mu_ortho_workspace_size(const mu_ortho* xs, int32_t n, const mu_muon_hparams* hp, size_t* bytes);
+
+/* Normalise + orthogonalise each input into its output (lr, weight_decay, mu
+ * and nesterov of hp are ignored). */
+int mu_muon_orthogonalize(const mu_ortho* xs, int32_t n, const mu_muon_hparams* hp,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes mu_adamw_step needs for n tensors (its descriptor table). */
+int mu_adamw_workspace_size(int32_t n, size_t* bytes);
+
+/* One AdamW step over the whole list in a single launch. */
+int mu_adamw_step(const mu_tensor* ts, int32_t n, const mu_adamw_hparams* hp,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static text for a status code. */
+const char* mu_status_string(int status);
+
+/* Detail of the last error on this host thread ("" if none). */
+const char* mu_last_error(void);
+
+/* MU_API_VERSION of the built library. */
+int mu_version(void);
+
+/*
+ * Kernel timing with HIP events recorded around every launch on the launch
+ * stream. mu_profile_enable(1) clears the counters and starts recording;
+ * mu_profile_enable(0) stops. mu_profile_read synchronises on the recorded
+ * events and reports, for kernel class `kernel` (MU_K_*), the summed duration
+ * in milliseconds, the number of launches, and the algorithmic floating-point
+ * operations and bytes those launches were given.
+ */
+#define MU_K_PREP 0      /* momentum + Nesterov + U write + norm partials */
+#define MU_K_NORM 1      /* per-head norm finalisation */
+#define MU_K_GRAM 2      /* X X^T (upper tiles, mirrored) */
+#define MU_K_GRAM2 3     /* A A^T for the quintic term */
+#define MU_K_APPLY 4     /* a X + b A X (last step fuses the update) */
+#define MU_K_FINISH 5    /* update when ns_steps == 0 */
+#define MU_K_ADAMW 6     /* AdamW */
+#define MU_K_COUNT 7
+int mu_profile_enable(int on);
+int mu_profile_read(int kernel, double* total_ms, int64_t* launches, double* flops, double* bytes);
+const char* mu_kernel_name(int kernel);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MUON_MI355X_H */

@@ -1,0 +1,110 @@
+// Device-side helpers and the internal descriptors shared by the kernels and
+// the host launcher. gfx950 (CDNA4) only: 64-lane wavefronts, MFMA, 160 KB LDS.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mu {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+enum : int { DT_F32 = 0, DT_BF16 = 1 };
+
+// Pointers read from descriptor tables are generic; casting them to the global
+// address space lets the compiler emit global_load/global_store (vmcnt only)
+// instead of flat accesses that also hold lgkmcnt.
+#define MU_GLOBAL __attribute__((address_space(1)))
+template <typename T>
+__device__ __forceinline__ MU_GLOBAL T* gp(T* p) {
+    return (MU_GLOBAL T*)p;
+}
+
+// ---------------------------------------------------------------------------
+// One Newton-Schulz problem: a (matrix, head) block in the Muon step, or one
+// head of an input in the orthogonalise-only call.
+//
+// U-space is the head block as stored: hr rows x hc cols, row pitch ld. X-space
+// is the wide orientation the iteration runs in: m = min(hr, hc) rows and
+// n = max(hr, hc) cols, X = U when hr <= hc and X = U^T otherwise ("tall").
+// The workspace copies of X and of the Gram matrix are padded with zeros to
+// mp x np and mp x mp (multiples of the GEMM tile); zero padding is preserved
+// by every step, so the GEMM kernels need no bounds checks.
+// ---------------------------------------------------------------------------
+struct NsProb {
+    const void* src;   // gradient (step) or input (orthogonalise), U-space
+    float* mom;        // momentum, U-space (step only)
+    void* param;       // parameter, U-space (step only)
+    void* out;         // output, U-space (orthogonalise only)
+    int64_t ld;        // row pitch of src/mom/param/out in elements
+    int32_t hr, hc;    // U-space shape
+    int32_t m, n;      // X-space shape
+    int32_t mp, np;    // padded X-space shape
+    int32_t tall;      // X = U^T
+    int32_t vec;       // 16-byte vector path is legal for the U-space buffers
+    float scale;       // update scale
+    int32_t pad0;
+    void* x[2];        // ping-pong X buffers, mp x np, NS element type
+    void* a;           // Gram matrix, mp x mp
+    void* b;           // b*A + c*A^2 (quintic steps), mp x mp, or null
+    float* partials;   // per prep-tile sums of squares
+    float* fold;       // 1 / (||U||_F + eps), written by the norm kernel
+    float* norm_out;   // optional ||U||_F
+    float* oout;       // optional float32 copy of O in U-space (step only)
+    int32_t nparts;    // number of prep tiles = (mp/64) * (np/64)
+    int32_t pad1;
+};
+
+// Binary search: index p with prefix[p] <= t < prefix[p+1].
+__device__ inline int find_prob(const int* prefix, int nprobs, int t) {
+    int lo = 0, hi = nprobs - 1;
+    while (lo < hi) {
+        int mid = (lo + hi + 1) >> 1;
+        if (prefix[mid] <= t) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+// Map a workgroup id so that consecutive logical tiles land on the same XCD.
+// Workgroups are dispatched round-robin over the 8 XCDs; when the grid is a
+// multiple of 8, XCD x receives ids x, x+8, ... and is given the contiguous
+// logical block [x*G/8, (x+1)*G/8).
+__device__ inline int xcd_remap(int wg, int grid) {
+    if ((grid & 7) != 0) return wg;
+    return (wg & 7) * (grid >> 3) + (wg >> 3);
+}
+
+__device__ inline float bf2f(bf16 v) { return (float)v; }
+__device__ inline bf16 f2bf(float v) { return (bf16)v; }  // v_cvt_pk_bf16_f32, round to nearest even
+
+template <typename T> __device__ inline float to_f32(T v);
+template <> __device__ inline float to_f32<float>(float v) { return v; }
+template <> __device__ inline float to_f32<bf16>(bf16 v) { return (float)v; }
+template <typename T> __device__ inline T from_f32(float v);
+template <> __device__ inline float from_f32<float>(float v) { return v; }
+template <> __device__ inline bf16 from_f32<bf16>(float v) { return (bf16)v; }
+
+// Load/store an element of a buffer whose element type is chosen at run time.
+__device__ inline float load_dt(const void* p, int64_t i, int dt) {
+    return dt == DT_BF16 ? (float)((const bf16*)p)[i] : ((const float*)p)[i];
+}
+__device__ inline void store_dt(void* p, int64_t i, int dt, float v) {
+    if (dt == DT_BF16) ((bf16*)p)[i] = (bf16)v; else ((float*)p)[i] = v;
+}
+
+// Wavefront sum in a fixed order (butterfly over 64 lanes): every lane ends
+// with the same value, and the order does not depend on timing.
+__device__ inline float wave_sum(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+}  // namespace mu

@@ -1,0 +1,397 @@
+// HBM-bound kernels of the Muon step and the AdamW step (gfx950).
+//
+//  k_prep    momentum EMA + Nesterov blend, write U into the X workspace in the
+//            wide orientation (LDS-transposed for tall blocks) with zero
+//            padding, and one sum of squares per 64x64 tile (fixed order).
+//  k_norm    per (matrix, head): fixed-order sum of the tile partials,
+//            fold = 1/(||U||_F + eps).
+//  k_finish  ns_steps == 0: O = fold * X0, then the update (or the output).
+//  k_adamw   bias-corrected AdamW over a flat list of tensors, one launch.
+//
+// Momentum: MuonClip Optimizer page, section "Momentum" (EMA, decay 0.95).
+// Nesterov blend: named on the nanochat optimizer page ("Muon Step
+// Implementation") and as the nesterov flag of _prepare on the NeMo AutoModel
+// muown_triton page; the blend used is U = (1-mu) G + mu M_new.
+// AdamW: nanochat optimizer page, "AdamW Step Implementation" (exp_avg,
+// exp_avg_sq, step, lr, betas, eps, weight decay).
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace mu {
+
+namespace {
+
+constexpr int T = PREP_TILE;  // 64
+constexpr int NTHR = 256;
+
+// Four consecutive U-space elements (row r, cols c0..c0+3) of a buffer whose
+// element type is TS; out-of-range columns read as 0.
+template <typename TS>
+__device__ inline void load4(const void* base, int64_t off, int valid, bool vec, float v[4]) {
+    const TS* p = (const TS*)base + off;
+    if (vec && valid == 4) {
+        if constexpr (sizeof(TS) == 2) {
+            bf16x4 q = *(const bf16x4*)p;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = (float)q[e];
+        } else {
+            f32x4 q = *(const f32x4*)p;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = q[e];
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = e < valid ? to_f32<TS>(p[e]) : 0.f;
+    }
+}
+
+template <typename TS>
+__device__ inline void store4(void* base, int64_t off, int valid, bool vec, const float v[4]) {
+    TS* p = (TS*)base + off;
+    if (vec && valid == 4) {
+        if constexpr (sizeof(TS) == 2) {
+            bf16x4 q;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) q[e] = (bf16)v[e];
+            *(bf16x4*)p = q;
+        } else {
+            f32x4 q = {v[0], v[1], v[2], v[3]};
+            *(f32x4*)p = q;
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (e < valid) p[e] = from_f32<TS>(v[e]);
+    }
+}
+
+// Four consecutive X-space elements; the X workspace is always 4-aligned.
+template <typename TX>
+__device__ inline void store_x4(TX* p, const float v[4]) {
+    if constexpr (sizeof(TX) == 2) {
+        bf16x4 q;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) q[e] = (bf16)v[e];
+        *(bf16x4*)p = q;
+    } else {
+        f32x4 q = {v[0], v[1], v[2], v[3]};
+        *(f32x4*)p = q;
+    }
+}
+template <typename TX>
+__device__ inline void load_x4(const TX* p, float v[4]) {
+    if constexpr (sizeof(TX) == 2) {
+        bf16x4 q = *(const bf16x4*)p;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (float)q[e];
+    } else {
+        f32x4 q = *(const f32x4*)p;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = q[e];
+    }
+}
+
+// Block-wide fixed-order sum (four waves); result valid in every thread.
+__device__ inline float block_sum(float v, float* red) {
+    v = wave_sum(v);
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) red[w] = v;
+    __syncthreads();
+    float s = ((red[0] + red[1]) + red[2]) + red[3];
+    __syncthreads();
+    return s;
+}
+
+// U for four consecutive elements of one U-space row. Updates momentum.
+template <typename TS>
+__device__ inline void make_u(const NsProb& P, int r, int c0, bool with_m, bool nesterov, float mu,
+                              float u[4]) {
+    const int valid = (r < P.hr) ? max(0, min(4, P.hc - c0)) : 0;
+    if (valid == 0) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) u[e] = 0.f;
+        return;
+    }
+    const int64_t off = (int64_t)r * P.ld + c0;
+    const bool vec = P.vec != 0;
+    float g[4];
+    load4<TS>(P.src, off, valid, vec, g);
+    if (!with_m) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) u[e] = g[e];
+        return;
+    }
+    float m[4];
+    load4<float>(P.mom, off, valid, vec, m);
+    const float omm = 1.f - mu;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        m[e] = mu * m[e] + omm * g[e];
+        u[e] = nesterov ? omm * g[e] + mu * m[e] : m[e];
+    }
+    store4<float>(P.mom, off, valid, vec, m);
+}
+
+template <typename TS, typename TX>
+__global__ __launch_bounds__(NTHR) void k_prep(PrepArgs A) {
+    __shared__ float tile[T][T + 1];
+    __shared__ float red[4];
+    const int t = blockIdx.x;
+    const int p = find_prob(A.prefix, A.nprobs, t);
+    const NsProb& P = A.probs[p];
+    const int local = t - A.prefix[p];
+    const int tiles_n = P.np / T;
+    const int ti = local / tiles_n, tj = local - ti * tiles_n;
+    const int tid = threadIdx.x;
+    const int rr = tid >> 4, cc = (tid & 15) * 4;
+    const bool with_m = A.with_momentum != 0, nest = A.nesterov != 0;
+    TX* X = (TX*)P.x[0];
+    float ss = 0.f;
+    if (!P.tall) {
+        // X = U: X-space tile (ti, tj) is the U-space tile (ti, tj).
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int r = ti * T + rr + 16 * k, c0 = tj * T + cc;
+            float u[4];
+            make_u<TS>(P, r, c0, with_m, nest, A.mu, u);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ss += u[e] * u[e];
+            store_x4<TX>(X + (int64_t)r * P.np + c0, u);
+        }
+    } else {
+        // X = U^T: X-space tile (ti, tj) is U-space tile (tj, ti), transposed in LDS.
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int r = tj * T + rr + 16 * k, c0 = ti * T + cc;
+            float u[4];
+            make_u<TS>(P, r, c0, with_m, nest, A.mu, u);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                ss += u[e] * u[e];
+                tile[rr + 16 * k][cc + e] = u[e];
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int a = rr + 16 * k;
+            float v[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = tile[cc + e][a];
+            store_x4<TX>(X + (int64_t)(ti * T + a) * P.np + tj * T + cc, v);
+        }
+    }
+    const float s = block_sum(ss, red);
+    if (tid == 0) P.partials[local] = s;
+}
+
+__global__ __launch_bounds__(NTHR) void k_norm(NormArgs A) {
+    __shared__ float red[4];
+    const NsProb& P = A.probs[blockIdx.x];
+    float s = 0.f;
+    for (int i = threadIdx.x; i < P.nparts; i += NTHR) s += P.partials[i];
+    s = block_sum(s, red);
+    if (threadIdx.x == 0) {
+        const float nrm = sqrtf(s);
+        P.fold[0] = 1.f / (nrm + A.eps);
+        if (P.norm_out) P.norm_out[0] = nrm;
+    }
+}
+
+// O = fold * X0 written back in U-space: update (W - lr*wd*W - lr*scale*O) or output.
+template <typename TS, typename TX>
+__global__ __launch_bounds__(NTHR) void k_finish(FinishArgs A) {
+    __shared__ float tile[T][T + 1];
+    const int t = blockIdx.x;
+    const int p = find_prob(A.prefix, A.nprobs, t);
+    const NsProb& P = A.probs[p];
+    const int local = t - A.prefix[p];
+    const int tiles_n = P.np / T;
+    const int ti = local / tiles_n, tj = local - ti * tiles_n;
+    const int tid = threadIdx.x;
+    const int rr = tid >> 4, cc = (tid & 15) * 4;
+    const float f = P.fold[0];
+    const TX* X = (const TX*)P.x[0];
+    const bool vec = P.vec != 0;
+    auto emit = [&](int r, int c0, const float o[4]) {
+        const int valid = (r < P.hr) ? max(0, min(4, P.hc - c0)) : 0;
+        if (valid == 0) return;
+        const int64_t off = (int64_t)r * P.ld + c0;
+        if (P.oout) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (e < valid) P.oout[off + e] = o[e];
+        }
+        float w[4];
+        if (A.with_update) {
+            load4<TS>(P.param, off, valid, vec, w);
+            const float decay = A.lr * A.wd, step = A.lr * P.scale;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) w[e] = (w[e] - decay * w[e]) - step * o[e];
+            store4<TS>(P.param, off, valid, vec, w);
+        } else {
+            store4<TS>(P.out, off, valid, vec, o);
+        }
+    };
+    if (!P.tall) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int r = ti * T + rr + 16 * k, c0 = tj * T + cc;
+            float o[4];
+            load_x4<TX>(X + (int64_t)r * P.np + c0, o);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] *= f;
+            emit(r, c0, o);
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int a = rr + 16 * k;
+            float v[4];
+            load_x4<TX>(X + (int64_t)(ti * T + a) * P.np + tj * T + cc, v);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) tile[cc + e][a] = v[e] * f;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int r = tj * T + rr + 16 * k, c0 = ti * T + cc;
+            float o[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = tile[rr + 16 * k][cc + e];
+            emit(r, c0, o);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// AdamW. Workgroup c handles elements [k*CHUNK, (k+1)*CHUNK) of tensor i where
+// prefix[i] <= c < prefix[i+1] and k = c - prefix[i]. Each thread handles two
+// groups of 8 consecutive elements (16-byte bf16 / 32-byte fp32 accesses).
+// ---------------------------------------------------------------------------
+template <typename TP>
+__device__ inline void adamw8(const AdamWDesc& D, int64_t i0, int cnt, const AdamWArgs& A) {
+    TP* p = (TP*)D.param + i0;
+    const TP* g = (const TP*)D.grad + i0;
+    float* m = D.m + i0;
+    float* v = D.v + i0;
+    float pv[8], gv[8], mv[8], vv[8];
+    const bool full = (cnt == 8) && D.vec;
+    if (full) {
+        if constexpr (sizeof(TP) == 2) {
+            bf16x8 a = *(const bf16x8*)p, b = *(const bf16x8*)g;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) { pv[e] = (float)a[e]; gv[e] = (float)b[e]; }
+        } else {
+            f32x4 a0 = ((const f32x4*)p)[0], a1 = ((const f32x4*)p)[1];
+            f32x4 b0 = ((const f32x4*)g)[0], b1 = ((const f32x4*)g)[1];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { pv[e] = a0[e]; pv[e + 4] = a1[e]; gv[e] = b0[e]; gv[e + 4] = b1[e]; }
+        }
+        f32x4 m0 = ((const f32x4*)m)[0], m1 = ((const f32x4*)m)[1];
+        f32x4 v0 = ((const f32x4*)v)[0], v1 = ((const f32x4*)v)[1];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { mv[e] = m0[e]; mv[e + 4] = m1[e]; vv[e] = v0[e]; vv[e + 4] = v1[e]; }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            if (e < cnt) { pv[e] = to_f32<TP>(p[e]); gv[e] = to_f32<TP>(g[e]); mv[e] = m[e]; vv[e] = v[e]; }
+            else { pv[e] = gv[e] = mv[e] = vv[e] = 0.f; }
+        }
+    }
+    const float b1 = A.beta1, b2 = A.beta2, omb1 = 1.f - b1, omb2 = 1.f - b2;
+    const float decay = D.lr * D.wd;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        mv[e] = b1 * mv[e] + omb1 * gv[e];
+        vv[e] = b2 * vv[e] + omb2 * gv[e] * gv[e];
+        const float mhat = mv[e] / A.bc1;
+        const float vhat = vv[e] / A.bc2;
+        pv[e] = (pv[e] - decay * pv[e]) - D.lr * mhat / (sqrtf(vhat) + A.eps);
+    }
+    if (full) {
+        if constexpr (sizeof(TP) == 2) {
+            bf16x8 a;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) a[e] = (bf16)pv[e];
+            *(bf16x8*)p = a;
+        } else {
+            ((f32x4*)p)[0] = f32x4{pv[0], pv[1], pv[2], pv[3]};
+            ((f32x4*)p)[1] = f32x4{pv[4], pv[5], pv[6], pv[7]};
+        }
+        ((f32x4*)m)[0] = f32x4{mv[0], mv[1], mv[2], mv[3]};
+        ((f32x4*)m)[1] = f32x4{mv[4], mv[5], mv[6], mv[7]};
+        ((f32x4*)v)[0] = f32x4{vv[0], vv[1], vv[2], vv[3]};
+        ((f32x4*)v)[1] = f32x4{vv[4], vv[5], vv[6], vv[7]};
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            if (e < cnt) { p[e] = from_f32<TP>(pv[e]); m[e] = mv[e]; v[e] = vv[e]; }
+    }
+}
+
+__device__ inline int find_tensor(const int64_t* prefix, int n, int64_t c) {
+    int lo = 0, hi = n - 1;
+    while (lo < hi) {
+        int mid = (lo + hi + 1) >> 1;
+        if (prefix[mid] <= c) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+__global__ __launch_bounds__(NTHR) void k_adamw(AdamWArgs A) {
+    const int64_t c = blockIdx.x;
+    const int i = find_tensor(A.prefix, A.n, c);
+    const AdamWDesc& D = A.descs[i];
+    const int64_t base = (c - A.prefix[i]) * ADAMW_CHUNK;
+#pragma unroll
+    for (int pass = 0; pass < ADAMW_CHUNK / (NTHR * 8); ++pass) {
+        const int64_t i0 = base + (int64_t)pass * NTHR * 8 + threadIdx.x * 8;
+        if (i0 >= D.numel) break;
+        const int cnt = (int)min<int64_t>(8, D.numel - i0);
+        if (D.dtype == DT_BF16) adamw8<bf16>(D, i0, cnt, A);
+        else adamw8<float>(D, i0, cnt, A);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_prep(const PrepArgs& a, hipStream_t s) {
+    if (a.total_tiles <= 0) return hipSuccess;
+    dim3 grid(a.total_tiles), block(NTHR);
+    if (a.src_dtype == DT_BF16) {
+        if (a.ns_dtype == DT_BF16) hipLaunchKernelGGL((k_prep<bf16, bf16>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((k_prep<bf16, float>), grid, block, 0, s, a);
+    } else {
+        if (a.ns_dtype == DT_BF16) hipLaunchKernelGGL((k_prep<float, bf16>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((k_prep<float, float>), grid, block, 0, s, a);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_norm(const NormArgs& a, hipStream_t s) {
+    if (a.nprobs <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_norm, dim3(a.nprobs), dim3(NTHR), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_finish(const FinishArgs& a, hipStream_t s) {
+    if (a.total_tiles <= 0) return hipSuccess;
+    dim3 grid(a.total_tiles), block(NTHR);
+    if (a.src_dtype == DT_BF16) {
+        if (a.ns_dtype == DT_BF16) hipLaunchKernelGGL((k_finish<bf16, bf16>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((k_finish<bf16, float>), grid, block, 0, s, a);
+    } else {
+        if (a.ns_dtype == DT_BF16) hipLaunchKernelGGL((k_finish<float, bf16>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((k_finish<float, float>), grid, block, 0, s, a);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_adamw(const AdamWArgs& a, hipStream_t s) {
+    if (a.total_chunks <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_adamw, dim3((unsigned)a.total_chunks), dim3(NTHR), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace mu

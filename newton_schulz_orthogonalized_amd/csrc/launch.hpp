@@ -1,0 +1,92 @@
+// Host-side launch interface between the C-ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.hpp"
+
+namespace mu {
+
+// Prep tile edge (elements) of the momentum / transpose kernel.
+constexpr int PREP_TILE = 64;
+
+struct PrepArgs {
+    const NsProb* probs;
+    const int* prefix;   // nprobs+1 cumulative prep tiles
+    int nprobs;
+    int total_tiles;
+    int src_dtype;       // element type of src/param/out
+    int ns_dtype;        // element type of the X buffers
+    int with_momentum;   // 1: Muon step, 0: orthogonalise-only (U = src)
+    int nesterov;
+    float mu;
+};
+hipError_t launch_prep(const PrepArgs& a, hipStream_t s);
+
+struct NormArgs {
+    const NsProb* probs;
+    int nprobs;
+    float eps;
+};
+hipError_t launch_norm(const NormArgs& a, hipStream_t s);
+
+enum GemmMode : int {
+    GM_GRAM = 0,        // A = f^2 * X X^T          (upper tiles, mirrored store)
+    GM_GRAM2 = 1,       // B = b*A + c*A A^T        (upper tiles, mirrored store)
+    GM_APPLY = 2,       // X' = f*(a*X + b*A X)  or  f*(a*X + B X)
+    GM_APPLY_LAST = 3,  // as GM_APPLY, result O goes to the update or to `out`
+};
+
+struct GemmArgs {
+    const NsProb* probs;
+    const int* prefix;   // nprobs+1 cumulative tiles for this mode
+    int nprobs;
+    int total_tiles;
+    int mode;
+    int src;             // which x[] buffer holds the current X
+    int first;           // apply the fold (1/||U||) of the first step
+    int use_b;           // apply multiplies by B (quintic) instead of A
+    int with_update;     // last step: 1 updates param, 0 writes out
+    int src_dtype;       // element type of param/out
+    float ca, cb, cc;    // step coefficients
+    float lr, wd;
+};
+// tile: 256 or 128 (square tiles, bf16) ; float32 uses 64.
+hipError_t launch_gemm_bf16(const GemmArgs& a, int tile, hipStream_t s);
+hipError_t launch_gemm_f32(const GemmArgs& a, hipStream_t s);
+
+struct FinishArgs {      // ns_steps == 0: O = fold * X0
+    const NsProb* probs;
+    const int* prefix;   // prep-tile prefix
+    int nprobs;
+    int total_tiles;
+    int ns_dtype;
+    int src_dtype;
+    int with_update;
+    float lr, wd;
+};
+hipError_t launch_finish(const FinishArgs& a, hipStream_t s);
+
+struct AdamWDesc {
+    void* param;
+    const void* grad;
+    float* m;
+    float* v;
+    int64_t numel;
+    int32_t dtype;
+    int32_t vec;         // 16-byte aligned bases: vector path
+    float lr, wd;
+};
+struct AdamWArgs {
+    const AdamWDesc* descs;
+    const int64_t* prefix;  // n+1 cumulative chunks
+    int n;
+    int64_t total_chunks;
+    float beta1, beta2, eps;
+    float bc1, bc2;         // 1 - beta^t
+};
+constexpr int ADAMW_CHUNK = 4096;  // elements per workgroup
+hipError_t launch_adamw(const AdamWArgs& a, hipStream_t s);
+
+}  // namespace mu

@@ -1,0 +1,132 @@
+"""The C-ABI library loads on a machine without a GPU, exports every symbol the
+header declares, and rejects bad arguments before any HIP call (status codes
+only; nothing here enqueues work or touches device memory)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "muon_mi355x.h")
+LIB = os.path.join(ROOT, "newton_schulz_orthogonalized_amd", "libmuon_mi355x.so")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(mu_\w+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libmuon_mi355x.so is not built (run __graft_entry__.build())")
+    from newton_schulz_orthogonalized_amd import _lib
+    return _lib
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for n in ("mu_muon_workspace_size", "mu_muon_step", "mu_muon_orthogonalize", "mu_ortho_workspace_size",
+              "mu_adamw_workspace_size", "mu_adamw_step", "mu_status_string", "mu_last_error", "mu_version"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    raw = ctypes.CDLL(LIB)
+    for n in _declared():
+        assert hasattr(raw, n), n
+    assert set(lib.EXPORTED) == set(_declared())
+
+
+def test_version_and_status_strings(lib):
+    assert lib.mu_version() == 1
+    assert lib.mu_status_string(0) == "ok"
+    assert "workspace" in lib.mu_status_string(lib.MU_ERR_WORKSPACE)
+    assert lib.mu_status_string(99) == "unknown status"
+
+
+# Fake, never-dereferenced device addresses: validation must reject these
+# calls before any HIP call is made.
+A = 0x7f0000000000
+
+
+def _mat(lib, **kw):
+    d = dict(param=A, grad=A + (1 << 24), momentum=A + (2 << 24), rows=64, cols=32, dtype=lib.MU_F32,
+             num_heads=1, scale=1.0, norm_out=None, ortho_out=None)
+    d.update(kw)
+    return lib.MuMatrix(**d)
+
+
+def _hp(lib, **kw):
+    d = dict(lr=0.02, weight_decay=0.01, mu=0.95, nesterov=1, norm_eps=1e-7, ns_steps=5, coeffs=None,
+             ns_precision=lib.MU_NS_BF16)
+    d.update(kw)
+    return lib.MuMuonHparams(**d)
+
+
+def _step(lib, mats, hp, ws=None, nbytes=0):
+    arr = (lib.MuMatrix * len(mats))(*mats)
+    return lib.LIB.mu_muon_step(arr, len(mats), ctypes.byref(hp), ws, nbytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(num_heads=3), 1), (dict(num_heads=0), 1), (dict(rows=0), 1), (dict(cols=-4), 1),
+    (dict(param=None), 1), (dict(dtype=7), 2), (dict(grad=A + 1), 3),
+])
+def test_bad_matrix_rejected(lib, kw, code):
+    assert _step(lib, [_mat(lib, **kw)], _hp(lib)) == code
+    assert lib.mu_last_error() != ""
+
+
+def test_bad_hparams_rejected(lib):
+    assert _step(lib, [_mat(lib)], _hp(lib, ns_steps=-1)) == lib.MU_ERR_INVALID_ARG
+    assert _step(lib, [_mat(lib)], _hp(lib, ns_precision=9)) == lib.MU_ERR_DTYPE
+    assert _step(lib, [_mat(lib)], _hp(lib, lr=float("nan"))) == lib.MU_ERR_INVALID_ARG
+
+
+def test_overlap_and_mixed_dtype_rejected(lib):
+    assert _step(lib, [_mat(lib, grad=A + 100)], _hp(lib)) == lib.MU_ERR_LAYOUT
+    m2 = _mat(lib, param=A + (3 << 24), grad=A + (4 << 24), momentum=A + (5 << 24), dtype=lib.MU_BF16)
+    assert _step(lib, [_mat(lib), m2], _hp(lib)) == lib.MU_ERR_DTYPE
+
+
+def test_workspace_checks(lib):
+    need = ctypes.c_size_t(0)
+    arr = (lib.MuMatrix * 1)(_mat(lib))
+    assert lib.LIB.mu_muon_workspace_size(arr, 1, ctypes.byref(_hp(lib)), ctypes.byref(need)) == 0
+    # 64x32 float32 -> X is 32x64, 128-tiles on the bf16 path: 2 x 128x128 x 2 B + 128x128 x 2 B + tables
+    assert need.value >= 3 * 128 * 128 * 2
+    assert _step(lib, [_mat(lib)], _hp(lib)) == lib.MU_ERR_WORKSPACE
+    assert _step(lib, [_mat(lib)], _hp(lib), ws=A + (9 << 24), nbytes=need.value - 1) == lib.MU_ERR_WORKSPACE
+    assert _step(lib, [_mat(lib)], _hp(lib), ws=A + (9 << 24) + 16, nbytes=need.value) == lib.MU_ERR_WORKSPACE
+
+
+def test_empty_list_is_ok_without_device(lib):
+    arr = (lib.MuMatrix * 1)()
+    assert lib.LIB.mu_muon_step(arr, 0, ctypes.byref(_hp(lib)), None, 0, None) == 0
+    need = ctypes.c_size_t(123)
+    assert lib.LIB.mu_muon_workspace_size(arr, 0, ctypes.byref(_hp(lib)), ctypes.byref(need)) == 0
+    assert need.value == 0
+
+
+def test_adamw_validation(lib):
+    t = lib.MuTensor(A, A + (1 << 24), A + (2 << 24), A + (3 << 24), 100, lib.MU_F32, 0.1, 0.0)
+    arr = (lib.MuTensor * 1)(t)
+    for hp, code in [((0.9, 0.95, 1e-8, 0), 1), ((1.0, 0.95, 1e-8, 1), 1), ((0.9, 0.95, float("inf"), 1), 1)]:
+        h = lib.MuAdamwHparams(*hp)
+        assert lib.LIB.mu_adamw_step(arr, 1, ctypes.byref(h), None, 0, None) == code
+    h = lib.MuAdamwHparams(0.9, 0.95, 1e-8, 1)
+    assert lib.LIB.mu_adamw_step(arr, 1, ctypes.byref(h), None, 0, None) == lib.MU_ERR_WORKSPACE
+    bad = (lib.MuTensor * 1)(lib.MuTensor(A, A + 2, A + (2 << 24), A + (3 << 24), 100, lib.MU_F32, 0.1, 0.0))
+    assert lib.LIB.mu_adamw_step(bad, 1, ctypes.byref(h), None, 0, None) == lib.MU_ERR_LAYOUT
+
+
+def test_ortho_validation(lib):
+    x = lib.MuOrtho(A, A + (1 << 24), 10, 20, lib.MU_BF16, 3, None)
+    arr = (lib.MuOrtho * 1)(x)
+    assert lib.LIB.mu_muon_orthogonalize(arr, 1, ctypes.byref(_hp(lib)), None, 0, None) == lib.MU_ERR_INVALID_ARG
+    x = lib.MuOrtho(A, A, 10, 20, lib.MU_BF16, 1, None)
+    arr = (lib.MuOrtho * 1)(x)
+    assert lib.LIB.mu_muon_orthogonalize(arr, 1, ctypes.byref(_hp(lib)), None, 0, None) == lib.MU_ERR_LAYOUT

@@ -1,0 +1,95 @@
+"""GPU parity of the multi-tensor AdamW step against the CPU oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import bf16_ulp, need_gpu, to_np
+from oracle import muon_oracle as O
+from workloads import as_dtype, host_normal
+
+pytestmark = pytest.mark.gpu
+
+SIZES = [1, 7, 8, 9, 4095, 4096, 4097, 10000, 70001]
+
+
+def f32(x):
+    return float(np.float32(x))
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    need_gpu()
+    yield
+
+
+def _case(dtype, step, seed, random_state):
+    import newton_schulz_orthogonalized_amd as nso
+    ps, gs, ms, vs, ref_in = [], [], [], [], []
+    lrs = [0.02 * (1 + i % 3) for i in range(len(SIZES))]
+    wds = [0.01 * (i % 2) for i in range(len(SIZES))]
+    for i, n in enumerate(SIZES):
+        p = as_dtype(host_normal(n, seed + 10 * i, 0.5), dtype)
+        g = as_dtype(host_normal(n, seed + 10 * i + 1, 1e-2), dtype)
+        if random_state:
+            m = as_dtype(host_normal(n, seed + 10 * i + 2, 1e-2), torch.float32)
+            v = as_dtype(host_normal(n, seed + 10 * i + 3, 1e-2) ** 2, torch.float32)
+        else:
+            m = torch.zeros(n)
+            v = torch.zeros(n)
+        ref_in.append((to_np(p), to_np(g), to_np(m), to_np(v)))
+        ps.append(p.cuda()); gs.append(g.cuda()); ms.append(m.cuda()); vs.append(v.cuda())
+    nso.adamw_step(ps, gs, ms, vs, lr=lrs, weight_decay=wds, beta1=0.9, beta2=0.95, eps=1e-8, step=step)
+    torch.cuda.synchronize()
+    for i in range(len(SIZES)):
+        p0, g0, m0, v0 = ref_in[i]
+        # the C ABI takes float32 hyper-parameters: give the oracle those same values
+        pr, mr, vr = O.adamw_ref(p0, g0, m0, v0, lr=f32(lrs[i]), weight_decay=f32(wds[i]), beta1=f32(0.9),
+                                 beta2=f32(0.95), eps=f32(1e-8), step=step)
+        yield i, to_np(ps[i]), to_np(ms[i]), to_np(vs[i]), pr, mr, vr, (p0, g0, m0, v0)
+
+
+U32 = 2.0 ** -24  # float32 unit roundoff
+
+
+def check_states(m, v, mr, vr, ins):
+    """Moments against the oracle: relative Frobenius error 1e-6, and per element
+    within a few float32 roundings of the operands of each update."""
+    p0, g0, m0, v0 = ins
+    assert O.rel_fro(m, mr) <= 1e-6
+    assert O.rel_fro(v, vr) <= 1e-6
+    assert np.all(np.abs(m - mr) <= 4 * U32 * (0.9 * np.abs(m0) + 0.1 * np.abs(g0)) + 1e-30)
+    assert np.all(np.abs(v - vr) <= 6 * U32 * (0.95 * np.abs(v0) + 0.05 * g0 * g0) + 1e-30)
+
+
+@pytest.mark.parametrize("step,random_state", [(1, False), (10, True), (1000, True)])
+def test_adamw_f32(step, random_state):
+    for i, p, m, v, pr, mr, vr, ins in _case(torch.float32, step, 20000 + step, random_state):
+        check_states(m, v, mr, vr, ins)
+        # the step p - p0 is lr-sized; compare it, not p, so the check has teeth
+        p0 = ins[0]
+        assert O.rel_fro(p - p0, pr - p0) <= 1e-4, i
+
+
+@pytest.mark.parametrize("step,random_state", [(1, False), (10, True)])
+def test_adamw_bf16(step, random_state):
+    for i, p, m, v, pr, mr, vr, ins in _case(torch.bfloat16, step, 21000 + step, random_state):
+        check_states(m, v, mr, vr, ins)
+        # the kernel rounds its float32 result once: within one bf16 ulp of the exact value
+        assert np.all(np.abs(p - pr) <= bf16_ulp(pr) * 1.0 + 1e-30), i
+
+
+def test_adamw_empty_tensor_and_list():
+    import newton_schulz_orthogonalized_amd as nso
+    nso.adamw_step([], [], [], [], lr=0.1, weight_decay=0.0)
+    z = torch.zeros(0, device="cuda")
+    nso.adamw_step([z], [z.clone()], [z.clone()], [z.clone()], lr=0.1, weight_decay=0.0, step=1)
+
+
+def test_adamw_rejects_step_zero():
+    import newton_schulz_orthogonalized_amd as nso
+    from newton_schulz_orthogonalized_amd import _lib
+    p = torch.ones(10, device="cuda")
+    with pytest.raises(_lib.MuonError):
+        nso.adamw_step([p], [p.clone()], [p.clone()], [p.clone()], lr=0.1, weight_decay=0.0, step=0)
+    assert torch.all(p == 1)

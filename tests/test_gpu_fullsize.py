@@ -1,0 +1,100 @@
+"""Full-size parity: each transformer-shaped parameter set runs as one Muon call
+and one AdamW call over the whole set (the launch configuration bench.py
+times), and sampled matrices / tensor slices are compared with the CPU oracle.
+O of the sampled matrices comes from the step's optional float32 ortho_out.
+"""
+
+import gc
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import need_gpu, to_np
+from oracle import muon_oracle as O
+from workloads import PARAM_SETS, device_normal, seed_for
+
+pytestmark = pytest.mark.gpu
+
+BF16_TOL = 2e-2
+MOM_TOL = 1e-6
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    need_gpu()
+    yield
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+SAMPLES = {
+    "gpt2_small": ["h0.attn.c_attn", "h0.attn.c_proj", "h5.mlp.c_fc", "h11.mlp.c_proj"],
+    "per_head_wq": ["l0.wq", "l23.wq"],
+    "llama_1b": ["l0.wk", "l23.up", "l11.down"],
+    "llama_8b": ["l0.wk", "l0.wq", "l31.gate"],
+}
+
+
+@pytest.mark.parametrize("set_name", ["gpt2_small", "per_head_wq", "llama_1b", "llama_8b"])
+def test_full_set_muon_step(set_name):
+    import newton_schulz_orthogonalized_amd as nso
+    idx = list(PARAM_SETS).index(set_name)
+    ps = PARAM_SETS[set_name]()
+    print(f"[fullsize muon] {set_name}: {len(ps.muon)} matrices, {ps.muon_elems()} elements", flush=True)
+    dt = torch.bfloat16
+    ws, gs, ms, oo, keep = [], [], [], [], {}
+    for j, e in enumerate(ps.muon):
+        s = seed_for(idx, j)
+        w = device_normal(e.shape, s, ps.weight_std, dt, "cuda")
+        g = device_normal(e.shape, s + 500000, ps.grad_std, dt, "cuda")
+        m = device_normal(e.shape, s + 900000, ps.mom_std, torch.float32, "cuda")
+        o = None
+        if e.name in SAMPLES[set_name]:
+            keep[j] = (to_np(w), to_np(g), to_np(m))
+            o = torch.zeros(e.shape, dtype=torch.float32, device="cuda")
+        ws.append(w); gs.append(g); ms.append(m); oo.append(o)
+    nso.muon_step(ws, gs, ms, lr=0.02, weight_decay=0.01, heads=[e.heads for e in ps.muon], ortho_outs=oo)
+    torch.cuda.synchronize()
+    for j, (w0, g0, m0) in keep.items():
+        e = ps.muon[j]
+        print(f"  oracle for {e.name} {e.shape} heads={e.heads}", flush=True)
+        ref = O.muon_step_ref(w0, g0, m0, lr=0.02, weight_decay=0.01, heads=e.heads)
+        assert O.rel_fro(to_np(oo[j]), ref["o"]) <= BF16_TOL, e.name
+        assert O.rel_fro(to_np(ms[j]), ref["m"]) <= MOM_TOL, e.name
+    # every matrix moved and stayed finite
+    for j, w in enumerate(ws):
+        assert torch.isfinite(w).all(), ps.muon[j].name
+    del ws, gs, ms, oo
+
+
+@pytest.mark.parametrize("set_name", ["gpt2_small", "llama_8b"])
+def test_full_set_adamw_step(set_name):
+    import newton_schulz_orthogonalized_amd as nso
+    idx = list(PARAM_SETS).index(set_name)
+    ps = PARAM_SETS[set_name]()
+    print(f"[fullsize adamw] {set_name}: {len(ps.adamw)} tensors, {ps.adamw_elems()} elements", flush=True)
+    p_, g_, m_, v_, keep = [], [], [], [], {}
+    rng = np.random.default_rng(idx)
+    for j, e in enumerate(ps.adamw):
+        s = seed_for(idx, 100 + j)
+        p = device_normal(e.shape, s, ps.weight_std, torch.bfloat16, "cuda")
+        g = device_normal(e.shape, s + 500000, ps.grad_std, torch.bfloat16, "cuda")
+        m = device_normal(e.shape, s + 900000, 1e-3, torch.float32, "cuda")
+        v = device_normal(e.shape, s + 700000, 1e-3, torch.float32, "cuda").square_()
+        n = p.numel()
+        lo = int(rng.integers(0, max(1, n - 1_000_000)))
+        sl = slice(lo, min(n, lo + 1_000_000))
+        keep[j] = (sl, to_np(p.view(-1)[sl]), to_np(g.view(-1)[sl]), to_np(m.view(-1)[sl]), to_np(v.view(-1)[sl]))
+        p_.append(p); g_.append(g); m_.append(m); v_.append(v)
+    nso.adamw_step(p_, g_, m_, v_, lr=0.02, weight_decay=0.01, beta1=0.9, beta2=0.95, eps=1e-8, step=10)
+    torch.cuda.synchronize()
+    for j, (sl, p0, g0, m0, v0) in keep.items():
+        f32 = lambda x: float(np.float32(x))  # noqa: E731  (the C ABI's float32 hyper-parameters)
+        pr, mr, vr = O.adamw_ref(p0, g0, m0, v0, lr=f32(0.02), weight_decay=f32(0.01), beta1=f32(0.9),
+                                 beta2=f32(0.95), eps=f32(1e-8), step=10)
+        p1 = to_np(p_[j].view(-1)[sl])
+        ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(pr), 2.0 ** -126))) - 7)
+        assert np.all(np.abs(p1 - pr) <= ulp), ps.adamw[j].name
+        assert O.rel_fro(to_np(m_[j].view(-1)[sl]), mr) <= 1e-6
+        assert O.rel_fro(to_np(v_[j].view(-1)[sl]), vr) <= 1e-6

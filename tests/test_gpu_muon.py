@@ -1,0 +1,238 @@
+"""GPU parity of the Muon step and the orthogonalise-only call against the CPU
+oracle, at sizes the oracle finishes in seconds (several GEMM tiles, ragged
+tails, tall and wide blocks, heads, mixed lists) and on the degenerate cases.
+
+Tolerances (relative Frobenius error against the float64 oracle): float32 path
+1e-4, bf16-MFMA path 2e-2, momentum 1e-6.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import bf16_ulp, make_matrix_inputs, need_gpu, to_np
+from oracle import muon_oracle as O
+from workloads import as_dtype, host_normal
+
+pytestmark = pytest.mark.gpu
+
+F32_TOL = 1e-4
+BF16_TOL = 2e-2
+MOM_TOL = 1e-6
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    need_gpu()
+    import newton_schulz_orthogonalized_amd as nso  # noqa: F401  (fails loudly without the library)
+    yield
+
+
+def nso():
+    import newton_schulz_orthogonalized_amd as m
+    return m
+
+
+SHAPES = [(128, 256), (256, 128), (77, 300), (300, 77), (5, 3), (1, 9), (9, 1), (129, 1000), (520, 520),
+          (640, 384), (768, 2304)]
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+def test_orthogonalize_f32(shape):
+    print(f"[orthogonalize f32] shape={shape}", flush=True)
+    x = as_dtype(host_normal(shape, 101), torch.float32)
+    out, = nso().orthogonalize([x.cuda()], precision="f32")
+    ref, _ = O.orthogonalize_ref(to_np(x))
+    assert O.rel_fro(to_np(out), ref) <= F32_TOL
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+def test_orthogonalize_bf16(shape):
+    print(f"[orthogonalize bf16] shape={shape}", flush=True)
+    x = as_dtype(host_normal(shape, 202, 1e-3), torch.bfloat16)
+    norm = torch.zeros(1, device="cuda")
+    out, = nso().orthogonalize([x.cuda()], precision="bf16", norm_outs=[norm])
+    ref, nref = O.orthogonalize_ref(to_np(x))
+    # the bf16 output itself is rounded, which costs at most 2^-9 relative
+    assert O.rel_fro(to_np(out), ref) <= BF16_TOL
+    assert abs(norm.item() - nref[0]) <= 1e-5 * nref[0]
+
+
+@pytest.mark.parametrize("prec,tol", [("f32", F32_TOL), ("bf16", BF16_TOL)])
+def test_orthogonalize_f32_input_any_precision(prec, tol):
+    x = as_dtype(host_normal((200, 330), 303), torch.float32)
+    out, = nso().orthogonalize([x.cuda()], precision=prec)
+    ref, _ = O.orthogonalize_ref(to_np(x))
+    assert O.rel_fro(to_np(out), ref) <= tol
+
+
+def _step_case(shape, dtype, prec, seed, heads=1, scale=1.0, lr=0.02, wd=0.01, nesterov=True, coeffs=None,
+               ns_steps=5, gstd=1.0, wstd=1.0, mstd=1.0):
+    w, g, m = make_matrix_inputs(shape, seed, dtype, gstd, wstd, mstd)
+    w0, g0, m0 = to_np(w), to_np(g), to_np(m)
+    oout = torch.zeros(shape, dtype=torch.float32, device="cuda")
+    norms = torch.zeros(heads, dtype=torch.float32, device="cuda")
+    nso().muon_step([w], [g], [m], lr=lr, weight_decay=wd, mu=0.95, nesterov=nesterov, heads=[heads],
+                    scales=[scale], ns_steps=ns_steps, coeffs=coeffs, precision=prec, norm_outs=[norms],
+                    ortho_outs=[oout])
+    torch.cuda.synchronize()
+    ref = O.muon_step_ref(w0, g0, m0, lr=lr, weight_decay=wd, mu=0.95, nesterov=nesterov, heads=heads,
+                          coeffs=None if coeffs is None else coeffs if ns_steps else [], scale=scale)
+    return w0, to_np(w), to_np(m), to_np(oout), to_np(norms), ref
+
+
+def test_fp32_config_step_128x256():
+    """The small float32 case: 128x256, N(0,1) inputs, 5 cubic steps, lr 0.02, wd 0.01."""
+    w0, w1, m1, o, norms, ref = _step_case((128, 256), torch.float32, "f32", 7000)
+    assert O.rel_fro(m1, ref["m"]) <= MOM_TOL
+    assert O.rel_fro(o, ref["o"]) <= F32_TOL
+    assert O.rel_fro(w1 - w0, ref["w"] - w0) <= F32_TOL
+    assert abs(norms[0] - ref["norms"][0]) <= 1e-5 * ref["norms"][0]
+
+
+@pytest.mark.parametrize("shape", [(768, 2304), (2304, 768), (768, 768), (300, 77), (129, 1000)])
+def test_bf16_step(shape):
+    print(f"[bf16 step] shape={shape}", flush=True)
+    w0, w1, m1, o, _, ref = _step_case(shape, torch.bfloat16, "bf16", 8000, gstd=1e-3, wstd=0.02, mstd=1e-3)
+    assert O.rel_fro(m1, ref["m"]) <= MOM_TOL
+    assert O.rel_fro(o, ref["o"]) <= BF16_TOL
+    # the update arithmetic: W1 is the bf16 rounding of W0 - lr wd W0 - lr O (with the GPU's O)
+    want = w0 - 0.02 * 0.01 * w0 - 0.02 * o
+    assert np.all(np.abs(w1 - want) <= bf16_ulp(want) * 0.5 + 1e-6 * np.abs(want) + 1e-30)
+
+
+@pytest.mark.parametrize("shape,heads", [((512, 256), 4), ((256, 64), 8), ((1024, 128), 2), ((4096, 4096), 32)])
+@pytest.mark.parametrize("prec", ["f32", "bf16"])
+def test_per_head(shape, heads, prec):
+    print(f"[per-head] shape={shape} heads={heads} prec={prec}", flush=True)
+    dtype = torch.float32 if prec == "f32" else torch.bfloat16
+    w0, w1, m1, o, norms, ref = _step_case(shape, dtype, prec, 9000 + heads, heads=heads, gstd=1e-3, wstd=0.02,
+                                           mstd=1e-3)
+    tol = F32_TOL if prec == "f32" else BF16_TOL
+    for h, sl in enumerate(O.head_blocks(shape[0], heads)):
+        assert O.rel_fro(o[sl], ref["o"][sl]) <= tol, h
+    assert np.allclose(norms, ref["norms"], rtol=1e-5, atol=0)
+
+
+COEFF_SETS = [
+    [(1.875, -1.25, 0.375)] * 5,                                   # quintic every step
+    [(1.5, -0.5, 0.0), (1.875, -1.25, 0.375), (2.0, -1.5, 0.5), (1.5, -0.5, 0.0)],   # mixed, 4 steps
+    [(1.5, -0.5, 0.0)] * 8,                                          # more cubic steps
+    [(1.5, -0.5, 0.0)],                                              # one step
+]
+
+
+@pytest.mark.parametrize("ci", range(len(COEFF_SETS)))
+@pytest.mark.parametrize("prec", ["f32", "bf16"])
+def test_configurable_coefficients(ci, prec):
+    coeffs = COEFF_SETS[ci]
+    dtype = torch.float32 if prec == "f32" else torch.bfloat16
+    w0, w1, m1, o, _, ref = _step_case((300, 520), dtype, prec, 9500 + ci, coeffs=coeffs, ns_steps=len(coeffs))
+    assert O.rel_fro(o, ref["o"]) <= (F32_TOL if prec == "f32" else BF16_TOL)
+
+
+@pytest.mark.parametrize("prec", ["f32", "bf16"])
+def test_zero_steps_applies_normalised_u(prec):
+    dtype = torch.float32 if prec == "f32" else torch.bfloat16
+    for shape in [(64, 200), (200, 64)]:
+        w0, w1, m1, o, _, ref = _step_case(shape, dtype, prec, 9700, ns_steps=0, coeffs=[])
+        assert O.rel_fro(o, ref["o"]) <= (F32_TOL if prec == "f32" else 4e-3)
+
+
+def test_nesterov_off_and_scale():
+    w0, w1, m1, o, _, ref = _step_case((256, 384), torch.float32, "f32", 9800, nesterov=False, scale=2.5,
+                                       lr=0.05, wd=0.1)
+    assert O.rel_fro(o, ref["o"]) <= F32_TOL
+    assert O.rel_fro(w1 - w0, ref["w"] - w0) <= F32_TOL
+    assert O.rel_fro(m1, ref["m"]) <= MOM_TOL
+
+
+def test_mixed_list_one_call():
+    """Shapes that land in different tile groups, tall and wide, with heads, in one call."""
+    specs = [((768, 2304), 1), ((2304, 768), 1), ((128, 4096), 1), ((512, 256), 4), ((77, 300), 1),
+             ((1024, 1024), 8), ((5, 3), 1)]
+    ws, gs, ms, oo, w0s, g0s, m0s = [], [], [], [], [], [], []
+    for i, (shape, heads) in enumerate(specs):
+        w, g, m = make_matrix_inputs(shape, 12000 + 10 * i, torch.bfloat16, 1e-3, 0.02, 1e-3)
+        ws.append(w); gs.append(g); ms.append(m)
+        w0s.append(to_np(w)); g0s.append(to_np(g)); m0s.append(to_np(m))
+        oo.append(torch.zeros(shape, dtype=torch.float32, device="cuda"))
+    nso().muon_step(ws, gs, ms, lr=0.02, weight_decay=0.01, heads=[h for _, h in specs], ortho_outs=oo)
+    torch.cuda.synchronize()
+    for i, (shape, heads) in enumerate(specs):
+        ref = O.muon_step_ref(w0s[i], g0s[i], m0s[i], lr=0.02, weight_decay=0.01, heads=heads)
+        assert O.rel_fro(to_np(oo[i]), ref["o"]) <= BF16_TOL, shape
+        assert O.rel_fro(to_np(ms[i]), ref["m"]) <= MOM_TOL, shape
+
+
+def test_zero_gradient_and_momentum_decay_only():
+    w = as_dtype(host_normal((256, 512), 13000, 0.02), torch.bfloat16).cuda()
+    w0 = to_np(w)
+    g = torch.zeros_like(w)
+    m = torch.zeros(w.shape, dtype=torch.float32, device="cuda")
+    oo = torch.full(w.shape, 7.0, dtype=torch.float32, device="cuda")
+    nso().muon_step([w], [g], [m], lr=0.1, weight_decay=0.5, ortho_outs=[oo])
+    torch.cuda.synchronize()
+    assert torch.all(oo == 0)
+    want = w0 - 0.1 * 0.5 * w0
+    assert np.all(np.abs(to_np(w) - want) <= bf16_ulp(want) * 0.5 + 1e-6 * np.abs(want) + 1e-30)
+
+
+def test_nan_stays_in_its_matrix():
+    a = as_dtype(host_normal((64, 128), 13100), torch.float32).cuda()
+    b = as_dtype(host_normal((64, 128), 13101), torch.float32).cuda()
+    a_cpu = a.clone()
+    a_cpu[3, 5] = float("nan")
+    outs = nso().orthogonalize([a_cpu, b], precision="f32")
+    torch.cuda.synchronize()
+    assert torch.all(torch.isnan(outs[0]))
+    ref, _ = O.orthogonalize_ref(to_np(b))
+    assert O.rel_fro(to_np(outs[1]), ref) <= F32_TOL
+
+
+def test_rank_one_inputs_keep_their_direction():
+    """A rank-1 gradient maps to its unit dyad, not to zero (rank-1 hazard claim of the MuonClip page)."""
+    u = host_normal(200, 13200)
+    v = host_normal(70, 13201)
+    x = as_dtype(np.outer(u, v), torch.float32).cuda()
+    col = as_dtype(u[:, None], torch.float32).cuda()
+    o1, o2 = nso().orthogonalize([x, col], precision="f32")
+    want = np.outer(u / np.linalg.norm(u), v / np.linalg.norm(v))
+    assert O.rel_fro(to_np(o1), want) <= F32_TOL
+    assert O.rel_fro(to_np(o2)[:, 0], u / np.linalg.norm(u)) <= F32_TOL
+
+
+def test_determinism_bitwise():
+    def run():
+        w, g, m = make_matrix_inputs((768, 2304), 14000, torch.bfloat16, 1e-3, 0.02, 1e-3)
+        oo = torch.zeros(w.shape, dtype=torch.float32, device="cuda")
+        nso().muon_step([w], [g], [m], lr=0.02, weight_decay=0.01, ortho_outs=[oo])
+        torch.cuda.synchronize()
+        return w.cpu(), m.cpu(), oo.cpu()
+    a, b = run(), run()
+    for x, y in zip(a, b):
+        assert torch.equal(x.view(torch.int16) if x.dtype == torch.bfloat16 else x.view(torch.int32),
+                           y.view(torch.int16) if y.dtype == torch.bfloat16 else y.view(torch.int32))
+
+
+def test_empty_list_is_noop():
+    nso().muon_step([], [], [], lr=0.02, weight_decay=0.01)
+    assert nso().orthogonalize([]) == []
+
+
+def test_errors_leave_buffers_untouched():
+    from newton_schulz_orthogonalized_amd import _lib
+    w, g, m = make_matrix_inputs((30, 40), 15000, torch.float32)
+    w0, m0 = w.clone(), m.clone()
+    with pytest.raises(_lib.MuonError) as e:
+        nso().muon_step([w], [g], [m], lr=0.02, weight_decay=0.01, heads=[7])
+    assert e.value.status == _lib.MU_ERR_INVALID_ARG
+    with pytest.raises(_lib.MuonError) as e:
+        nso().muon_step([w], [g], [m], lr=0.02, weight_decay=0.01, workspace=torch.empty(256, dtype=torch.uint8,
+                                                                                          device="cuda"))
+    assert e.value.status == _lib.MU_ERR_WORKSPACE
+    with pytest.raises(_lib.MuonError) as e:
+        nso().muon_step([w], [w], [m], lr=0.02, weight_decay=0.01)   # grad aliases param
+    assert e.value.status == _lib.MU_ERR_LAYOUT
+    torch.cuda.synchronize()
+    assert torch.equal(w, w0) and torch.equal(m, m0)
