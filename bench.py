@@ -96,8 +96,8 @@ def cpu_baseline(ps, set_index, ns_steps):
         cores = max([int(i.get("num_threads", 1)) for i in threadpool_info()] + [1])
     except Exception:  # pragma: no cover
         cores = os.cpu_count() or 1
-    # sample: the Muon matrices of layer 0 that the oracle finishes in seconds
-    # (the set's smallest distinct shapes, at most two) + 8M AdamW elements
+    # sample: layer 0's distinct Muon shapes, smallest first, up to three
+    # (about 10 s of float64 work on the 8B set) + 8M AdamW elements
     shapes, picked = [], []
     for e in ps.muon:
         key = (e.shape, e.heads)
@@ -105,7 +105,7 @@ def cpu_baseline(ps, set_index, ns_steps):
             shapes.append(key)
             picked.append(e)
     picked.sort(key=lambda e: e.shape[0] * e.shape[1] * min(e.shape) // e.heads)
-    picked = picked[:2]
+    picked = picked[:3]
     from workloads import MuonEntry, ParamSet
     sample = ParamSet("sample", [MuonEntry(e.name, e.shape, e.heads) for e in picked])
     t_muon = 0.0

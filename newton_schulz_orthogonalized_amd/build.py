@@ -11,6 +11,10 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmuon_mi355x.so")
 SOURCES = ["capi.hip", "elementwise.hip", "ns_gemm.hip"]
 ARCH = "gfx950"
+# Per-source extra flags. The Newton-Schulz GEMMs keep 256 accumulator AGPRs
+# and two fragment buffers live; the register-minimising scheduler keeps the
+# accumulators in place (no spills, no copies in the K loop).
+EXTRA = {"ns_gemm.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-minreg"]}
 
 
 def hipcc() -> str:
@@ -19,29 +23,44 @@ def hipcc() -> str:
     return cand if os.path.exists(cand) else "hipcc"
 
 
-def command(out: str = LIB) -> list:
-    return [
-        hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-        # no packed fp32 instructions in any kernel
-        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-        "-Wno-unused-command-line-argument",
-        "-I", os.path.join(os.path.dirname(HERE), "include"),
-        "-o", out,
-    ] + [os.path.join(CSRC, s) for s in SOURCES]
+COMMON = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+    # no packed fp32 instructions in any kernel
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wno-unused-command-line-argument",
+]
 
 
-def build(verbose: bool = True) -> str:
-    tmp = LIB + ".tmp"
-    cmd = command(tmp)
+def compile_commands(objdir: str) -> list:
+    cmds = []
+    for src in SOURCES:
+        obj = os.path.join(objdir, src.replace(".hip", ".o"))
+        cmds.append([hipcc()] + COMMON + EXTRA.get(src, []) +
+                    ["-I", os.path.join(os.path.dirname(HERE), "include"), "-c", os.path.join(CSRC, src), "-o", obj])
+    return cmds
+
+
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
-    out = "\n".join(l for l in res.stdout.splitlines() if "packed-fp32-ops" not in l and "target-feature" not in l)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{res.stdout}")
+    out = "\n".join(l for l in res.stdout.splitlines() if "packed-fp32-ops" not in l and "target-feature" not in l)
     if verbose and out.strip():
         print(out, flush=True)
-    os.replace(tmp, LIB)
+
+
+def build(verbose: bool = True) -> str:
+    import tempfile
+    with tempfile.TemporaryDirectory(prefix="mu_build_") as objdir:
+        cmds = compile_commands(objdir)
+        for c in cmds:
+            _run(c, verbose)
+        tmp = LIB + ".tmp"
+        objs = [c[c.index("-o") + 1] for c in cmds]
+        _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs, verbose)
+        os.replace(tmp, LIB)
     return LIB
 
 

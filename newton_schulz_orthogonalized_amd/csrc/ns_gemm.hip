@@ -40,11 +40,11 @@ namespace {
 
 constexpr int NTHR = 256;
 
-// XOR swizzle of the eight 16-byte chunks of a 128-byte K-contiguous LDS row.
-// Any 8 consecutive rows get distinct chunks, and any 16 consecutive rows get
-// distinct (row parity, chunk) pairs, so ds_read_b128 of 16 rows at one logical
-// chunk touches every bank once whether the LDS serves 128 or 256 bytes/clock.
-__device__ __forceinline__ int swz_k(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+// XOR swizzle of the eight 16-byte chunks of a 128-byte K-contiguous LDS row:
+// physical chunk = logical chunk ^ (row & 7). A fragment read (16 rows at one
+// logical chunk) then runs at the rate of a linear ds_read_b128 on gfx950, as
+// measured; variants that also flip on row bit 3 ran about 1.45x slower.
+__device__ __forceinline__ int swz_k(int r) { return r & 7; }
 
 // XOR swizzle of the 32-byte groups of an N-contiguous LDS row (X tile of the
 // apply). A transposed read touches rows 8g + {0..3} (+4) for g = 0..3 at one
@@ -164,15 +164,14 @@ __device__ __forceinline__ void store8(TX* p, const float* v) {
 // ---------------------------------------------------------------------------
 // Epilogue shared by the bf16 and fp32 kernels. The accumulator layout is the
 // 16x16 MFMA one: lane l holds C[4*(l>>4) + e][l & 15] of each fragment.
-// `stage` must hold 4 waves x 16 x (F*16 + 4) floats and not be in use.
+// `st` is this wave's LDS strip of 16 x (F*16 + 4) floats, not otherwise in use.
 // ---------------------------------------------------------------------------
 template <typename TX, typename TS, int F>
 __device__ __forceinline__ void epilogue(const GemmArgs& A, const NsProb& P, int ti, int tj, int TS_, int wm0,
-                                int wn0, f32x4 (&acc)[F][F], float* stage) {
+                                int wn0, f32x4 (&acc)[F][F], float* st) {
     constexpr int WT = F * 16;
     constexpr int SP = WT + 4;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    float* st = stage + wave * 16 * SP;
+    const int lane = threadIdx.x & 63;
     const int mode = A.mode;
     const float f = A.first ? P.fold[0] : 1.f;
     const bool gram = mode == GM_GRAM || mode == GM_GRAM2;
@@ -256,15 +255,47 @@ __device__ __forceinline__ void epilogue(const GemmArgs& A, const NsProb& P, int
 
 // ---------------------------------------------------------------------------
 // bf16 kernel
+//
+// K loop, BK = 64, two LDS stages (separate arrays, so the compiler's wait
+// insertion can tell a direct-to-LDS load into one stage from reads of the
+// other). Operand tiles move HBM/L2 -> LDS with global_load_lds_dwordx4: each
+// instruction writes 64 lanes x 16 B contiguously (LDS base + lane*16), so the
+// XOR swizzle is applied by permuting the global addresses the lanes load.
+//
+// Iteration kt (stage S holds tile kt; fragments F0 = k-half 0 of tile kt are
+// already in registers):
+//   phase 1: read F1 (k-half 1 of tile kt) from stage S   | MFMAs on F0
+//   phase 2: first MFMAs on F1; wait own loads; barrier    | (tile kt+1 ready,
+//            all waves done with stage S)
+//            DMA tile kt+2 into stage S; read F0 of tile kt+1 from stage S^1
+//            | remaining MFMAs on F1
+// One barrier per K step; loads run ~1.25 steps ahead of their use.
 // ---------------------------------------------------------------------------
+#define LDSP __attribute__((address_space(3)))
+
+template <int N>
+struct Stage {
+    static constexpr int value = N;
+};
+
+// s_waitcnt with only vmcnt (gfx9 encoding: vmcnt[3:0] bits 3:0, [5:4] bits 15:14)
+#define MU_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14))
+#define MU_WAIT_LGKMCNT0() __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (0 << 8) | (3 << 14))
+
 template <int TS, bool NN, typename TSRC>
 __global__ __launch_bounds__(NTHR) void k_gemm_bf16(GemmArgs A) {
     constexpr int BK = 64;
     constexpr int WT = TS / 2;
     constexpr int F = WT / 16;
-    constexpr int LA = TS * BK;                     // elements per operand tile
-    constexpr int LOADS = LA / 8 / NTHR;            // 16-byte chunks per thread per operand
-    __shared__ __attribute__((aligned(16))) bf16 smem[2 * 2 * LA];
+    constexpr int LA = TS * BK;           // elements per operand tile
+    constexpr int NBLK = LA * 2 / 1024;   // 1 KB direct-load blocks per operand tile
+    constexpr int BPW = NBLK / 4;         // blocks per wave per operand
+    constexpr int RB = NN ? 1024 / (TS * 2) : 8;   // rows of a block (B operand)
+    constexpr int LPR = 64 / RB;                   // lanes per row (B operand)
+    __shared__ __attribute__((aligned(1024))) bf16 sA0[LA];
+    __shared__ __attribute__((aligned(1024))) bf16 sB0[LA];
+    __shared__ __attribute__((aligned(1024))) bf16 sA1[LA];
+    __shared__ __attribute__((aligned(1024))) bf16 sB1[LA];
 
     const int wg = xcd_remap(blockIdx.x, gridDim.x);
     if (wg >= A.total_tiles) return;
@@ -289,39 +320,87 @@ __global__ __launch_bounds__(NTHR) void k_gemm_bf16(GemmArgs A) {
     const bf16* pt = pm + (int64_t)ti * TS * ldp;
     const bf16* qt = NN ? qm + tj * TS : qm + (int64_t)tj * TS * ldq;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm0 = (wave >> 1) * WT, wn0 = (wave & 1) * WT;
 
-    u32x4 ga[LOADS], gb[LOADS];
-    auto gload = [&](int kt) {
-        const int k0 = kt * BK;
+    // Direct-load sources. Block b = s*4 + wave of an operand tile is 1 KB:
+    // K-contiguous: rows 8b .. 8b+7, lane -> row 8b + lane/8, physical chunk
+    //   lane%8 holds logical chunk (lane%8) ^ swz_k(row) = (lane%8) ^ (lane/8),
+    //   so block s is the block-0 address plus s*32 rows.
+    // N-contiguous (apply X tile): rows RB*b .. RB*b+RB-1, lane -> row RB*b + lane/LPR,
+    //   16-byte piece lane%LPR; its 32-byte group is XOR-ed with swz_n(row).
+    // Every source address is a wave-uniform base (scalar registers) plus a
+    // fixed 32-bit per-lane byte offset, so the loads use the saddr form.
+    const int ca = (lane & 7) ^ (lane >> 3);
+    const uint32_t offA = (uint32_t)((8 * wave + (lane >> 3)) * ldp + ca * 8) * 2u;
+    const int64_t strideA = (int64_t)32 * ldp;   // elements between blocks s and s+1
+    uint32_t offB0, offB1;                        // NN with RB == 2: odd s swizzles differently
+    int64_t strideB;
+    if (NN) {
+        const int r0 = RB * wave + lane / LPR;     // row of block s = 0
+        const int pch = lane % LPR;
+        const int g_even = (pch >> 1) ^ swz_n(r0);
+        const int g_odd = (pch >> 1) ^ swz_n(r0 + RB * 4);
+        offB0 = (uint32_t)(r0 * ldq + (2 * g_even + (pch & 1)) * 8) * 2u;
+        offB1 = (uint32_t)((r0 + RB * 4) * ldq + (2 * g_odd + (pch & 1)) * 8) * 2u;
+        strideB = (int64_t)RB * 8 * ldq;           // elements between blocks s and s+2
+    } else {
+        offB0 = offB1 = (uint32_t)((8 * wave + (lane >> 3)) * ldq + ca * 8) * 2u;
+        strideB = (int64_t)32 * ldq;
+    }
+    const int64_t stepB = NN ? (int64_t)BK * ldq : BK;
+
+    auto dma = [&](auto st, int kt) {
+        constexpr int S = decltype(st)::value;
+        bf16* sa = S ? sA1 : sA0;
+        bf16* sb = S ? sB1 : sB0;
+        const char* abase = (const char*)(pt + kt * BK);
+        const char* bbase = (const char*)(qt + kt * stepB);
 #pragma unroll
-        for (int s = 0; s < LOADS; ++s) {
-            const int q = s * NTHR + tid;
-            ga[s] = *gp((const u32x4*)(pt + (int64_t)(q >> 3) * ldp + k0 + (q & 7) * 8));
-            if (NN) {
-                const int k = q / (TS / 8), c16 = q % (TS / 8);
-                gb[s] = *gp((const u32x4*)(qt + (int64_t)(k0 + k) * ldq + c16 * 8));
-            } else {
-                gb[s] = *gp((const u32x4*)(qt + (int64_t)(q >> 3) * ldq + k0 + (q & 7) * 8));
-            }
+        for (int s = 0; s < BPW; ++s) {
+            const int blk = s * 4 + wave;
+            __builtin_amdgcn_global_load_lds((const void*)(abase + s * strideA * 2 + offA), (LDSP void*)(sa + blk * 512),
+                                             16, 0, 0);
+            const char* bsrc = NN ? bbase + (s >> 1) * strideB * 2 + ((s & 1) ? offB1 : offB0)
+                                  : bbase + s * strideB * 2 + offB0;
+            __builtin_amdgcn_global_load_lds((const void*)bsrc, (LDSP void*)(sb + blk * 512), 16, 0, 0);
         }
     };
-    auto sstore = [&](int stage) {
-        bf16* as = smem + stage * 2 * LA;
-        bf16* bs = as + LA;
+
+    // Fragment reads. K-contiguous operand: lane reads row (lane&15) of each
+    // 16-row fragment at logical chunk kh*4 + lane/16, whose physical chunk is
+    // that ^ swz_k(row) = ^ (lane&7): a lane constant per kh.
+    const int swl = lane & 7;
+    const int offk0 = (lane & 15) * BK + (((lane >> 4) ^ swl) << 3);
+    const int offk1 = (lane & 15) * BK + (((4 + (lane >> 4)) ^ swl) << 3);
+    // N-contiguous operand (transposed reads): 16-lane group G reads rows
+    // kh*32 + 8G + rq (+4), columns of fragment fn at group (wn0/16 + fn) ^ swz_n(row),
+    // and swz_n(row) = rq | (G&1)<<2 for every kh and half.
+    const int Gq = lane >> 4, rq = (lane >> 2) & 3, q4 = lane & 3;
+    const int swn = rq | ((Gq & 1) << 2);
+    const int offn = (8 * Gq + rq) * TS + q4 * 4;
+
+    auto frags = [&](auto st, int kh, bf16x8 (&af)[F], bf16x8 (&bfv)[F]) {
+        constexpr int S = decltype(st)::value;
+        const bf16* as = S ? sA1 : sA0;
+        const bf16* bs = S ? sB1 : sB0;
+        const int ok = kh ? offk1 : offk0;
 #pragma unroll
-        for (int s = 0; s < LOADS; ++s) {
-            const int q = s * NTHR + tid;
-            const int r = q >> 3, c = q & 7;
-            *(u32x4*)(as + r * BK + ((c ^ swz_k(r)) << 3)) = ga[s];
-            if (NN) {
-                const int k = q / (TS / 8), c16 = q % (TS / 8);
-                const int g = c16 >> 1, h = c16 & 1;
-                *(u32x4*)(bs + k * TS + ((((g ^ swz_n(k)) << 1) | h) << 3)) = gb[s];
-            } else {
-                *(u32x4*)(bs + r * BK + ((c ^ swz_k(r)) << 3)) = gb[s];
+        for (int fm = 0; fm < F; ++fm) af[fm] = *(const bf16x8*)(as + (wm0 + fm * 16) * BK + ok);
+        if (NN) {
+#pragma unroll
+            for (int fn = 0; fn < F; ++fn) {
+                // the XOR acts on the low three bits of the group index, so it
+                // is applied to the whole index (wn0/16 + fn), not to fn alone
+                const bf16* base = bs + offn + ((((wn0 >> 4) + fn) ^ swn) << 4) + kh * 32 * TS;
+                const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDSP i16x4*)base);
+                const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDSP i16x4*)(base + 4 * TS));
+                bfv[fn] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
             }
+        } else {
+#pragma unroll
+            for (int fn = 0; fn < F; ++fn) bfv[fn] = *(const bf16x8*)(bs + (wn0 + fn * 16) * BK + ok);
         }
     };
 
@@ -331,60 +410,51 @@ __global__ __launch_bounds__(NTHR) void k_gemm_bf16(GemmArgs A) {
 #pragma unroll
         for (int j = 0; j < F; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const int KT = K / BK;
-    gload(0);
-    sstore(0);
-    __syncthreads();
-    for (int kt = 0; kt < KT; ++kt) {
-        if (kt + 1 < KT) gload(kt + 1);
-        const bf16* as = smem + (kt & 1) * 2 * LA;
-        const bf16* bs = as + LA;
+    auto mma_rows = [&](int fm0, int fm1, const bf16x8 (&af)[F], const bf16x8 (&bfv)[F]) {
 #pragma unroll
-        for (int kh = 0; kh < 2; ++kh) {
-            bf16x8 af[F], bfv[F];
-            const int c = kh * 4 + (lane >> 4);
-#pragma unroll
-            for (int fm = 0; fm < F; ++fm) {
-                const int r = wm0 + fm * 16 + (lane & 15);
-                af[fm] = *(const bf16x8*)(as + r * BK + ((c ^ swz_k(r)) << 3));
-            }
-            if (NN) {
-                const int G = lane >> 4, rq = (lane >> 2) & 3, q4 = lane & 3;
-#pragma unroll
-                for (int fn = 0; fn < F; ++fn) {
-                    const int g = (wn0 + fn * 16) >> 4;
-                    i16x4 lo, hi;
-                    {
-                        const int k = kh * 32 + 8 * G + rq;
-                        lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (__attribute__((address_space(3))) i16x4*)(bs + k * TS + ((g ^ swz_n(k)) << 4) + q4 * 4));
-                    }
-                    {
-                        const int k = kh * 32 + 8 * G + 4 + rq;
-                        hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (__attribute__((address_space(3))) i16x4*)(bs + k * TS + ((g ^ swz_n(k)) << 4) + q4 * 4));
-                    }
-                    typedef short i16x8 __attribute__((ext_vector_type(8)));
-                    i16x8 both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                    bfv[fn] = __builtin_bit_cast(bf16x8, both);
-                }
-            } else {
-#pragma unroll
-                for (int fn = 0; fn < F; ++fn) {
-                    const int r = wn0 + fn * 16 + (lane & 15);
-                    bfv[fn] = *(const bf16x8*)(bs + r * BK + ((c ^ swz_k(r)) << 3));
-                }
-            }
-#pragma unroll
-            for (int fm = 0; fm < F; ++fm)
+        for (int fm = 0; fm < F; ++fm)
+            if (fm >= fm0 && fm < fm1)
 #pragma unroll
                 for (int fn = 0; fn < F; ++fn)
                     acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[fm], bfv[fn], acc[fm][fn], 0, 0, 0);
-        }
-        if (kt + 1 < KT) sstore((kt + 1) & 1);
-        __syncthreads();
+    };
+
+    constexpr int NRD = NN ? 3 * F : 2 * F;  // fragment reads per k-half
+    bf16x8 a0[F], b0[F], a1[F], b1[F];
+    const int KT = K / BK;
+
+    dma(Stage<0>{}, 0);
+    MU_WAIT_VMCNT(0);
+    __builtin_amdgcn_s_barrier();
+    dma(Stage<1>{}, 1);
+    frags(Stage<0>{}, 0, a0, b0);
+
+    // Straight-line body, unrolled over the two stages so every LDS access
+    // names one array. K/BK is even (K is a multiple of the tile >= 128); the
+    // prefetch index is clamped, so the last two prefetches reload the final
+    // tile into a stage nobody reads again instead of branching.
+    auto half = [&](auto st, int kt) {
+        constexpr int S = decltype(st)::value;
+        // phase 1: k-half 1 fragments of tile kt against the MFMAs of k-half 0
+        frags(st, 1, a1, b1);
+        mma_rows(0, F, a0, b0);
+        // phase 2: tile kt+1 landed (own loads + barrier), stage S is free
+        constexpr int HEAD = F / 4 > 0 ? F / 4 : 1;
+        mma_rows(0, HEAD, a1, b1);
+        MU_WAIT_VMCNT(0);
+        __builtin_amdgcn_s_barrier();
+        dma(st, min(kt + 2, KT - 1));
+        frags(Stage<1 - S>{}, 0, a0, b0);
+        mma_rows(HEAD, F, a1, b1);
+    };
+    for (int kt = 0; kt < KT; kt += 2) {
+        half(Stage<0>{}, kt);
+        half(Stage<1>{}, kt + 1);
     }
-    epilogue<bf16, TSRC, F>(A, P, ti, tj, TS, wm0, wn0, acc, (float*)smem);
+    __syncthreads();
+    // epilogue staging: waves 0-1 in stage 0's A array, waves 2-3 in its B array
+    float* st = (float*)((wave < 2) ? sA0 : sB0) + (wave & 1) * 16 * (WT + 4);
+    epilogue<bf16, TSRC, F>(A, P, ti, tj, TS, wm0, wn0, acc, st);
 }
 
 // ---------------------------------------------------------------------------
@@ -489,7 +559,7 @@ __global__ __launch_bounds__(NTHR) void k_gemm_f32(GemmArgs A) {
         if (kt + 1 < KT) sstore((kt + 1) & 1);
         __syncthreads();
     }
-    epilogue<float, TSRC, F>(A, P, ti, tj, TS, wm0, wn0, acc, smem);
+    epilogue<float, TSRC, F>(A, P, ti, tj, TS, wm0, wn0, acc, smem + wave * 16 * (WT + 4));
 }
 
 template <int TS, bool NN>

@@ -94,7 +94,11 @@ def test_full_set_adamw_step(set_name):
         pr, mr, vr = O.adamw_ref(p0, g0, m0, v0, lr=f32(0.02), weight_decay=f32(0.01), beta1=f32(0.9),
                                  beta2=f32(0.95), eps=f32(1e-8), step=10)
         p1 = to_np(p_[j].view(-1)[sl])
+        # one rounding to bf16 of a float32 result: half an ulp of the result plus
+        # float32 rounding of the operands (the update can cancel p to near zero)
         ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(pr), 2.0 ** -126))) - 7)
-        assert np.all(np.abs(p1 - pr) <= ulp), ps.adamw[j].name
+        tol = 0.5 * ulp + 8 * 2.0 ** -24 * (np.abs(p0) + np.abs(pr - p0))
+        bad = np.abs(p1 - pr) > tol
+        assert not bad.any(), (ps.adamw[j].name, int(bad.sum()), p0[bad][:3], pr[bad][:3], p1[bad][:3])
         assert O.rel_fro(to_np(m_[j].view(-1)[sl]), mr) <= 1e-6
         assert O.rel_fro(to_np(v_[j].view(-1)[sl]), vr) <= 1e-6
