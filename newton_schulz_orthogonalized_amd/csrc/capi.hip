@@ -230,7 +230,7 @@ void build_plan(const std::vector<Item>& items, int ns_dt, const std::vector<Coe
     pl.off_fold = o;
     o = align_up(o + sizeof(float) * P);
     pl.off_bufs = o;
-    for (auto& pp : pl.probs) o += 2 * pp.x_bytes + pp.a_bytes * (pl.quintic ? 2 : 1);
+    for (auto& pp : pl.probs) o += 4 * pp.x_bytes + pp.a_bytes * (pl.quintic ? 2 : 1);
     pl.total = o;
 }
 
@@ -245,6 +245,10 @@ void carve(Plan& pl, char* ws, std::vector<char>& host_table) {
         d.x[0] = ws + o;
         o += pl.probs[i].x_bytes;
         d.x[1] = ws + o;
+        o += pl.probs[i].x_bytes;
+        d.xt[0] = ws + o;
+        o += pl.probs[i].x_bytes;
+        d.xt[1] = ws + o;
         o += pl.probs[i].x_bytes;
         d.a = ws + o;
         o += pl.probs[i].a_bytes;

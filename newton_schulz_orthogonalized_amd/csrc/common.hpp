@@ -34,8 +34,10 @@ __device__ __forceinline__ MU_GLOBAL T* gp(T* p) {
 // U-space is the head block as stored: hr rows x hc cols, row pitch ld. X-space
 // is the wide orientation the iteration runs in: m = min(hr, hc) rows and
 // n = max(hr, hc) cols, X = U when hr <= hc and X = U^T otherwise ("tall").
-// The workspace copies of X and of the Gram matrix are padded with zeros to
-// mp x np and mp x mp (multiples of the GEMM tile); zero padding is preserved
+// The workspace keeps X (mp x np) and its transpose X^T (np x mp), so both
+// products of a step contract over the contiguous dimension of both operands:
+// the Gram X X^T reads X twice, the apply A X reads A and X^T. Buffers are
+// padded with zeros to multiples of the GEMM tile; zero padding is preserved
 // by every step, so the GEMM kernels need no bounds checks.
 // ---------------------------------------------------------------------------
 struct NsProb {
@@ -52,6 +54,7 @@ struct NsProb {
     float scale;       // update scale
     int32_t pad0;
     void* x[2];        // ping-pong X buffers, mp x np, NS element type
+    void* xt[2];       // their transposes, np x mp
     void* a;           // Gram matrix, mp x mp
     void* b;           // b*A + c*A^2 (quintic steps), mp x mp, or null
     float* partials;   // per prep-tile sums of squares

@@ -1,8 +1,9 @@
 // HBM-bound kernels of the Muon step and the AdamW step (gfx950).
 //
-//  k_prep    momentum EMA + Nesterov blend, write U into the X workspace in the
-//            wide orientation (LDS-transposed for tall blocks) with zero
-//            padding, and one sum of squares per 64x64 tile (fixed order).
+//  k_prep    momentum EMA + Nesterov blend, write U into the workspace as X
+//            (wide orientation) and X^T with zero padding (one of the two
+//            through an LDS transpose), and one sum of squares per 64x64 tile
+//            (fixed order).
 //  k_norm    per (matrix, head): fixed-order sum of the tile partials,
 //            fold = 1/(||U||_F + eps).
 //  k_finish  ns_steps == 0: O = fold * X0, then the update (or the output).
@@ -132,6 +133,10 @@ __device__ inline void make_u(const NsProb& P, int r, int c0, bool with_m, bool 
     store4<float>(P.mom, off, valid, vec, m);
 }
 
+// Tiles run over the buffer that has U's orientation (X for wide blocks, X^T
+// for tall ones): each 64x64 U tile is written there directly and, through an
+// LDS transpose, into the other buffer. Out-of-range elements are written as
+// zeros, which is the padding every later step relies on.
 template <typename TS, typename TX>
 __global__ __launch_bounds__(NTHR) void k_prep(PrepArgs A) {
     __shared__ float tile[T][T + 1];
@@ -140,46 +145,37 @@ __global__ __launch_bounds__(NTHR) void k_prep(PrepArgs A) {
     const int p = find_prob(A.prefix, A.nprobs, t);
     const NsProb& P = A.probs[p];
     const int local = t - A.prefix[p];
-    const int tiles_n = P.np / T;
+    const bool wide = !P.tall;
+    const int dpitch = wide ? P.np : P.mp;   // U-oriented buffer: X (wide) or X^T (tall)
+    const int tpitch = wide ? P.mp : P.np;   // the other one
+    TX* D = (TX*)(wide ? P.x[0] : P.xt[0]);
+    TX* Tt = (TX*)(wide ? P.xt[0] : P.x[0]);
+    const int tiles_n = dpitch / T;
     const int ti = local / tiles_n, tj = local - ti * tiles_n;
     const int tid = threadIdx.x;
     const int rr = tid >> 4, cc = (tid & 15) * 4;
     const bool with_m = A.with_momentum != 0, nest = A.nesterov != 0;
-    TX* X = (TX*)P.x[0];
     float ss = 0.f;
-    if (!P.tall) {
-        // X = U: X-space tile (ti, tj) is the U-space tile (ti, tj).
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int r = ti * T + rr + 16 * k, c0 = tj * T + cc;
-            float u[4];
-            make_u<TS>(P, r, c0, with_m, nest, A.mu, u);
+    for (int k = 0; k < 4; ++k) {
+        const int r = ti * T + rr + 16 * k, c0 = tj * T + cc;
+        float u[4];
+        make_u<TS>(P, r, c0, with_m, nest, A.mu, u);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) ss += u[e] * u[e];
-            store_x4<TX>(X + (int64_t)r * P.np + c0, u);
+        for (int e = 0; e < 4; ++e) {
+            ss += u[e] * u[e];
+            tile[rr + 16 * k][cc + e] = u[e];
         }
-    } else {
-        // X = U^T: X-space tile (ti, tj) is U-space tile (tj, ti), transposed in LDS.
+        store_x4<TX>(D + (int64_t)r * dpitch + c0, u);
+    }
+    __syncthreads();
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int r = tj * T + rr + 16 * k, c0 = ti * T + cc;
-            float u[4];
-            make_u<TS>(P, r, c0, with_m, nest, A.mu, u);
+    for (int k = 0; k < 4; ++k) {
+        const int a = rr + 16 * k;
+        float v[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                ss += u[e] * u[e];
-                tile[rr + 16 * k][cc + e] = u[e];
-            }
-        }
-        __syncthreads();
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int a = rr + 16 * k;
-            float v[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = tile[cc + e][a];
-            store_x4<TX>(X + (int64_t)(ti * T + a) * P.np + tj * T + cc, v);
-        }
+        for (int e = 0; e < 4; ++e) v[e] = tile[cc + e][a];
+        store_x4<TX>(Tt + (int64_t)(tj * T + a) * tpitch + ti * T + cc, v);
     }
     const float s = block_sum(ss, red);
     if (tid == 0) P.partials[local] = s;

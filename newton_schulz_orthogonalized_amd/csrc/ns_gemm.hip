@@ -13,21 +13,19 @@
 // by binary search over a tile prefix, and workgroup ids are remapped so that
 // neighbouring tiles run on the same XCD (shared L2).
 //
-//   Gram modes ("NT"): C = P Q^T with both operands K-contiguous rows. Only
-//   tiles on or above the diagonal are computed; the epilogue also stores the
-//   transposed tile, so A is written whole.
-//   Apply mode ("NN"): C = P X with X row-major (N-contiguous). The X tile is
-//   staged in LDS as stored and read with ds_read_b64_tr_b16, which hands each
-//   lane four rows of one column: the MFMA B operand without any transposed
-//   copy of X in memory.
+// Every product is "NT", C = P Q^T with both operands K-contiguous: the Gram
+// X X^T reads X twice; the apply A X reads A and the transposed copy X^T that
+// the previous step's epilogue (or the prep kernel) wrote. Gram products only
+// compute tiles on or above the diagonal and also store the transposed tile.
 //
 // bf16: v_mfma_f32_16x16x32_bf16, fp32 accumulation, 256x256 or 128x128
-// workgroup tiles, BK = 64, 4 waves in 2x2, LDS double buffer.
+// workgroup tiles, BK = 64, 4 waves in 2x2 (128x128 per wave for 256 tiles),
+// operands moved with direct-to-LDS loads into two LDS stages.
 // fp32: v_mfma_f32_16x16x4_f32, 64x64 tiles, BK = 32.
 //
 // Epilogue: accumulators are staged per wave through LDS in 16-row strips,
-// then stored with 16-byte row-major accesses (and, for the Gram mirror or a
-// tall weight, a column pass for the transposed store). It applies the fold
+// then stored with 16-byte row-major accesses and, for transposed outputs
+// (Gram mirror, X'^T, or a tall weight), a column pass. It applies the fold
 // 1/||U||_F of the first step (so the normalised X0 is never materialised), the
 // step coefficients, and on the last step the decoupled-weight-decay update
 // W <- W - lr*wd*W - lr*scale*O straight into the parameter.
@@ -46,10 +44,6 @@ constexpr int NTHR = 256;
 // measured; variants that also flip on row bit 3 ran about 1.45x slower.
 __device__ __forceinline__ int swz_k(int r) { return r & 7; }
 
-// XOR swizzle of the 32-byte groups of an N-contiguous LDS row (X tile of the
-// apply). A transposed read touches rows 8g + {0..3} (+4) for g = 0..3 at one
-// logical group; this maps rows {0..3, 8..11} to eight distinct groups.
-__device__ __forceinline__ int swz_n(int k) { return (k & 3) | (((k >> 3) & 1) << 2); }
 
 // ---------------------------------------------------------------------------
 // Tile enumeration
@@ -161,46 +155,88 @@ __device__ __forceinline__ void store8(TX* p, const float* v) {
     }
 }
 
+// Eight consecutive X-space values of a bf16 or float buffer, held raw.
+template <typename TX>
+struct Vec8;
+template <>
+struct Vec8<bf16> {
+    bf16x8 v;
+    __device__ __forceinline__ void load(const bf16* p) { v = *gp((const bf16x8*)p); }
+    __device__ __forceinline__ float get(int e) const { return (float)v[e]; }
+};
+template <>
+struct Vec8<float> {
+    f32x4 a, b;
+    __device__ __forceinline__ void load(const float* p) {
+        a = gp((const f32x4*)p)[0];
+        b = gp((const f32x4*)p)[1];
+    }
+    __device__ __forceinline__ float get(int e) const { return e < 4 ? a[e] : b[e - 4]; }
+};
+
+// Order LDS accesses of this wave (a wave's LDS operations complete in issue
+// order; only compiler reordering has to be prevented).
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // ---------------------------------------------------------------------------
 // Epilogue shared by the bf16 and fp32 kernels. The accumulator layout is the
 // 16x16 MFMA one: lane l holds C[4*(l>>4) + e][l & 15] of each fragment.
-// `st` is this wave's LDS strip of 16 x (F*16 + 4) floats, not otherwise in use.
+// `st` is this wave's LDS strip of 16 x (F*16 + 4) floats, not otherwise in
+// use; each wave stages only its own strip, so syncs are wave-local. In the
+// apply modes the X values of the whole tile are requested before the first
+// strip, so their latency is paid once.
 // ---------------------------------------------------------------------------
 template <typename TX, typename TS, int F>
 __device__ __forceinline__ void epilogue(const GemmArgs& A, const NsProb& P, int ti, int tj, int TS_, int wm0,
-                                int wn0, f32x4 (&acc)[F][F], float* st) {
+                                         int wn0, f32x4 (&acc)[F][F], float* st) {
     constexpr int WT = F * 16;
     constexpr int SP = WT + 4;
+    constexpr int PASSES = (16 * WT / 8) / 64;
     const int lane = threadIdx.x & 63;
     const int mode = A.mode;
     const float f = A.first ? P.fold[0] : 1.f;
     const bool gram = mode == GM_GRAM || mode == GM_GRAM2;
+    const bool apply = !gram;
     const bool mirror = gram && ti != tj;
     const bool last = mode == GM_APPLY_LAST;
-    const bool trans_out = mirror || (last && P.tall);
+    // transposed outputs: the Gram mirror, X'^T for the next apply, or the
+    // parameter of a tall block on the last step
+    const bool trans_out = mirror || (apply && !last) || (last && P.tall);
     const int row_base = ti * TS_ + wm0, col_base = tj * TS_ + wn0;
     const int mp = P.mp, np = P.np;
     const float cb_eff = A.use_b ? 1.f : A.cb;
     TX* gdst = (TX*)(mode == GM_GRAM ? P.a : P.b);
     const TX* xsrc = (const TX*)P.x[A.src];
     TX* xdst = (TX*)P.x[A.src ^ 1];
+    TX* xtdst = (TX*)P.xt[A.src ^ 1];
 
-    for (int fm = 0; fm < F; ++fm) {
-        __syncthreads();
-        // static register indices: one uniform branch per fragment row
+    Vec8<TX> xv[F][PASSES];
+    if (apply) {
 #pragma unroll
-        for (int i = 0; i < F; ++i) {
-            if (i == fm) {
+        for (int fm = 0; fm < F; ++fm)
 #pragma unroll
-                for (int fn = 0; fn < F; ++fn)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) st[(4 * (lane >> 4) + e) * SP + fn * 16 + (lane & 15)] = acc[i][fn][e];
+            for (int pass = 0; pass < PASSES; ++pass) {
+                const int idx = pass * 64 + lane;
+                const int rr = idx / (WT / 8), c8 = (idx % (WT / 8)) * 8;
+                xv[fm][pass].load(xsrc + (int64_t)(row_base + fm * 16 + rr) * np + col_base + c8);
             }
-        }
-        __syncthreads();
+    }
+
+#pragma clang loop unroll(full)
+    for (int fm = 0; fm < F; ++fm) {
+        wave_lds_sync();
+#pragma unroll
+        for (int fn = 0; fn < F; ++fn)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) st[(4 * (lane >> 4) + e) * SP + fn * 16 + (lane & 15)] = acc[fm][fn][e];
+        wave_lds_sync();
         // row-major pass: 8 consecutive columns per lane
 #pragma unroll
-        for (int pass = 0; pass < (16 * WT / 8) / 64; ++pass) {
+        for (int pass = 0; pass < PASSES; ++pass) {
             const int idx = pass * 64 + lane;
             const int rr = idx / (WT / 8), c8 = (idx % (WT / 8)) * 8;
             float v[8];
@@ -223,10 +259,8 @@ __device__ __forceinline__ void epilogue(const GemmArgs& A, const NsProb& P, int
                 for (int e = 0; e < 8; ++e) v[e] = A.cb * a8[e] + A.cc * v[e];
                 store8<TX>(gdst + (int64_t)r * mp + c, v);
             } else {
-                float x8[8];
-                load8<TX>(xsrc + (int64_t)r * np + c, x8);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) v[e] = f * (A.ca * x8[e] + cb_eff * v[e]);
+                for (int e = 0; e < 8; ++e) v[e] = f * (A.ca * xv[fm][pass].get(e) + cb_eff * v[e]);
                 if (!last) store8<TX>(xdst + (int64_t)r * np + c, v);
                 else if (!P.tall) emit_u8<TS>(A, P, r, c, v);
             }
@@ -236,7 +270,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& A, const NsProb& P, int
             }
         }
         if (trans_out) {
-            __syncthreads();
+            wave_lds_sync();
             // column pass: lane takes one column and 8 consecutive rows
 #pragma unroll
             for (int pass = 0; pass < (2 * WT) / 64; ++pass) {
@@ -247,6 +281,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& A, const NsProb& P, int
                 for (int t = 0; t < 8; ++t) v[t] = st[(half * 8 + t) * SP + jj];
                 const int r = row_base + fm * 16 + half * 8, c = col_base + jj;
                 if (mirror) store8<TX>(gdst + (int64_t)c * mp + r, v);
+                else if (!last) store8<TX>(xtdst + (int64_t)c * mp + r, v);
                 else emit_u8<TS>(A, P, c, r, v);
             }
         }
@@ -282,7 +317,7 @@ struct Stage {
 #define MU_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14))
 #define MU_WAIT_LGKMCNT0() __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (0 << 8) | (3 << 14))
 
-template <int TS, bool NN, typename TSRC>
+template <int TS, bool SYM, typename TSRC>
 __global__ __launch_bounds__(NTHR) void k_gemm_bf16(GemmArgs A) {
     constexpr int BK = 64;
     constexpr int WT = TS / 2;
@@ -290,8 +325,6 @@ __global__ __launch_bounds__(NTHR) void k_gemm_bf16(GemmArgs A) {
     constexpr int LA = TS * BK;           // elements per operand tile
     constexpr int NBLK = LA * 2 / 1024;   // 1 KB direct-load blocks per operand tile
     constexpr int BPW = NBLK / 4;         // blocks per wave per operand
-    constexpr int RB = NN ? 1024 / (TS * 2) : 8;   // rows of a block (B operand)
-    constexpr int LPR = 64 / RB;                   // lanes per row (B operand)
     __shared__ __attribute__((aligned(1024))) bf16 sA0[LA];
     __shared__ __attribute__((aligned(1024))) bf16 sB0[LA];
     __shared__ __attribute__((aligned(1024))) bf16 sA1[LA];
@@ -304,9 +337,10 @@ __global__ __launch_bounds__(NTHR) void k_gemm_bf16(GemmArgs A) {
     const int local = wg - A.prefix[p];
     const int mode = A.mode;
     int ti, tj;
-    if (NN) apply_tile(local, P.mp / TS, P.np / TS, ti, tj);
-    else upper_tile(local, P.mp / TS, ti, tj);
+    if (SYM) upper_tile(local, P.mp / TS, ti, tj);
+    else apply_tile(local, P.mp / TS, P.np / TS, ti, tj);
 
+    // C = P Q^T, both operands with K contiguous
     const bf16 *pm, *qm;
     int ldp, ldq, K;
     if (mode == GM_GRAM) {
@@ -315,93 +349,55 @@ __global__ __launch_bounds__(NTHR) void k_gemm_bf16(GemmArgs A) {
         pm = qm = (const bf16*)P.a; ldp = ldq = P.mp; K = P.mp;
     } else {
         pm = (const bf16*)(A.use_b ? P.b : P.a); ldp = P.mp;
-        qm = (const bf16*)P.x[A.src]; ldq = P.np; K = P.mp;
+        qm = (const bf16*)P.xt[A.src]; ldq = P.mp; K = P.mp;
     }
     const bf16* pt = pm + (int64_t)ti * TS * ldp;
-    const bf16* qt = NN ? qm + tj * TS : qm + (int64_t)tj * TS * ldq;
+    const bf16* qt = qm + (int64_t)tj * TS * ldq;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm0 = (wave >> 1) * WT, wn0 = (wave & 1) * WT;
 
-    // Direct-load sources. Block b = s*4 + wave of an operand tile is 1 KB:
-    // K-contiguous: rows 8b .. 8b+7, lane -> row 8b + lane/8, physical chunk
-    //   lane%8 holds logical chunk (lane%8) ^ swz_k(row) = (lane%8) ^ (lane/8),
-    //   so block s is the block-0 address plus s*32 rows.
-    // N-contiguous (apply X tile): rows RB*b .. RB*b+RB-1, lane -> row RB*b + lane/LPR,
-    //   16-byte piece lane%LPR; its 32-byte group is XOR-ed with swz_n(row).
-    // Every source address is a wave-uniform base (scalar registers) plus a
-    // fixed 32-bit per-lane byte offset, so the loads use the saddr form.
+    // Direct-load sources. Block b = s*4 + wave of an operand tile is 1 KB =
+    // rows 8b .. 8b+7; lane -> row 8b + lane/8 and physical chunk lane%8, which
+    // holds logical chunk (lane%8) ^ swz_k(row) = (lane%8) ^ (lane/8). Block s
+    // is the block-0 address plus s*32 rows. Every source address is a
+    // wave-uniform base (scalar registers) plus a fixed 32-bit lane offset.
     const int ca = (lane & 7) ^ (lane >> 3);
     const uint32_t offA = (uint32_t)((8 * wave + (lane >> 3)) * ldp + ca * 8) * 2u;
-    const int64_t strideA = (int64_t)32 * ldp;   // elements between blocks s and s+1
-    uint32_t offB0, offB1;                        // NN with RB == 2: odd s swizzles differently
-    int64_t strideB;
-    if (NN) {
-        const int r0 = RB * wave + lane / LPR;     // row of block s = 0
-        const int pch = lane % LPR;
-        const int g_even = (pch >> 1) ^ swz_n(r0);
-        const int g_odd = (pch >> 1) ^ swz_n(r0 + RB * 4);
-        offB0 = (uint32_t)(r0 * ldq + (2 * g_even + (pch & 1)) * 8) * 2u;
-        offB1 = (uint32_t)((r0 + RB * 4) * ldq + (2 * g_odd + (pch & 1)) * 8) * 2u;
-        strideB = (int64_t)RB * 8 * ldq;           // elements between blocks s and s+2
-    } else {
-        offB0 = offB1 = (uint32_t)((8 * wave + (lane >> 3)) * ldq + ca * 8) * 2u;
-        strideB = (int64_t)32 * ldq;
-    }
-    const int64_t stepB = NN ? (int64_t)BK * ldq : BK;
+    const uint32_t offB = (uint32_t)((8 * wave + (lane >> 3)) * ldq + ca * 8) * 2u;
+    const int64_t strideA = (int64_t)32 * ldp, strideB = (int64_t)32 * ldq;
 
-    auto dma = [&](auto st, int kt) {
+    // direct load i of K step kt into stage S: i < BPW loads A block s = i,
+    // otherwise B block s = i - BPW
+    auto dma_one = [&](auto st, int kt, int i) {
         constexpr int S = decltype(st)::value;
-        bf16* sa = S ? sA1 : sA0;
-        bf16* sb = S ? sB1 : sB0;
-        const char* abase = (const char*)(pt + kt * BK);
-        const char* bbase = (const char*)(qt + kt * stepB);
+        const bool isA = i < BPW;
+        const int s = isA ? i : i - BPW;
+        bf16* dst = isA ? (S ? sA1 : sA0) : (S ? sB1 : sB0);
+        const char* src = isA ? (const char*)(pt + kt * BK) + s * strideA * 2 + offA
+                              : (const char*)(qt + kt * BK) + s * strideB * 2 + offB;
+        __builtin_amdgcn_global_load_lds((const void*)src, (LDSP void*)(dst + (s * 4 + wave) * 512), 16, 0, 0);
+    };
+    auto dma = [&](auto st, int kt) {
 #pragma unroll
-        for (int s = 0; s < BPW; ++s) {
-            const int blk = s * 4 + wave;
-            __builtin_amdgcn_global_load_lds((const void*)(abase + s * strideA * 2 + offA), (LDSP void*)(sa + blk * 512),
-                                             16, 0, 0);
-            const char* bsrc = NN ? bbase + (s >> 1) * strideB * 2 + ((s & 1) ? offB1 : offB0)
-                                  : bbase + s * strideB * 2 + offB0;
-            __builtin_amdgcn_global_load_lds((const void*)bsrc, (LDSP void*)(sb + blk * 512), 16, 0, 0);
-        }
+        for (int i = 0; i < 2 * BPW; ++i) dma_one(st, kt, i);
     };
 
-    // Fragment reads. K-contiguous operand: lane reads row (lane&15) of each
-    // 16-row fragment at logical chunk kh*4 + lane/16, whose physical chunk is
-    // that ^ swz_k(row) = ^ (lane&7): a lane constant per kh.
+    // Fragment reads: lane reads row (lane&15) of a 16-row fragment at logical
+    // chunk kh*4 + lane/16, stored at that ^ swz_k(row) = ^ (lane&7).
     const int swl = lane & 7;
     const int offk0 = (lane & 15) * BK + (((lane >> 4) ^ swl) << 3);
     const int offk1 = (lane & 15) * BK + (((4 + (lane >> 4)) ^ swl) << 3);
-    // N-contiguous operand (transposed reads): 16-lane group G reads rows
-    // kh*32 + 8G + rq (+4), columns of fragment fn at group (wn0/16 + fn) ^ swz_n(row),
-    // and swz_n(row) = rq | (G&1)<<2 for every kh and half.
-    const int Gq = lane >> 4, rq = (lane >> 2) & 3, q4 = lane & 3;
-    const int swn = rq | ((Gq & 1) << 2);
-    const int offn = (8 * Gq + rq) * TS + q4 * 4;
-
-    auto frags = [&](auto st, int kh, bf16x8 (&af)[F], bf16x8 (&bfv)[F]) {
+    auto read_a = [&](auto st, int kh, int fm) -> bf16x8 {
         constexpr int S = decltype(st)::value;
         const bf16* as = S ? sA1 : sA0;
+        return *(const bf16x8*)(as + (wm0 + fm * 16) * BK + (kh ? offk1 : offk0));
+    };
+    auto read_b = [&](auto st, int kh, int fn) -> bf16x8 {
+        constexpr int S = decltype(st)::value;
         const bf16* bs = S ? sB1 : sB0;
-        const int ok = kh ? offk1 : offk0;
-#pragma unroll
-        for (int fm = 0; fm < F; ++fm) af[fm] = *(const bf16x8*)(as + (wm0 + fm * 16) * BK + ok);
-        if (NN) {
-#pragma unroll
-            for (int fn = 0; fn < F; ++fn) {
-                // the XOR acts on the low three bits of the group index, so it
-                // is applied to the whole index (wn0/16 + fn), not to fn alone
-                const bf16* base = bs + offn + ((((wn0 >> 4) + fn) ^ swn) << 4) + kh * 32 * TS;
-                const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDSP i16x4*)base);
-                const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDSP i16x4*)(base + 4 * TS));
-                bfv[fn] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-            }
-        } else {
-#pragma unroll
-            for (int fn = 0; fn < F; ++fn) bfv[fn] = *(const bf16x8*)(bs + (wn0 + fn * 16) * BK + ok);
-        }
+        return *(const bf16x8*)(bs + (wn0 + fn * 16) * BK + (kh ? offk1 : offk0));
     };
 
     f32x4 acc[F][F];
@@ -410,16 +406,6 @@ __global__ __launch_bounds__(NTHR) void k_gemm_bf16(GemmArgs A) {
 #pragma unroll
         for (int j = 0; j < F; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    auto mma_rows = [&](int fm0, int fm1, const bf16x8 (&af)[F], const bf16x8 (&bfv)[F]) {
-#pragma unroll
-        for (int fm = 0; fm < F; ++fm)
-            if (fm >= fm0 && fm < fm1)
-#pragma unroll
-                for (int fn = 0; fn < F; ++fn)
-                    acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[fm], bfv[fn], acc[fm][fn], 0, 0, 0);
-    };
-
-    constexpr int NRD = NN ? 3 * F : 2 * F;  // fragment reads per k-half
     bf16x8 a0[F], b0[F], a1[F], b1[F];
     const int KT = K / BK;
 
@@ -427,25 +413,63 @@ __global__ __launch_bounds__(NTHR) void k_gemm_bf16(GemmArgs A) {
     MU_WAIT_VMCNT(0);
     __builtin_amdgcn_s_barrier();
     dma(Stage<1>{}, 1);
-    frags(Stage<0>{}, 0, a0, b0);
+#pragma unroll
+    for (int fn = 0; fn < F; ++fn) b0[fn] = read_b(Stage<0>{}, 0, fn);
+#pragma unroll
+    for (int fm = 0; fm < F; ++fm) a0[fm] = read_a(Stage<0>{}, 0, fm);
 
-    // Straight-line body, unrolled over the two stages so every LDS access
-    // names one array. K/BK is even (K is a multiple of the tile >= 128); the
+    // The body is emitted in the exact issue order wanted and fenced with
+    // sched_barrier, so the MFMA stream is never starved: with one wave per
+    // SIMD the matrix core drains within a couple of MFMAs of any gap.
+    // Phase 1: 2F groups of {one k-half-1 fragment read, F/2 MFMAs on k-half 0}
+    //          (B fragments first: the first MFMAs of phase 2 need all of them).
+    // Phase 2: HEAD rows of MFMAs on k-half 1; wait own loads; barrier; then 2F
+    //          groups of {a direct load of tile kt+2, one k-half-0 read of tile
+    //          kt+1, the remaining k-half-1 MFMAs}.
+    // K/BK is even (K is a multiple of the tile >= 128) and the body is
+    // unrolled over the two stages, so every LDS access names one array; the
     // prefetch index is clamped, so the last two prefetches reload the final
     // tile into a stage nobody reads again instead of branching.
+    constexpr int HEAD = F / 4 > 0 ? F / 4 : 1;
+    constexpr int G = 2 * F;                 // fragment reads per k-half
+    constexpr int NMF2 = (F - HEAD) * F;     // MFMAs after the barrier
+    constexpr int NDMA = 2 * BPW;            // direct loads per K step
+    auto mma1 = [&](int idx, const bf16x8 (&af)[F], const bf16x8 (&bfv)[F]) {
+        const int fm = idx / F, fn = idx % F;
+#pragma unroll
+        for (int r = 0; r < F; ++r)
+#pragma unroll
+            for (int c = 0; c < F; ++c)
+                if (r == fm && c == fn)
+                    acc[r][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[r], bfv[c], acc[r][c], 0, 0, 0);
+    };
     auto half = [&](auto st, int kt) {
         constexpr int S = decltype(st)::value;
-        // phase 1: k-half 1 fragments of tile kt against the MFMAs of k-half 0
-        frags(st, 1, a1, b1);
-        mma_rows(0, F, a0, b0);
-        // phase 2: tile kt+1 landed (own loads + barrier), stage S is free
-        constexpr int HEAD = F / 4 > 0 ? F / 4 : 1;
-        mma_rows(0, HEAD, a1, b1);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            if (g < F) b1[g] = read_b(st, 1, g);
+            else a1[g - F] = read_a(st, 1, g - F);
+#pragma unroll
+            for (int j = 0; j < F * F / G; ++j) mma1(g * (F * F / G) + j, a0, b0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int j = 0; j < HEAD * F; ++j) mma1(j, a1, b1);
+        __builtin_amdgcn_sched_barrier(0);
         MU_WAIT_VMCNT(0);
         __builtin_amdgcn_s_barrier();
-        dma(st, min(kt + 2, KT - 1));
-        frags(Stage<1 - S>{}, 0, a0, b0);
-        mma_rows(HEAD, F, a1, b1);
+        const int kn = min(kt + 2, KT - 1);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+#pragma unroll
+            for (int i = 0; i < NDMA; ++i)
+                if (i * G / NDMA == g) dma_one(st, kn, i);
+            if (g < F) b0[g] = read_b(Stage<1 - S>{}, 0, g);
+            else a0[g - F] = read_a(Stage<1 - S>{}, 0, g - F);
+#pragma unroll
+            for (int j = g * NMF2 / G; j < (g + 1) * NMF2 / G; ++j) mma1(HEAD * F + j, a1, b1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     };
     for (int kt = 0; kt < KT; kt += 2) {
         half(Stage<0>{}, kt);
@@ -458,17 +482,17 @@ __global__ __launch_bounds__(NTHR) void k_gemm_bf16(GemmArgs A) {
 }
 
 // ---------------------------------------------------------------------------
-// fp32 kernel: 64x64 tiles, BK = 32, v_mfma_f32_16x16x4_f32. Within a block
-// of 16 k, lane l holds k = 4*(l>>4) + s in MFMA s for both operands (any
-// permutation of k shared by both operands leaves the sum unchanged).
+// fp32 kernel: 64x64 tiles, BK = 32, v_mfma_f32_16x16x4_f32, operands staged
+// through registers into padded LDS rows. Within a block of 16 k, lane l holds
+// k = 4*(l>>4) + s in MFMA s for both operands (any permutation of k shared by
+// both operands leaves the sum unchanged).
 // ---------------------------------------------------------------------------
-template <bool NN, typename TSRC>
+template <bool SYM, typename TSRC>
 __global__ __launch_bounds__(NTHR) void k_gemm_f32(GemmArgs A) {
     constexpr int TS = 64, BK = 32, WT = 32, F = 2;
-    constexpr int SPK = BK + 4, SPN = TS + 4;
+    constexpr int SPK = BK + 4;
     constexpr int LA = TS * SPK;
-    constexpr int LB = NN ? BK * SPN : TS * SPK;
-    __shared__ __attribute__((aligned(16))) float smem[2 * (LA + LB)];
+    __shared__ __attribute__((aligned(16))) float smem[2 * 2 * LA];
 
     const int wg = xcd_remap(blockIdx.x, gridDim.x);
     if (wg >= A.total_tiles) return;
@@ -477,8 +501,8 @@ __global__ __launch_bounds__(NTHR) void k_gemm_f32(GemmArgs A) {
     const int local = wg - A.prefix[p];
     const int mode = A.mode;
     int ti, tj;
-    if (NN) apply_tile(local, P.mp / TS, P.np / TS, ti, tj);
-    else upper_tile(local, P.mp / TS, ti, tj);
+    if (SYM) upper_tile(local, P.mp / TS, ti, tj);
+    else apply_tile(local, P.mp / TS, P.np / TS, ti, tj);
 
     const float *pm, *qm;
     int ldp, ldq, K;
@@ -488,10 +512,10 @@ __global__ __launch_bounds__(NTHR) void k_gemm_f32(GemmArgs A) {
         pm = qm = (const float*)P.a; ldp = ldq = P.mp; K = P.mp;
     } else {
         pm = (const float*)(A.use_b ? P.b : P.a); ldp = P.mp;
-        qm = (const float*)P.x[A.src]; ldq = P.np; K = P.mp;
+        qm = (const float*)P.xt[A.src]; ldq = P.mp; K = P.mp;
     }
     const float* pt = pm + (int64_t)ti * TS * ldp;
-    const float* qt = NN ? qm + tj * TS : qm + (int64_t)tj * TS * ldq;
+    const float* qt = qm + (int64_t)tj * TS * ldq;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm0 = (wave >> 1) * WT, wn0 = (wave & 1) * WT;
@@ -503,19 +527,17 @@ __global__ __launch_bounds__(NTHR) void k_gemm_f32(GemmArgs A) {
         for (int s = 0; s < 2; ++s) {
             const int q = s * NTHR + tid;
             ga[s] = *gp((const f32x4*)(pt + (int64_t)(q >> 3) * ldp + k0 + (q & 7) * 4));
-            if (NN) gb[s] = *gp((const f32x4*)(qt + (int64_t)(k0 + (q >> 4)) * ldq + (q & 15) * 4));
-            else gb[s] = *gp((const f32x4*)(qt + (int64_t)(q >> 3) * ldq + k0 + (q & 7) * 4));
+            gb[s] = *gp((const f32x4*)(qt + (int64_t)(q >> 3) * ldq + k0 + (q & 7) * 4));
         }
     };
     auto sstore = [&](int stage) {
-        float* as = smem + stage * (LA + LB);
+        float* as = smem + stage * 2 * LA;
         float* bs = as + LA;
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             const int q = s * NTHR + tid;
             *(f32x4*)(as + (q >> 3) * SPK + (q & 7) * 4) = ga[s];
-            if (NN) *(f32x4*)(bs + (q >> 4) * SPN + (q & 15) * 4) = gb[s];
-            else *(f32x4*)(bs + (q >> 3) * SPK + (q & 7) * 4) = gb[s];
+            *(f32x4*)(bs + (q >> 3) * SPK + (q & 7) * 4) = gb[s];
         }
     };
 
@@ -531,7 +553,7 @@ __global__ __launch_bounds__(NTHR) void k_gemm_f32(GemmArgs A) {
     __syncthreads();
     for (int kt = 0; kt < KT; ++kt) {
         if (kt + 1 < KT) gload(kt + 1);
-        const float* as = smem + (kt & 1) * (LA + LB);
+        const float* as = smem + (kt & 1) * 2 * LA;
         const float* bs = as + LA;
 #pragma unroll
         for (int kb = 0; kb < BK / 16; ++kb) {
@@ -540,14 +562,7 @@ __global__ __launch_bounds__(NTHR) void k_gemm_f32(GemmArgs A) {
 #pragma unroll
             for (int fm = 0; fm < F; ++fm) af[fm] = *(const f32x4*)(as + (wm0 + fm * 16 + (lane & 15)) * SPK + kk);
 #pragma unroll
-            for (int fn = 0; fn < F; ++fn) {
-                if (NN) {
-#pragma unroll
-                    for (int s = 0; s < 4; ++s) bfv[fn][s] = bs[(kk + s) * SPN + wn0 + fn * 16 + (lane & 15)];
-                } else {
-                    bfv[fn] = *(const f32x4*)(bs + (wn0 + fn * 16 + (lane & 15)) * SPK + kk);
-                }
-            }
+            for (int fn = 0; fn < F; ++fn) bfv[fn] = *(const f32x4*)(bs + (wn0 + fn * 16 + (lane & 15)) * SPK + kk);
 #pragma unroll
             for (int s = 0; s < 4; ++s)
 #pragma unroll
@@ -562,11 +577,11 @@ __global__ __launch_bounds__(NTHR) void k_gemm_f32(GemmArgs A) {
     epilogue<float, TSRC, F>(A, P, ti, tj, TS, wm0, wn0, acc, smem + wave * 16 * (WT + 4));
 }
 
-template <int TS, bool NN>
+template <int TS, bool SYM>
 hipError_t launch_bf16_t(const GemmArgs& a, hipStream_t s) {
     const unsigned grid = (unsigned)((a.total_tiles + 7) / 8 * 8);
-    if (a.src_dtype == DT_BF16) hipLaunchKernelGGL((k_gemm_bf16<TS, NN, bf16>), dim3(grid), dim3(NTHR), 0, s, a);
-    else hipLaunchKernelGGL((k_gemm_bf16<TS, NN, float>), dim3(grid), dim3(NTHR), 0, s, a);
+    if (a.src_dtype == DT_BF16) hipLaunchKernelGGL((k_gemm_bf16<TS, SYM, bf16>), dim3(grid), dim3(NTHR), 0, s, a);
+    else hipLaunchKernelGGL((k_gemm_bf16<TS, SYM, float>), dim3(grid), dim3(NTHR), 0, s, a);
     return hipGetLastError();
 }
 
@@ -574,21 +589,21 @@ hipError_t launch_bf16_t(const GemmArgs& a, hipStream_t s) {
 
 hipError_t launch_gemm_bf16(const GemmArgs& a, int tile, hipStream_t s) {
     if (a.total_tiles <= 0) return hipSuccess;
-    const bool nn = a.mode == GM_APPLY || a.mode == GM_APPLY_LAST;
-    if (tile == 256) return nn ? launch_bf16_t<256, true>(a, s) : launch_bf16_t<256, false>(a, s);
-    if (tile == 128) return nn ? launch_bf16_t<128, true>(a, s) : launch_bf16_t<128, false>(a, s);
+    const bool sym = a.mode == GM_GRAM || a.mode == GM_GRAM2;
+    if (tile == 256) return sym ? launch_bf16_t<256, true>(a, s) : launch_bf16_t<256, false>(a, s);
+    if (tile == 128) return sym ? launch_bf16_t<128, true>(a, s) : launch_bf16_t<128, false>(a, s);
     return hipErrorInvalidValue;
 }
 
 hipError_t launch_gemm_f32(const GemmArgs& a, hipStream_t s) {
     if (a.total_tiles <= 0) return hipSuccess;
-    const bool nn = a.mode == GM_APPLY || a.mode == GM_APPLY_LAST;
+    const bool sym = a.mode == GM_GRAM || a.mode == GM_GRAM2;
     const unsigned grid = (unsigned)((a.total_tiles + 7) / 8 * 8);
     if (a.src_dtype == DT_BF16) {
-        if (nn) hipLaunchKernelGGL((k_gemm_f32<true, bf16>), dim3(grid), dim3(NTHR), 0, s, a);
+        if (sym) hipLaunchKernelGGL((k_gemm_f32<true, bf16>), dim3(grid), dim3(NTHR), 0, s, a);
         else hipLaunchKernelGGL((k_gemm_f32<false, bf16>), dim3(grid), dim3(NTHR), 0, s, a);
     } else {
-        if (nn) hipLaunchKernelGGL((k_gemm_f32<true, float>), dim3(grid), dim3(NTHR), 0, s, a);
+        if (sym) hipLaunchKernelGGL((k_gemm_f32<true, float>), dim3(grid), dim3(NTHR), 0, s, a);
         else hipLaunchKernelGGL((k_gemm_f32<false, float>), dim3(grid), dim3(NTHR), 0, s, a);
     }
     return hipGetLastError();
