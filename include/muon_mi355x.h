@@ -50,6 +50,11 @@ extern "C" {
 #define MU_ERR_WORKSPACE 4   /* workspace null, too small, or misaligned */
 #define MU_ERR_HIP 5         /* a HIP call failed; detail in mu_last_error() */
 
+/* Largest accepted rows or cols of a matrix (MU_ERR_INVALID_ARG above it): a
+ * 256-row strip of the padded long side stays below 2 GiB, the range that the
+ * GEMM kernels address with 32-bit offsets. */
+#define MU_MAX_DIM (1 << 21)
+
 /*
  * One 2-D weight under the Muon rule.
  *
@@ -188,9 +193,9 @@ int mu_version(void);
  */
 #define MU_K_PREP 0      /* momentum + Nesterov + U write + norm partials */
 #define MU_K_NORM 1      /* per-head norm finalisation */
-#define MU_K_GRAM 2      /* X X^T (upper tiles, mirrored) */
-#define MU_K_GRAM2 3     /* A A^T for the quintic term */
-#define MU_K_APPLY 4     /* a X + b A X (last step fuses the update) */
+#define MU_K_GRAM 2      /* X X^T (upper tiles, mirrored); writes B = aI + bA on cubic steps */
+#define MU_K_GRAM2 3     /* A A^T for the quintic term; writes B = aI + bA + cA^2 */
+#define MU_K_APPLY 4     /* B X (last step fuses the update) */
 #define MU_K_FINISH 5    /* update when ns_steps == 0 */
 #define MU_K_ADAMW 6     /* AdamW */
 #define MU_K_COUNT 7

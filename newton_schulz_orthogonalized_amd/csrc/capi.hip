@@ -450,6 +450,7 @@ int run_pipeline(Plan& pl, char* ws, const mu_muon_hparams* hp, int src_dt, bool
             ga.ca = co[k].a;
             ga.cb = co[k].b;
             ga.cc = co[k].c;
+            ga.use_b = quint ? 1 : 0;   // the Gram writes B itself on cubic steps
             ga.lr = hp->lr;
             ga.wd = hp->weight_decay;
             ga.with_update = step_mode ? 1 : 0;
@@ -478,7 +479,6 @@ int run_pipeline(Plan& pl, char* ws, const mu_muon_hparams* hp, int src_dt, bool
             ap.prefix = apply_pf[gi];
             ap.total_tiles = g.apply_prefix.back();
             ap.first = first ? 1 : 0;
-            ap.use_b = quint ? 1 : 0;
             rc = timed_launch(MU_K_APPLY, aflops, abytes, s, [&] { return launch(ap); }, "apply launch");
             if (rc) return rc;
         }
@@ -500,7 +500,7 @@ int validate_mats(const mu_matrix* m, int32_t n, std::vector<Item>& items, int& 
         if (x.dtype != dt) return fail(MU_ERR_DTYPE, "matrix %d: all matrices of one call must share a dtype", i);
         if (!x.param || !x.grad || !x.momentum) return fail(MU_ERR_INVALID_ARG, "matrix %d: null param/grad/momentum", i);
         if (x.rows <= 0 || x.cols <= 0) return fail(MU_ERR_INVALID_ARG, "matrix %d: rows and cols must be > 0", i);
-        if (x.rows > (1 << 30) || x.cols > (1 << 30)) return fail(MU_ERR_INVALID_ARG, "matrix %d: dimension too large", i);
+        if (x.rows > MU_MAX_DIM || x.cols > MU_MAX_DIM) return fail(MU_ERR_INVALID_ARG, "matrix %d: dimension above %d", i, MU_MAX_DIM);
         if (x.num_heads < 1 || x.rows % x.num_heads != 0)
             return fail(MU_ERR_INVALID_ARG, "matrix %d: num_heads (%d) must be >= 1 and divide rows (%lld)", i, x.num_heads,
                         (long long)x.rows);
@@ -546,7 +546,7 @@ int validate_ortho(const mu_ortho* xs, int32_t n, std::vector<Item>& items, int&
         if (x.dtype != dt) return fail(MU_ERR_DTYPE, "input %d: all inputs of one call must share a dtype", i);
         if (!x.input || !x.output) return fail(MU_ERR_INVALID_ARG, "input %d: null input/output", i);
         if (x.rows <= 0 || x.cols <= 0) return fail(MU_ERR_INVALID_ARG, "input %d: rows and cols must be > 0", i);
-        if (x.rows > (1 << 30) || x.cols > (1 << 30)) return fail(MU_ERR_INVALID_ARG, "input %d: dimension too large", i);
+        if (x.rows > MU_MAX_DIM || x.cols > MU_MAX_DIM) return fail(MU_ERR_INVALID_ARG, "input %d: dimension above %d", i, MU_MAX_DIM);
         if (x.num_heads < 1 || x.rows % x.num_heads != 0)
             return fail(MU_ERR_INVALID_ARG, "input %d: num_heads (%d) must be >= 1 and divide rows", i, x.num_heads);
         const size_t es = dtype_size(x.dtype);

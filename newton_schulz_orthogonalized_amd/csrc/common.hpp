@@ -35,10 +35,13 @@ __device__ __forceinline__ MU_GLOBAL T* gp(T* p) {
 // is the wide orientation the iteration runs in: m = min(hr, hc) rows and
 // n = max(hr, hc) cols, X = U when hr <= hc and X = U^T otherwise ("tall").
 // The workspace keeps X (mp x np) and its transpose X^T (np x mp), so both
-// products of a step contract over the contiguous dimension of both operands:
-// the Gram X X^T reads X twice, the apply A X reads A and X^T. Buffers are
-// padded with zeros to multiples of the GEMM tile; zero padding is preserved
-// by every step, so the GEMM kernels need no bounds checks.
+// products of a step contract over the K dimension of both operands stored
+// K-contiguously: the Gram X X^T reads X twice, the apply B X reads B and X^T.
+// Buffers are padded with zeros to multiples of the GEMM tile; zero padding is
+// preserved by every step, so the GEMM kernels need no bounds checks.
+//
+// Storage of the workspace operands (X, X^T, A, B): with bf16 Newton-Schulz
+// they are K-blocked (see kb_off), with fp32 Newton-Schulz plain row-major.
 // ---------------------------------------------------------------------------
 struct NsProb {
     const void* src;   // gradient (step) or input (orthogonalise), U-space
@@ -55,8 +58,8 @@ struct NsProb {
     int32_t pad0;
     void* x[2];        // ping-pong X buffers, mp x np, NS element type
     void* xt[2];       // their transposes, np x mp
-    void* a;           // Gram matrix, mp x mp
-    void* b;           // b*A + c*A^2 (quintic steps), mp x mp, or null
+    void* a;           // a I + b A (cubic steps) or A = X X^T (quintic steps), mp x mp
+    void* b;           // a I + b A + c A^2 (quintic steps), mp x mp, or null
     float* partials;   // per prep-tile sums of squares
     float* fold;       // 1 / (||U||_F + eps), written by the norm kernel
     float* norm_out;   // optional ||U||_F
@@ -82,6 +85,24 @@ __device__ inline int find_prob(const int* prefix, int nprobs, int t) {
 __device__ inline int xcd_remap(int wg, int grid) {
     if ((grid & 7) != 0) return wg;
     return (wg & 7) * (grid >> 3) + (wg >> 3);
+}
+
+// Element (r, k) of a K-blocked operand with R rows (R a multiple of 16, K a
+// multiple of 32): 1 KB blocks of 16 rows x 32 k, ordered panel-major (block
+// of k-panel k/32 and row group r/16 at index (k/32)*(R/16) + r/16); inside a
+// block, the 16-byte chunk of k (k%32)/8 of row r%16 sits at byte
+// 16*(16*((k%32)/8) + r%16). A block is the lane order of one 16x16x32 MFMA
+// fragment, and the TS x 32 slice of a TS-row tile is one contiguous run.
+__device__ inline int64_t kb_off(int r, int k, int R) {
+    return ((int64_t)(k >> 5) * (R >> 4) + (r >> 4)) * 512 + ((k & 31) >> 3) * 128 + (r & 15) * 8 + (k & 7);
+}
+// Offset of element (r, k) of a workspace operand with R rows and K columns:
+// K-blocked for bf16, row-major for fp32. k is a multiple of 4 whenever four
+// or eight consecutive elements are accessed at once.
+template <typename TX>
+__device__ inline int64_t op_off(int r, int k, int R, int K) {
+    if constexpr (sizeof(TX) == 2) return kb_off(r, k, R);
+    else return (int64_t)r * K + k;
 }
 
 __device__ inline float bf2f(bf16 v) { return (float)v; }

@@ -1,9 +1,8 @@
 // HBM-bound kernels of the Muon step and the AdamW step (gfx950).
 //
 //  k_prep    momentum EMA + Nesterov blend, write U into the workspace as X
-//            (wide orientation) and X^T with zero padding (one of the two
-//            through an LDS transpose), and one sum of squares per 64x64 tile
-//            (fixed order).
+//            (wide orientation) and X^T with zero padding, through an LDS
+//            tile, and one sum of squares per 64x64 tile (fixed order).
 //  k_norm    per (matrix, head): fixed-order sum of the tile partials,
 //            fold = 1/(||U||_F + eps).
 //  k_finish  ns_steps == 0: O = fold * X0, then the update (or the output).
@@ -134,9 +133,12 @@ __device__ inline void make_u(const NsProb& P, int r, int c0, bool with_m, bool 
 }
 
 // Tiles run over the buffer that has U's orientation (X for wide blocks, X^T
-// for tall ones): each 64x64 U tile is written there directly and, through an
-// LDS transpose, into the other buffer. Out-of-range elements are written as
-// zeros, which is the padding every later step relies on.
+// for tall ones): U is computed into an LDS tile, then written into that buffer
+// and, transposed, into the other one. Out-of-range elements are written as
+// zeros, which is the padding every later step relies on. With bf16
+// Newton-Schulz both buffers are K-blocked: a 64x64 tile is 2 panels x 4 row
+// groups of 1 KB blocks, and thread q of a pass writes 16-byte chunk q, so a
+// wave stores one whole block.
 template <typename TS, typename TX>
 __global__ __launch_bounds__(NTHR) void k_prep(PrepArgs A) {
     __shared__ float tile[T][T + 1];
@@ -146,11 +148,11 @@ __global__ __launch_bounds__(NTHR) void k_prep(PrepArgs A) {
     const NsProb& P = A.probs[p];
     const int local = t - A.prefix[p];
     const bool wide = !P.tall;
-    const int dpitch = wide ? P.np : P.mp;   // U-oriented buffer: X (wide) or X^T (tall)
-    const int tpitch = wide ? P.mp : P.np;   // the other one
+    const int RD = wide ? P.mp : P.np;   // rows of the U-oriented buffer
+    const int KD = wide ? P.np : P.mp;   // its columns = rows of the other one
     TX* D = (TX*)(wide ? P.x[0] : P.xt[0]);
     TX* Tt = (TX*)(wide ? P.xt[0] : P.x[0]);
-    const int tiles_n = dpitch / T;
+    const int tiles_n = KD / T;
     const int ti = local / tiles_n, tj = local - ti * tiles_n;
     const int tid = threadIdx.x;
     const int rr = tid >> 4, cc = (tid & 15) * 4;
@@ -166,16 +168,41 @@ __global__ __launch_bounds__(NTHR) void k_prep(PrepArgs A) {
             ss += u[e] * u[e];
             tile[rr + 16 * k][cc + e] = u[e];
         }
-        store_x4<TX>(D + (int64_t)r * dpitch + c0, u);
+        if constexpr (sizeof(TX) == 4) store_x4<TX>(D + (int64_t)r * KD + c0, u);
     }
     __syncthreads();
+    if constexpr (sizeof(TX) == 2) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const int a = rr + 16 * k;
-        float v[4];
+        for (int pass = 0; pass < 2; ++pass) {
+            const int q = pass * NTHR + tid;
+            const int pl = q >> 8, g = (q >> 6) & 3, c = (q >> 4) & 3, r16 = q & 15;
+            // D: row g*16 + r16, columns pl*32 + c*8 .. +7 of the tile
+            {
+                const int row = g * 16 + r16, col = pl * 32 + c * 8;
+                bf16x8 o;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = tile[cc + e][a];
-        store_x4<TX>(Tt + (int64_t)(tj * T + a) * tpitch + ti * T + cc, v);
+                for (int e = 0; e < 8; ++e) o[e] = (bf16)tile[row][col + e];
+                *(bf16x8*)(D + kb_off(ti * T + row, tj * T + col, RD)) = o;
+            }
+            // the other buffer: row (= tile column) g*16 + r16, columns (= tile
+            // rows) pl*32 + c*8 .. +7
+            {
+                const int row = g * 16 + r16, col = pl * 32 + c * 8;
+                bf16x8 o;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) o[e] = (bf16)tile[col + e][row];
+                *(bf16x8*)(Tt + kb_off(tj * T + row, ti * T + col, KD)) = o;
+            }
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int a = rr + 16 * k;
+            float v[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = tile[cc + e][a];
+            store_x4<TX>(Tt + (int64_t)(tj * T + a) * RD + ti * T + cc, v);
+        }
     }
     const float s = block_sum(ss, red);
     if (tid == 0) P.partials[local] = s;
@@ -234,7 +261,7 @@ __global__ __launch_bounds__(NTHR) void k_finish(FinishArgs A) {
         for (int k = 0; k < 4; ++k) {
             const int r = ti * T + rr + 16 * k, c0 = tj * T + cc;
             float o[4];
-            load_x4<TX>(X + (int64_t)r * P.np + c0, o);
+            load_x4<TX>(X + op_off<TX>(r, c0, P.mp, P.np), o);
 #pragma unroll
             for (int e = 0; e < 4; ++e) o[e] *= f;
             emit(r, c0, o);
@@ -244,7 +271,7 @@ __global__ __launch_bounds__(NTHR) void k_finish(FinishArgs A) {
         for (int k = 0; k < 4; ++k) {
             const int a = rr + 16 * k;
             float v[4];
-            load_x4<TX>(X + (int64_t)(ti * T + a) * P.np + tj * T + cc, v);
+            load_x4<TX>(X + op_off<TX>(ti * T + a, tj * T + cc, P.mp, P.np), v);
 #pragma unroll
             for (int e = 0; e < 4; ++e) tile[cc + e][a] = v[e] * f;
         }

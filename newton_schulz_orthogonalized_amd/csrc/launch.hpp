@@ -46,7 +46,7 @@ struct GemmArgs {
     int mode;
     int src;             // which x[] buffer holds the current X
     int first;           // apply the fold (1/||U||) of the first step
-    int use_b;           // apply multiplies by B (quintic) instead of A
+    int use_b;           // quintic step: Gram writes A, the A^2 pass writes B, apply reads b
     int with_update;     // last step: 1 updates param, 0 writes out
     int src_dtype;       // element type of param/out
     float ca, cb, cc;    // step coefficients

@@ -2,11 +2,12 @@
 //
 // One Newton-Schulz step on the wide X (m x n, m <= n) is
 //     A  = X X^T                       (Gram, m x m, symmetric)
-//     B  = b A + c A A^T               (only for steps with a quintic term)
-//     X' = a X + b A X   or   a X + B X
+//     X' = a X + b A X + c A A X  =  B X,   B = a I + b A + c A A^T
 // (MuonClip Optimizer page, section "Newton-Schulz Orthogonalization", gives
-// the cubic step with a = 1.5, b = -0.5, written as X (X^T X), which equals
-// (X X^T) X; the Gram side is kept on the short dimension.)
+// the cubic step with a = 1.5, b = -0.5, c = 0, written as X (X^T X), which
+// equals (X X^T) X; the Gram side is kept on the short dimension.) B is formed
+// in the Gram epilogue (cubic steps) or in an A A^T pass (quintic steps), so
+// the apply is a plain product.
 //
 // All products are grouped GEMMs over every (matrix, head) problem of a call:
 // one launch per mode covers all problems, each workgroup finds its problem
@@ -14,17 +15,19 @@
 // neighbouring tiles run on the same XCD (shared L2).
 //
 // Every product is "NT", C = P Q^T with both operands K-contiguous: the Gram
-// X X^T reads X twice; the apply A X reads A and the transposed copy X^T that
-// the previous step's epilogue (or the prep kernel) wrote. Gram products only
-// compute tiles on or above the diagonal and also store the transposed tile.
+// X X^T reads X twice; the apply B X reads B (symmetric) and the transposed
+// copy X^T that the previous step's epilogue (or the prep kernel) wrote. Gram
+// products only compute tiles on or above the diagonal and also store the
+// transposed tile.
 //
 // bf16: v_mfma_f32_16x16x32_bf16, fp32 accumulation, 256x256 or 128x128
-// workgroup tiles, BK = 64, 4 waves in 2x2 (128x128 per wave for 256 tiles),
-// operands moved with direct-to-LDS loads into two LDS stages.
-// fp32: v_mfma_f32_16x16x4_f32, 64x64 tiles, BK = 32.
+// workgroup tiles, BK = 32, 4 waves in 2x2 (128x128 per wave for 256 tiles),
+// K-blocked operands moved with direct-to-LDS buffer loads through a ring of
+// four LDS slots.
+// fp32: v_mfma_f32_16x16x4_f32, 64x64 tiles, BK = 32, row-major operands.
 //
 // Epilogue: accumulators are staged per wave through LDS in 16-row strips,
-// then stored with 16-byte row-major accesses and, for transposed outputs
+// then stored with 16-byte accesses in a row pass and, for transposed outputs
 // (Gram mirror, X'^T, or a tall weight), a column pass. It applies the fold
 // 1/||U||_F of the first step (so the normalised X0 is never materialised), the
 // step coefficients, and on the last step the decoupled-weight-decay update
@@ -38,11 +41,6 @@ namespace {
 
 constexpr int NTHR = 256;
 
-// XOR swizzle of the eight 16-byte chunks of a 128-byte K-contiguous LDS row:
-// physical chunk = logical chunk ^ (row & 7). A fragment read (16 rows at one
-// logical chunk) then runs at the rate of a linear ds_read_b128 on gfx950, as
-// measured; variants that also flip on row bit 3 ran about 1.45x slower.
-__device__ __forceinline__ int swz_k(int r) { return r & 7; }
 
 
 // ---------------------------------------------------------------------------
@@ -155,25 +153,6 @@ __device__ __forceinline__ void store8(TX* p, const float* v) {
     }
 }
 
-// Eight consecutive X-space values of a bf16 or float buffer, held raw.
-template <typename TX>
-struct Vec8;
-template <>
-struct Vec8<bf16> {
-    bf16x8 v;
-    __device__ __forceinline__ void load(const bf16* p) { v = *gp((const bf16x8*)p); }
-    __device__ __forceinline__ float get(int e) const { return (float)v[e]; }
-};
-template <>
-struct Vec8<float> {
-    f32x4 a, b;
-    __device__ __forceinline__ void load(const float* p) {
-        a = gp((const f32x4*)p)[0];
-        b = gp((const f32x4*)p)[1];
-    }
-    __device__ __forceinline__ float get(int e) const { return e < 4 ? a[e] : b[e - 4]; }
-};
-
 // Order LDS accesses of this wave (a wave's LDS operations complete in issue
 // order; only compiler reordering has to be prevented).
 __device__ __forceinline__ void wave_lds_sync() {
@@ -186,45 +165,47 @@ __device__ __forceinline__ void wave_lds_sync() {
 // Epilogue shared by the bf16 and fp32 kernels. The accumulator layout is the
 // 16x16 MFMA one: lane l holds C[4*(l>>4) + e][l & 15] of each fragment.
 // `st` is this wave's LDS strip of 16 x (F*16 + 4) floats, not otherwise in
-// use; each wave stages only its own strip, so syncs are wave-local. In the
-// apply modes the X values of the whole tile are requested before the first
-// strip, so their latency is paid once.
+// use; each wave stages only its own strip, so syncs are wave-local.
+//
+// What each mode stores (f = 1/(||U||_F + eps) on the first step, else 1):
+//   Gram, cubic step     B = a I + b f^2 (X X^T)      -> P.a (mirrored)
+//   Gram, quintic step   A = f^2 (X X^T)              -> P.a (mirrored)
+//   A^2 pass             B = a I + b A + c A A^T      -> P.b (mirrored)
+//   apply                X' = f (B X)                 -> X', X'^T
+//   last apply           O = f (B X) -> parameter update (or output)
+// Folding a I into B keeps X itself out of the apply epilogue; padding stays
+// zero because a padded row of X' is a*0 + (rows of A that are zero).
+//
+// Row pass: lane -> row idx%16 and 8 consecutive columns, so with the K-blocked
+// layout a wave writes whole 1 KB blocks. Column pass (transposed outputs):
+// lane -> column and 8 consecutive rows, again 16 columns per 256 bytes.
 // ---------------------------------------------------------------------------
 template <typename TX, typename TS, int F>
 __device__ __forceinline__ void epilogue(const GemmArgs& A, const NsProb& P, int ti, int tj, int TS_, int wm0,
                                          int wn0, f32x4 (&acc)[F][F], float* st) {
     constexpr int WT = F * 16;
     constexpr int SP = WT + 4;
-    constexpr int PASSES = (16 * WT / 8) / 64;
+    constexpr int PASSES = WT / 32;            // row pass: 16 rows x 32 columns per pass
+    constexpr int CPASSES = (2 * WT) / 64;     // column pass: WT columns x 2 halves
     const int lane = threadIdx.x & 63;
     const int mode = A.mode;
     const float f = A.first ? P.fold[0] : 1.f;
     const bool gram = mode == GM_GRAM || mode == GM_GRAM2;
-    const bool apply = !gram;
+    const bool diag = gram && ti == tj;
     const bool mirror = gram && ti != tj;
     const bool last = mode == GM_APPLY_LAST;
     // transposed outputs: the Gram mirror, X'^T for the next apply, or the
     // parameter of a tall block on the last step
-    const bool trans_out = mirror || (apply && !last) || (last && P.tall);
+    const bool trans_out = mirror || (!gram && !last) || (last && P.tall);
     const int row_base = ti * TS_ + wm0, col_base = tj * TS_ + wn0;
     const int mp = P.mp, np = P.np;
-    const float cb_eff = A.use_b ? 1.f : A.cb;
-    TX* gdst = (TX*)(mode == GM_GRAM ? P.a : P.b);
-    const TX* xsrc = (const TX*)P.x[A.src];
+    // Gram scale and diagonal term
+    float gs = f * f, gd = 0.f;
+    if (mode == GM_GRAM && !A.use_b) { gs = A.cb * f * f; gd = A.ca; }
+    if (mode == GM_GRAM2) { gs = A.cc; gd = A.ca; }
+    TX* gdst = (TX*)(mode == GM_GRAM2 ? P.b : P.a);
     TX* xdst = (TX*)P.x[A.src ^ 1];
     TX* xtdst = (TX*)P.xt[A.src ^ 1];
-
-    Vec8<TX> xv[F][PASSES];
-    if (apply) {
-#pragma unroll
-        for (int fm = 0; fm < F; ++fm)
-#pragma unroll
-            for (int pass = 0; pass < PASSES; ++pass) {
-                const int idx = pass * 64 + lane;
-                const int rr = idx / (WT / 8), c8 = (idx % (WT / 8)) * 8;
-                xv[fm][pass].load(xsrc + (int64_t)(row_base + fm * 16 + rr) * np + col_base + c8);
-            }
-    }
 
 #pragma clang loop unroll(full)
     for (int fm = 0; fm < F; ++fm) {
@@ -234,34 +215,37 @@ __device__ __forceinline__ void epilogue(const GemmArgs& A, const NsProb& P, int
 #pragma unroll
             for (int e = 0; e < 4; ++e) st[(4 * (lane >> 4) + e) * SP + fn * 16 + (lane & 15)] = acc[fm][fn][e];
         wave_lds_sync();
-        // row-major pass: 8 consecutive columns per lane
 #pragma unroll
         for (int pass = 0; pass < PASSES; ++pass) {
-            const int idx = pass * 64 + lane;
-            const int rr = idx / (WT / 8), c8 = (idx % (WT / 8)) * 8;
+            const int rr = lane & 15, c8 = pass * 32 + (lane >> 4) * 8;
             float v[8];
             {
-                const f32x4 a = *(const f32x4*)(st + rr * SP + c8);
-                const f32x4 b = *(const f32x4*)(st + rr * SP + c8 + 4);
+                const f32x4 lo = *(const f32x4*)(st + rr * SP + c8);
+                const f32x4 hi = *(const f32x4*)(st + rr * SP + c8 + 4);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) { v[e] = a[e]; v[e + 4] = b[e]; }
+                for (int e = 0; e < 4; ++e) { v[e] = lo[e]; v[e + 4] = hi[e]; }
             }
             const int r = row_base + fm * 16 + rr, c = col_base + c8;
-            if (mode == GM_GRAM) {
-                const float s = f * f;
+            if (gram) {
+                if (mode == GM_GRAM2) {
+                    float a8[8];
+                    load8<TX>((const TX*)P.a + op_off<TX>(r, c, mp, mp), a8);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) v[e] *= s;
-                store8<TX>(gdst + (int64_t)r * mp + c, v);
-            } else if (mode == GM_GRAM2) {
-                float a8[8];
-                load8<TX>((const TX*)P.a + (int64_t)r * mp + c, a8);
+                    for (int e = 0; e < 8; ++e) v[e] = A.cb * a8[e] + gs * v[e];
+                } else {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) v[e] = A.cb * a8[e] + A.cc * v[e];
-                store8<TX>(gdst + (int64_t)r * mp + c, v);
+                    for (int e = 0; e < 8; ++e) v[e] *= gs;
+                }
+                if (diag) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        if (r == c + e) v[e] += gd;
+                }
+                store8<TX>(gdst + op_off<TX>(r, c, mp, mp), v);
             } else {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) v[e] = f * (A.ca * xv[fm][pass].get(e) + cb_eff * v[e]);
-                if (!last) store8<TX>(xdst + (int64_t)r * np + c, v);
+                for (int e = 0; e < 8; ++e) v[e] *= f;
+                if (!last) store8<TX>(xdst + op_off<TX>(r, c, mp, np), v);
                 else if (!P.tall) emit_u8<TS>(A, P, r, c, v);
             }
             if (trans_out) {
@@ -271,17 +255,16 @@ __device__ __forceinline__ void epilogue(const GemmArgs& A, const NsProb& P, int
         }
         if (trans_out) {
             wave_lds_sync();
-            // column pass: lane takes one column and 8 consecutive rows
 #pragma unroll
-            for (int pass = 0; pass < (2 * WT) / 64; ++pass) {
-                const int idx = pass * 64 + lane;
-                const int jj = idx >> 1, half = idx & 1;
+            for (int pass = 0; pass < CPASSES; ++pass) {
+                const int q = pass * 64 + lane;
+                const int jj = (q >> 5) * 16 + (q & 15), half = (q >> 4) & 1;
                 float v[8];
 #pragma unroll
                 for (int t = 0; t < 8; ++t) v[t] = st[(half * 8 + t) * SP + jj];
                 const int r = row_base + fm * 16 + half * 8, c = col_base + jj;
-                if (mirror) store8<TX>(gdst + (int64_t)c * mp + r, v);
-                else if (!last) store8<TX>(xtdst + (int64_t)c * mp + r, v);
+                if (mirror) store8<TX>(gdst + op_off<TX>(c, r, mp, mp), v);
+                else if (!last) store8<TX>(xtdst + op_off<TX>(c, r, np, mp), v);
                 else emit_u8<TS>(A, P, c, r, v);
             }
         }
@@ -291,44 +274,70 @@ __device__ __forceinline__ void epilogue(const GemmArgs& A, const NsProb& P, int
 // ---------------------------------------------------------------------------
 // bf16 kernel
 //
-// K loop, BK = 64, two LDS stages (separate arrays, so the compiler's wait
-// insertion can tell a direct-to-LDS load into one stage from reads of the
-// other). Operand tiles move HBM/L2 -> LDS with global_load_lds_dwordx4: each
-// instruction writes 64 lanes x 16 B contiguously (LDS base + lane*16), so the
-// XOR swizzle is applied by permuting the global addresses the lanes load.
+// K loop over steps of BK = 32 through a ring of NS = 4 LDS slots (separate
+// arrays, so the compiler's wait insertion can tell a direct-to-LDS load into
+// one slot from reads of another). Operand slices move HBM/L2 -> LDS with
+// global_load_lds_dwordx4: each instruction writes 64 lanes x 16 B
+// contiguously (LDS base + lane*16). A slot holds an operand slice as 1 KB
+// blocks of 16 rows x 32 k, chunk-major inside the block (16-byte chunk c of
+// row r at byte 16*(16c + r)): that is exactly the lane order of a 16x16x32
+// MFMA fragment, so a fragment read is one linear ds_read_b128 of a block
+// (lane l at byte 16*l, free of bank conflicts) and one direct load fills one
+// block.
 //
-// Iteration kt (stage S holds tile kt; fragments F0 = k-half 0 of tile kt are
-// already in registers):
-//   phase 1: read F1 (k-half 1 of tile kt) from stage S   | MFMAs on F0
-//   phase 2: first MFMAs on F1; wait own loads; barrier    | (tile kt+1 ready,
-//            all waves done with stage S)
-//            DMA tile kt+2 into stage S; read F0 of tile kt+1 from stage S^1
-//            | remaining MFMAs on F1
-// One barrier per K step; loads run ~1.25 steps ahead of their use.
+// Step kt (slot kt%NS holds slice kt, whose fragments are in registers; the
+// slices up to kt+NS-1 are in flight):
+//   phase A: the first HEAD fragment rows of MFMAs; wait until slice kt+1 has
+//            landed and the reads of slice kt are done; barrier
+//   phase B: direct loads of slice kt+NS into slot kt%NS, reads of slice
+//            kt+1's fragments, the remaining MFMAs, interleaved in a fixed
+//            order (loads spread out: a burst of them starves the MFMA stream)
+// One barrier per step; each load has NS-1 steps (~1.5 us at 256x256 tiles)
+// to arrive, which covers an L2 miss under full load.
 // ---------------------------------------------------------------------------
 #define LDSP __attribute__((address_space(3)))
+
+// Word 3 of a raw buffer resource: 32-bit data format, no swizzle, no stride.
+constexpr int BUF_RAW32 = 0x00020000;
 
 template <int N>
 struct Stage {
     static constexpr int value = N;
 };
 
+// fn(Stage<i>{}) for i = B .. E-1, every index a compile-time constant
+template <int B, int E, typename Fn>
+__device__ __forceinline__ void static_for(Fn&& fn) {
+    if constexpr (B < E) {
+        fn(Stage<B>{});
+        static_for<B + 1, E>(fn);
+    }
+}
+
 // s_waitcnt with only vmcnt (gfx9 encoding: vmcnt[3:0] bits 3:0, [5:4] bits 15:14)
 #define MU_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14))
-#define MU_WAIT_LGKMCNT0() __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (0 << 8) | (3 << 14))
+// s_waitcnt with vmcnt and lgkmcnt(0)
+#define MU_WAIT_VMCNT_LGKM0(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (0 << 8) | (((n) >> 4) << 14))
 
 template <int TS, bool SYM, typename TSRC>
 __global__ __launch_bounds__(NTHR) void k_gemm_bf16(GemmArgs A) {
-    constexpr int BK = 64;
+    constexpr int BK = 32;
+    constexpr int NS = 4;
     constexpr int WT = TS / 2;
     constexpr int F = WT / 16;
-    constexpr int LA = TS * BK;           // elements per operand tile
-    constexpr int NBLK = LA * 2 / 1024;   // 1 KB direct-load blocks per operand tile
+    constexpr int LS = TS * BK;           // elements per operand slot
+    constexpr int NBLK = TS / 16;         // 1 KB blocks per operand slot
     constexpr int BPW = NBLK / 4;         // blocks per wave per operand
-    __shared__ __attribute__((aligned(1024))) bf16 sA0[LA];
-    __shared__ __attribute__((aligned(1024))) bf16 sB0[LA];
-    __shared__ __attribute__((aligned(1024))) bf16 sA1[LA];
-    __shared__ __attribute__((aligned(1024))) bf16 sB1[LA];
+    constexpr int NDMA = 2 * BPW;         // direct loads per wave per step
+    static_assert((NS - 1) * NDMA <= 63, "vmcnt range");
+    __shared__ __attribute__((aligned(1024))) bf16 sA0[LS];
+    __shared__ __attribute__((aligned(1024))) bf16 sA1[LS];
+    __shared__ __attribute__((aligned(1024))) bf16 sA2[LS];
+    __shared__ __attribute__((aligned(1024))) bf16 sA3[LS];
+    __shared__ __attribute__((aligned(1024))) bf16 sB0[LS];
+    __shared__ __attribute__((aligned(1024))) bf16 sB1[LS];
+    __shared__ __attribute__((aligned(1024))) bf16 sB2[LS];
+    __shared__ __attribute__((aligned(1024))) bf16 sB3[LS];
 
     const int wg = xcd_remap(blockIdx.x, gridDim.x);
     if (wg >= A.total_tiles) return;
@@ -340,64 +349,67 @@ __global__ __launch_bounds__(NTHR) void k_gemm_bf16(GemmArgs A) {
     if (SYM) upper_tile(local, P.mp / TS, ti, tj);
     else apply_tile(local, P.mp / TS, P.np / TS, ti, tj);
 
-    // C = P Q^T, both operands with K contiguous
+    // C = P Q^T over K; P has RP rows, Q has RQ rows, both K-blocked
     const bf16 *pm, *qm;
-    int ldp, ldq, K;
+    int RP, RQ, K;
     if (mode == GM_GRAM) {
-        pm = qm = (const bf16*)P.x[A.src]; ldp = ldq = P.np; K = P.np;
+        pm = qm = (const bf16*)P.x[A.src]; RP = RQ = P.mp; K = P.np;
     } else if (mode == GM_GRAM2) {
-        pm = qm = (const bf16*)P.a; ldp = ldq = P.mp; K = P.mp;
+        pm = qm = (const bf16*)P.a; RP = RQ = P.mp; K = P.mp;
     } else {
-        pm = (const bf16*)(A.use_b ? P.b : P.a); ldp = P.mp;
-        qm = (const bf16*)P.xt[A.src]; ldq = P.mp; K = P.mp;
+        pm = (const bf16*)(A.use_b ? P.b : P.a); RP = P.mp;
+        qm = (const bf16*)P.xt[A.src]; RQ = P.np; K = P.mp;
     }
-    const bf16* pt = pm + (int64_t)ti * TS * ldp;
-    const bf16* qt = qm + (int64_t)tj * TS * ldq;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm0 = (wave >> 1) * WT, wn0 = (wave & 1) * WT;
 
-    // Direct-load sources. Block b = s*4 + wave of an operand tile is 1 KB =
-    // rows 8b .. 8b+7; lane -> row 8b + lane/8 and physical chunk lane%8, which
-    // holds logical chunk (lane%8) ^ swz_k(row) = (lane%8) ^ (lane/8). Block s
-    // is the block-0 address plus s*32 rows. Every source address is a
-    // wave-uniform base (scalar registers) plus a fixed 32-bit lane offset.
-    const int ca = (lane & 7) ^ (lane >> 3);
-    const uint32_t offA = (uint32_t)((8 * wave + (lane >> 3)) * ldp + ca * 8) * 2u;
-    const uint32_t offB = (uint32_t)((8 * wave + (lane >> 3)) * ldq + ca * 8) * 2u;
-    const int64_t strideA = (int64_t)32 * ldp, strideB = (int64_t)32 * ldq;
-
-    // direct load i of K step kt into stage S: i < BPW loads A block s = i,
-    // otherwise B block s = i - BPW
-    auto dma_one = [&](auto st, int kt, int i) {
+    auto slot_a = [&](auto st) -> bf16* {
         constexpr int S = decltype(st)::value;
-        const bool isA = i < BPW;
-        const int s = isA ? i : i - BPW;
-        bf16* dst = isA ? (S ? sA1 : sA0) : (S ? sB1 : sB0);
-        const char* src = isA ? (const char*)(pt + kt * BK) + s * strideA * 2 + offA
-                              : (const char*)(qt + kt * BK) + s * strideB * 2 + offB;
-        __builtin_amdgcn_global_load_lds((const void*)src, (LDSP void*)(dst + (s * 4 + wave) * 512), 16, 0, 0);
+        if constexpr (S == 0) return sA0;
+        else if constexpr (S == 1) return sA1;
+        else if constexpr (S == 2) return sA2;
+        else return sA3;
     };
-    auto dma = [&](auto st, int kt) {
-#pragma unroll
-        for (int i = 0; i < 2 * BPW; ++i) dma_one(st, kt, i);
+    auto slot_b = [&](auto st) -> bf16* {
+        constexpr int S = decltype(st)::value;
+        if constexpr (S == 0) return sB0;
+        else if constexpr (S == 1) return sB1;
+        else if constexpr (S == 2) return sB2;
+        else return sB3;
     };
 
-    // Fragment reads: lane reads row (lane&15) of a 16-row fragment at logical
-    // chunk kh*4 + lane/16, stored at that ^ swz_k(row) = ^ (lane&7).
-    const int swl = lane & 7;
-    const int offk0 = (lane & 15) * BK + (((lane >> 4) ^ swl) << 3);
-    const int offk1 = (lane & 15) * BK + (((4 + (lane >> 4)) ^ swl) << 3);
-    auto read_a = [&](auto st, int kh, int fm) -> bf16x8 {
-        constexpr int S = decltype(st)::value;
-        const bf16* as = S ? sA1 : sA0;
-        return *(const bf16x8*)(as + (wm0 + fm * 16) * BK + (kh ? offk1 : offk0));
+    // Direct loads. The TS x 32 slice kt of an operand tile is NBLK contiguous
+    // 1 KB blocks starting at block kt*R/16 + tile*TS/16; a buffer resource
+    // covering exactly that run (an offset outside it reads zeros instead of
+    // faulting) is built per step from the wave-uniform address. Block b of
+    // the slice goes to block b of the slot, lane l moving bytes 16l..16l+15:
+    // a plain 1 KB copy, eight whole 128-byte lines per instruction.
+    const uint32_t lane_off = (uint32_t)lane * 16u;
+    auto slice = [&](const bf16* base, int R, int tile, int kt) {
+        return __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(base + ((int64_t)kt * (R >> 4) + (int64_t)tile * (TS >> 4)) * 512), 0, NBLK * 1024, BUF_RAW32);
     };
-    auto read_b = [&](auto st, int kh, int fn) -> bf16x8 {
-        constexpr int S = decltype(st)::value;
-        const bf16* bs = S ? sB1 : sB0;
-        return *(const bf16x8*)(bs + (wn0 + fn * 16) * BK + (kh ? offk1 : offk0));
+    auto dma_slice = [&](auto st, int kt, auto first, auto count) {
+        constexpr int I0 = decltype(first)::value, NI = decltype(count)::value;
+        const __amdgpu_buffer_rsrc_t ra = slice(pm, RP, ti, kt);
+        const __amdgpu_buffer_rsrc_t rb = slice(qm, RQ, tj, kt);
+        static_for<I0, I0 + NI>([&](auto ic) {
+            constexpr int i = decltype(ic)::value;
+            constexpr bool isA = i < BPW;
+            const int b = (isA ? i : i - BPW) * 4 + wave;
+            bf16* dst = (isA ? slot_a(st) : slot_b(st)) + b * 512;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(isA ? ra : rb, (LDSP void*)dst, 16, lane_off, (uint32_t)b * 1024u,
+                                                     0, 0);
+        });
+    };
+    auto dma = [&](auto st, int kt) { dma_slice(st, kt, Stage<0>{}, Stage<NDMA>{}); };
+    auto read_a = [&](auto st, int fm) -> bf16x8 {
+        return *(const bf16x8*)(slot_a(st) + (wm0 + fm * 16) * BK + lane * 8);
+    };
+    auto read_b = [&](auto st, int fn) -> bf16x8 {
+        return *(const bf16x8*)(slot_b(st) + (wn0 + fn * 16) * BK + lane * 8);
     };
 
     f32x4 acc[F][F];
@@ -407,77 +419,77 @@ __global__ __launch_bounds__(NTHR) void k_gemm_bf16(GemmArgs A) {
         for (int j = 0; j < F; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     bf16x8 a0[F], b0[F], a1[F], b1[F];
-    const int KT = K / BK;
+    const int KT = K / BK;   // a multiple of NS: K is a multiple of 128
 
     dma(Stage<0>{}, 0);
-    MU_WAIT_VMCNT(0);
-    __builtin_amdgcn_s_barrier();
     dma(Stage<1>{}, 1);
+    dma(Stage<2>{}, 2);
+    dma(Stage<3>{}, 3);
+    MU_WAIT_VMCNT((NS - 1) * NDMA);
+    __builtin_amdgcn_s_barrier();
 #pragma unroll
-    for (int fn = 0; fn < F; ++fn) b0[fn] = read_b(Stage<0>{}, 0, fn);
+    for (int fn = 0; fn < F; ++fn) b0[fn] = read_b(Stage<0>{}, fn);
 #pragma unroll
-    for (int fm = 0; fm < F; ++fm) a0[fm] = read_a(Stage<0>{}, 0, fm);
+    for (int fm = 0; fm < F; ++fm) a0[fm] = read_a(Stage<0>{}, fm);
 
     // The body is emitted in the exact issue order wanted and fenced with
     // sched_barrier, so the MFMA stream is never starved: with one wave per
-    // SIMD the matrix core drains within a couple of MFMAs of any gap.
-    // Phase 1: 2F groups of {one k-half-1 fragment read, F/2 MFMAs on k-half 0}
-    //          (B fragments first: the first MFMAs of phase 2 need all of them).
-    // Phase 2: HEAD rows of MFMAs on k-half 1; wait own loads; barrier; then 2F
-    //          groups of {a direct load of tile kt+2, one k-half-0 read of tile
-    //          kt+1, the remaining k-half-1 MFMAs}.
-    // K/BK is even (K is a multiple of the tile >= 128) and the body is
-    // unrolled over the two stages, so every LDS access names one array; the
-    // prefetch index is clamped, so the last two prefetches reload the final
-    // tile into a stage nobody reads again instead of branching.
+    // SIMD the matrix core drains within a couple of MFMAs of any gap. Next
+    // fragments are read B first: phase A of the next step needs all of B and
+    // the first HEAD rows of A. Slice indices past the end are clamped, so the
+    // last loads refill slots nobody reads again instead of branching.
     constexpr int HEAD = F / 4 > 0 ? F / 4 : 1;
-    constexpr int G = 2 * F;                 // fragment reads per k-half
-    constexpr int NMF2 = (F - HEAD) * F;     // MFMAs after the barrier
-    constexpr int NDMA = 2 * BPW;            // direct loads per K step
-    auto mma1 = [&](int idx, const bf16x8 (&af)[F], const bf16x8 (&bfv)[F]) {
-        const int fm = idx / F, fn = idx % F;
-#pragma unroll
-        for (int r = 0; r < F; ++r)
-#pragma unroll
-            for (int c = 0; c < F; ++c)
-                if (r == fm && c == fn)
-                    acc[r][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[r], bfv[c], acc[r][c], 0, 0, 0);
+    constexpr int G = 2 * F;                 // fragment reads per step
+    constexpr int NMB = (F - HEAD) * F;      // MFMAs after the barrier
+    // one MFMA on accumulator tile idx (row-major over the F x F fragments);
+    // the instruction is written out so that the accumulators stay pinned in
+    // AGPRs across the loop (the builtin lets the allocator shuffle them)
+    auto mma_acc = [](auto idx, f32x4 (&c)[F][F], const bf16x8 (&af)[F], const bf16x8 (&bfv)[F]) {
+        constexpr int fm = decltype(idx)::value / F, fn = decltype(idx)::value % F;
+        asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c[fm][fn]) : "v"(af[fm]), "v"(bfv[fn]));
     };
-    auto half = [&](auto st, int kt) {
+    auto mma = [&](auto idx, const bf16x8 (&af)[F], const bf16x8 (&bfv)[F]) { mma_acc(idx, acc, af, bfv); };
+    auto step = [&](auto st, int kt, const bf16x8 (&ac)[F], const bf16x8 (&bc)[F], bf16x8 (&an)[F],
+                    bf16x8 (&bn)[F]) {
         constexpr int S = decltype(st)::value;
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-            if (g < F) b1[g] = read_b(st, 1, g);
-            else a1[g - F] = read_a(st, 1, g - F);
-#pragma unroll
-            for (int j = 0; j < F * F / G; ++j) mma1(g * (F * F / G) + j, a0, b0);
+        using SN = Stage<(S + 1) % NS>;
+        if constexpr (S == 0) {
+            // loop head: two wait states after the accumulator zeroing
+            // (a VALU write read as SrcC), which the compiler cannot see here
+            asm volatile("s_nop 1");
             __builtin_amdgcn_sched_barrier(0);
         }
-#pragma unroll
-        for (int j = 0; j < HEAD * F; ++j) mma1(j, a1, b1);
+        static_for<0, HEAD * F>([&](auto j) { mma(j, ac, bc); });
         __builtin_amdgcn_sched_barrier(0);
-        MU_WAIT_VMCNT(0);
+        MU_WAIT_VMCNT_LGKM0((NS - 2) * NDMA);
         __builtin_amdgcn_s_barrier();
-        const int kn = min(kt + 2, KT - 1);
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-#pragma unroll
-            for (int i = 0; i < NDMA; ++i)
-                if (i * G / NDMA == g) dma_one(st, kn, i);
-            if (g < F) b0[g] = read_b(Stage<1 - S>{}, 0, g);
-            else a0[g - F] = read_a(Stage<1 - S>{}, 0, g - F);
-#pragma unroll
-            for (int j = g * NMF2 / G; j < (g + 1) * NMF2 / G; ++j) mma1(HEAD * F + j, a1, b1);
+        const int kn = min(kt + NS, KT - 1);
+        static_for<0, G>([&](auto gc) {
+            constexpr int g = decltype(gc)::value;
+            // the loads of this group: i with i*G/NDMA == g
+            constexpr int i0 = (g * NDMA + G - 1) / G, i1 = ((g + 1) * NDMA + G - 1) / G;
+            if constexpr (i1 > i0) dma_slice(st, kn, Stage<i0>{}, Stage<i1 - i0>{});
+            if constexpr (g < F) bn[g] = read_b(SN{}, g);
+            else an[g - F] = read_a(SN{}, g - F);
+            static_for<HEAD * F + g * NMB / G, HEAD * F + (g + 1) * NMB / G>([&](auto j) { mma(j, ac, bc); });
             __builtin_amdgcn_sched_barrier(0);
-        }
+        });
     };
-    for (int kt = 0; kt < KT; kt += 2) {
-        half(Stage<0>{}, kt);
-        half(Stage<1>{}, kt + 1);
+    for (int kt = 0; kt < KT; kt += NS) {
+        step(Stage<0>{}, kt, a0, b0, a1, b1);
+        step(Stage<1>{}, kt + 1, a1, b1, a0, b0);
+        step(Stage<2>{}, kt + 2, a0, b0, a1, b1);
+        step(Stage<3>{}, kt + 3, a1, b1, a0, b0);
     }
+    // The MFMAs above are opaque to the compiler's hazard recognizer: give the
+    // last ones the wait states (>= passes + 2) that an accumulator read needs.
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    MU_WAIT_VMCNT(0);
     __syncthreads();
-    // epilogue staging: waves 0-1 in stage 0's A array, waves 2-3 in its B array
-    float* st = (float*)((wave < 2) ? sA0 : sB0) + (wave & 1) * 16 * (WT + 4);
+    // epilogue staging: one strip per wave, each in its own slot array
+    float* st = (float*)(wave == 0 ? sA0 : wave == 1 ? sA1 : wave == 2 ? sA2 : sA3);
     epilogue<bf16, TSRC, F>(A, P, ti, tj, TS, wm0, wn0, acc, st);
 }
 

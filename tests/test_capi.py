@@ -74,6 +74,7 @@ def _step(lib, mats, hp, ws=None, nbytes=0):
 @pytest.mark.parametrize("kw,code", [
     (dict(num_heads=3), 1), (dict(num_heads=0), 1), (dict(rows=0), 1), (dict(cols=-4), 1),
     (dict(param=None), 1), (dict(dtype=7), 2), (dict(grad=A + 1), 3),
+    (dict(rows=(1 << 21) + 1, cols=8), 1), (dict(rows=8, cols=(1 << 21) + 1), 1),
 ])
 def test_bad_matrix_rejected(lib, kw, code):
     assert _step(lib, [_mat(lib, **kw)], _hp(lib)) == code
