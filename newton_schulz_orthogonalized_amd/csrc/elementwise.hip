@@ -144,8 +144,8 @@ __global__ __launch_bounds__(NTHR) void k_prep(PrepArgs A) {
     __shared__ float tile[T][T + 1];
     __shared__ float red[4];
     const int t = blockIdx.x;
-    const int p = find_prob(A.prefix, A.nprobs, t);
-    const NsProb& P = A.probs[p];
+    const int p = __builtin_amdgcn_readfirstlane(find_prob(A.prefix, A.nprobs, t));
+    const NsProb P = A.probs[p];   // by value: held in registers, never re-read after a store
     const int local = t - A.prefix[p];
     const bool wide = !P.tall;
     const int RD = wide ? P.mp : P.np;   // rows of the U-oriented buffer
@@ -226,8 +226,8 @@ template <typename TS, typename TX>
 __global__ __launch_bounds__(NTHR) void k_finish(FinishArgs A) {
     __shared__ float tile[T][T + 1];
     const int t = blockIdx.x;
-    const int p = find_prob(A.prefix, A.nprobs, t);
-    const NsProb& P = A.probs[p];
+    const int p = __builtin_amdgcn_readfirstlane(find_prob(A.prefix, A.nprobs, t));
+    const NsProb P = A.probs[p];   // by value: held in registers, never re-read after a store
     const int local = t - A.prefix[p];
     const int tiles_n = P.np / T;
     const int ti = local / tiles_n, tj = local - ti * tiles_n;

@@ -67,64 +67,65 @@ __device__ __forceinline__ void apply_tile(int local, int TM, int TN, int& ti, i
 
 // ---------------------------------------------------------------------------
 // U-space write of 8 consecutive values (update or plain output); row ur,
-// columns uc0 .. uc0+7 (uc0 a multiple of 8), clipped to the head block.
+// columns uc0 .. uc0+7 (uc0 a multiple of 8), clipped to the head block. A
+// whole run on vector-capable buffers takes two 4-wide read-modify-writes; a
+// run cut by the block edge goes element by element in a loop that is kept
+// rolled, so the many inlined copies of this stay small.
 // ---------------------------------------------------------------------------
 template <typename TS>
 __device__ __forceinline__ void emit_u8(const GemmArgs& A, const NsProb& P, int ur, int uc0, const float* v) {
     if (ur >= P.hr || uc0 >= P.hc) return;
-    const int valid = min(8, P.hc - uc0);
     const int64_t off = (int64_t)ur * P.ld + uc0;
-    const bool vec = P.vec != 0;
-    if (P.oout) {
-        float* o = P.oout + off;
+    const float decay = A.lr * A.wd, step = A.lr * P.scale;
+    if (P.vec && uc0 + 8 <= P.hc) {
+        if (P.oout) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-            if (e < valid) o[e] = v[e];
-    }
-    if (A.with_update) {
-        TS* w = (TS*)P.param + off;
-        const float decay = A.lr * A.wd, step = A.lr * P.scale;
+            for (int e = 0; e < 8; ++e) P.oout[off + e] = v[e];
+        }
+        TS* dst = (TS*)(A.with_update ? P.param : P.out) + off;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            const int cnt = min(4, valid - 4 * h);
-            if (cnt <= 0) break;
             float x[4];
-            if (vec && cnt == 4) {
+            if (A.with_update) {
                 if constexpr (sizeof(TS) == 2) {
-                    bf16x4 q = *(const bf16x4*)(w + 4 * h);
+                    const bf16x4 q = *gp((const bf16x4*)(dst + 4 * h));
 #pragma unroll
                     for (int e = 0; e < 4; ++e) x[e] = (float)q[e];
                 } else {
-                    f32x4 q = *(const f32x4*)(w + 4 * h);
+                    const f32x4 q = *gp((const f32x4*)(dst + 4 * h));
 #pragma unroll
                     for (int e = 0; e < 4; ++e) x[e] = q[e];
                 }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) x[e] = (x[e] - decay * x[e]) - step * v[4 * h + e];
             } else {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) x[e] = e < cnt ? to_f32<TS>(w[4 * h + e]) : 0.f;
+                for (int e = 0; e < 4; ++e) x[e] = v[4 * h + e];
             }
+            if constexpr (sizeof(TS) == 2) {
+                bf16x4 q;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) x[e] = (x[e] - decay * x[e]) - step * v[4 * h + e];
-            if (vec && cnt == 4) {
-                if constexpr (sizeof(TS) == 2) {
-                    bf16x4 q;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) q[e] = (bf16)x[e];
-                    *(bf16x4*)(w + 4 * h) = q;
-                } else {
-                    *(f32x4*)(w + 4 * h) = f32x4{x[0], x[1], x[2], x[3]};
-                }
+                for (int e = 0; e < 4; ++e) q[e] = (bf16)x[e];
+                *gp((bf16x4*)(dst + 4 * h)) = q;
             } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (e < cnt) w[4 * h + e] = from_f32<TS>(x[e]);
+                *gp((f32x4*)(dst + 4 * h)) = f32x4{x[0], x[1], x[2], x[3]};
             }
         }
-    } else {
-        TS* o = (TS*)P.out + off;
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-            if (e < valid) o[e] = from_f32<TS>(v[e]);
+        return;
+    }
+    const int valid = min(8, P.hc - uc0);
+#pragma clang loop unroll(disable)
+    for (int e = 0; e < valid; ++e) {
+        const float ve = e == 0 ? v[0] : e == 1 ? v[1] : e == 2 ? v[2] : e == 3 ? v[3]
+                       : e == 4 ? v[4] : e == 5 ? v[5] : e == 6 ? v[6] : v[7];
+        if (P.oout) P.oout[off + e] = ve;
+        if (A.with_update) {
+            TS* w = (TS*)P.param + off + e;
+            const float x = to_f32<TS>(*w);
+            *w = from_f32<TS>((x - decay * x) - step * ve);
+        } else {
+            ((TS*)P.out)[off + e] = from_f32<TS>(ve);
+        }
     }
 }
 
@@ -153,19 +154,23 @@ __device__ __forceinline__ void store8(TX* p, const float* v) {
     }
 }
 
-// Order LDS accesses of this wave (a wave's LDS operations complete in issue
-// order; only compiler reordering has to be prevented).
-__device__ __forceinline__ void wave_lds_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+// Copy one accumulator out of its AGPR at this point of the program (the
+// compiler would otherwise hoist all 256 copies to the end of the K loop).
+__device__ __forceinline__ float agpr_read(float a) {
+    float v;
+    asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(a));
+    return v;
 }
+
+// Order LDS accesses of this wave. A wave's LDS instructions execute in issue
+// order, so lanes see each other's earlier writes without any wait; only the
+// compiler must not move accesses across this point. (A memory fence would do
+// that too, but it also waits for every global store still in flight.)
+__device__ __forceinline__ void wave_lds_sync() { asm volatile("" ::: "memory"); }
 
 // ---------------------------------------------------------------------------
 // Epilogue shared by the bf16 and fp32 kernels. The accumulator layout is the
 // 16x16 MFMA one: lane l holds C[4*(l>>4) + e][l & 15] of each fragment.
-// `st` is this wave's LDS strip of 16 x (F*16 + 4) floats, not otherwise in
-// use; each wave stages only its own strip, so syncs are wave-local.
 //
 // What each mode stores (f = 1/(||U||_F + eps) on the first step, else 1):
 //   Gram, cubic step     B = a I + b f^2 (X X^T)      -> P.a (mirrored)
@@ -176,27 +181,32 @@ __device__ __forceinline__ void wave_lds_sync() {
 // Folding a I into B keeps X itself out of the apply epilogue; padding stays
 // zero because a padded row of X' is a*0 + (rows of A that are zero).
 //
-// Row pass: lane -> row idx%16 and 8 consecutive columns, so with the K-blocked
-// layout a wave writes whole 1 KB blocks. Column pass (transposed outputs):
-// lane -> column and 8 consecutive rows, again 16 columns per 256 bytes.
+// Transposed outputs (Gram mirror, X'^T, a tall block's parameter) come
+// straight from registers: v_permlane16_swap on the accumulators of two
+// neighbouring fragments leaves every lane with 8 consecutive rows of one
+// column, one 16-byte chunk of the transposed (K-blocked) output.
+// Row-major outputs go through `st`, this wave's LDS strip of 16 x (F*16 + 4)
+// floats: lane -> row idx%16 and 8 consecutive columns, so with the K-blocked
+// layout a wave writes whole 1 KB blocks. Each wave stages only its own strip,
+// so syncs are wave-local.
 // ---------------------------------------------------------------------------
-template <typename TX, typename TS, int F>
-__device__ __forceinline__ void epilogue(const GemmArgs& A, const NsProb& P, int ti, int tj, int TS_, int wm0,
-                                         int wn0, f32x4 (&acc)[F][F], float* st) {
+template <int MODE, typename TX, typename TS, int F>
+__device__ __forceinline__ void epilogue_mode(const GemmArgs& A, const NsProb& P, int ti, int tj, int TS_, int wm0,
+                                              int wn0, f32x4 (&acc)[F][F], float* st) {
+    static_assert(F % 2 == 0, "fragments are paired for the transposed stores");
     constexpr int WT = F * 16;
     constexpr int SP = WT + 4;
     constexpr int PASSES = WT / 32;            // row pass: 16 rows x 32 columns per pass
-    constexpr int CPASSES = (2 * WT) / 64;     // column pass: WT columns x 2 halves
     const int lane = threadIdx.x & 63;
-    const int mode = A.mode;
+    const int g4 = lane >> 4, l16 = lane & 15;
+    constexpr int mode = MODE;
     const float f = A.first ? P.fold[0] : 1.f;
-    const bool gram = mode == GM_GRAM || mode == GM_GRAM2;
+    constexpr bool gram = mode == GM_GRAM || mode == GM_GRAM2;
     const bool diag = gram && ti == tj;
     const bool mirror = gram && ti != tj;
-    const bool last = mode == GM_APPLY_LAST;
-    // transposed outputs: the Gram mirror, X'^T for the next apply, or the
-    // parameter of a tall block on the last step
+    constexpr bool last = mode == GM_APPLY_LAST;
     const bool trans_out = mirror || (!gram && !last) || (last && P.tall);
+    const bool row_out = !(last && P.tall);
     const int row_base = ti * TS_ + wm0, col_base = tj * TS_ + wn0;
     const int mp = P.mp, np = P.np;
     // Gram scale and diagonal term
@@ -204,20 +214,63 @@ __device__ __forceinline__ void epilogue(const GemmArgs& A, const NsProb& P, int
     if (mode == GM_GRAM && !A.use_b) { gs = A.cb * f * f; gd = A.ca; }
     if (mode == GM_GRAM2) { gs = A.cc; gd = A.ca; }
     TX* gdst = (TX*)(mode == GM_GRAM2 ? P.b : P.a);
-    TX* xdst = (TX*)P.x[A.src ^ 1];
-    TX* xtdst = (TX*)P.xt[A.src ^ 1];
+    TX* xdst = (TX*)(A.src ? P.x[0] : P.x[1]);
+    TX* xtdst = (TX*)(A.src ? P.xt[0] : P.xt[1]);
 
 #pragma clang loop unroll(full)
     for (int fm = 0; fm < F; ++fm) {
+        // this strip's accumulators, copied out of the AGPRs here and only
+        // here, so register use stays bounded by one strip
+        float av[F][4];
+#pragma unroll
+        for (int fn = 0; fn < F; ++fn)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) av[fn][e] = agpr_read(acc[fm][fn][e]);
+        if (trans_out) {
+#pragma unroll
+            for (int fp = 0; fp < F; fp += 2) {
+                float w[8];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(av[fp][e]),
+                                                                     __float_as_uint(av[fp + 1][e]), false, false);
+                    w[e] = __uint_as_float(sw[0]);
+                    w[4 + e] = __uint_as_float(sw[1]);
+                }
+                // this lane: column c of C, rows r0 .. r0+7 (off the diagonal
+                // for mirrored tiles)
+                const int c = col_base + (fp + (g4 & 1)) * 16 + l16;
+                const int r0 = row_base + fm * 16 + 8 * (g4 >> 1);
+                float v[8];
+                if constexpr (gram) {
+                    if constexpr (mode == GM_GRAM2) {
+                        float a8[8];   // A[r0+e][c] = A[c][r0+e]
+                        load8<TX>((const TX*)P.a + op_off<TX>(c, r0, mp, mp), a8);
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) v[e] = A.cb * a8[e] + gs * w[e];
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) v[e] = gs * w[e];
+                    }
+                    store8<TX>(gdst + op_off<TX>(c, r0, mp, mp), v);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) v[e] = f * w[e];
+                    if constexpr (!last) store8<TX>(xtdst + op_off<TX>(c, r0, np, mp), v);
+                    else emit_u8<TS>(A, P, c, r0, v);
+                }
+            }
+        }
+        if (!row_out) continue;
         wave_lds_sync();
 #pragma unroll
         for (int fn = 0; fn < F; ++fn)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) st[(4 * (lane >> 4) + e) * SP + fn * 16 + (lane & 15)] = acc[fm][fn][e];
+            for (int e = 0; e < 4; ++e) st[(4 * g4 + e) * SP + fn * 16 + l16] = av[fn][e];
         wave_lds_sync();
 #pragma unroll
         for (int pass = 0; pass < PASSES; ++pass) {
-            const int rr = lane & 15, c8 = pass * 32 + (lane >> 4) * 8;
+            const int rr = l16, c8 = pass * 32 + g4 * 8;
             float v[8];
             {
                 const f32x4 lo = *(const f32x4*)(st + rr * SP + c8);
@@ -226,8 +279,8 @@ __device__ __forceinline__ void epilogue(const GemmArgs& A, const NsProb& P, int
                 for (int e = 0; e < 4; ++e) { v[e] = lo[e]; v[e + 4] = hi[e]; }
             }
             const int r = row_base + fm * 16 + rr, c = col_base + c8;
-            if (gram) {
-                if (mode == GM_GRAM2) {
+            if constexpr (gram) {
+                if constexpr (mode == GM_GRAM2) {
                     float a8[8];
                     load8<TX>((const TX*)P.a + op_off<TX>(r, c, mp, mp), a8);
 #pragma unroll
@@ -245,29 +298,24 @@ __device__ __forceinline__ void epilogue(const GemmArgs& A, const NsProb& P, int
             } else {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) v[e] *= f;
-                if (!last) store8<TX>(xdst + op_off<TX>(r, c, mp, np), v);
-                else if (!P.tall) emit_u8<TS>(A, P, r, c, v);
-            }
-            if (trans_out) {
-                *(f32x4*)(st + rr * SP + c8) = f32x4{v[0], v[1], v[2], v[3]};
-                *(f32x4*)(st + rr * SP + c8 + 4) = f32x4{v[4], v[5], v[6], v[7]};
+                if constexpr (!last) store8<TX>(xdst + op_off<TX>(r, c, mp, np), v);
+                else emit_u8<TS>(A, P, r, c, v);
             }
         }
-        if (trans_out) {
-            wave_lds_sync();
-#pragma unroll
-            for (int pass = 0; pass < CPASSES; ++pass) {
-                const int q = pass * 64 + lane;
-                const int jj = (q >> 5) * 16 + (q & 15), half = (q >> 4) & 1;
-                float v[8];
-#pragma unroll
-                for (int t = 0; t < 8; ++t) v[t] = st[(half * 8 + t) * SP + jj];
-                const int r = row_base + fm * 16 + half * 8, c = col_base + jj;
-                if (mirror) store8<TX>(gdst + op_off<TX>(c, r, mp, mp), v);
-                else if (!last) store8<TX>(xtdst + op_off<TX>(c, r, np, mp), v);
-                else emit_u8<TS>(A, P, c, r, v);
-            }
-        }
+    }
+}
+
+// One specialised, contiguous epilogue per mode: a generic one with every
+// mode's code unrolled over the strips outgrows the instruction cache.
+template <bool SYM, typename TX, typename TS, int F>
+__device__ __forceinline__ void epilogue(const GemmArgs& A, const NsProb& P, int ti, int tj, int TS_, int wm0,
+                                         int wn0, f32x4 (&acc)[F][F], float* st) {
+    if constexpr (SYM) {
+        if (A.mode == GM_GRAM) epilogue_mode<GM_GRAM, TX, TS, F>(A, P, ti, tj, TS_, wm0, wn0, acc, st);
+        else epilogue_mode<GM_GRAM2, TX, TS, F>(A, P, ti, tj, TS_, wm0, wn0, acc, st);
+    } else {
+        if (A.mode == GM_APPLY) epilogue_mode<GM_APPLY, TX, TS, F>(A, P, ti, tj, TS_, wm0, wn0, acc, st);
+        else epilogue_mode<GM_APPLY_LAST, TX, TS, F>(A, P, ti, tj, TS_, wm0, wn0, acc, st);
     }
 }
 
@@ -341,8 +389,8 @@ __global__ __launch_bounds__(NTHR) void k_gemm_bf16(GemmArgs A) {
 
     const int wg = xcd_remap(blockIdx.x, gridDim.x);
     if (wg >= A.total_tiles) return;
-    const int p = find_prob(A.prefix, A.nprobs, wg);
-    const NsProb& P = A.probs[p];
+    const int p = __builtin_amdgcn_readfirstlane(find_prob(A.prefix, A.nprobs, wg));
+    const NsProb P = A.probs[p];   // by value: held in registers, never re-read after a store
     const int local = wg - A.prefix[p];
     const int mode = A.mode;
     int ti, tj;
@@ -353,12 +401,12 @@ __global__ __launch_bounds__(NTHR) void k_gemm_bf16(GemmArgs A) {
     const bf16 *pm, *qm;
     int RP, RQ, K;
     if (mode == GM_GRAM) {
-        pm = qm = (const bf16*)P.x[A.src]; RP = RQ = P.mp; K = P.np;
+        pm = qm = (const bf16*)(A.src ? P.x[1] : P.x[0]); RP = RQ = P.mp; K = P.np;
     } else if (mode == GM_GRAM2) {
         pm = qm = (const bf16*)P.a; RP = RQ = P.mp; K = P.mp;
     } else {
         pm = (const bf16*)(A.use_b ? P.b : P.a); RP = P.mp;
-        qm = (const bf16*)P.xt[A.src]; RQ = P.np; K = P.mp;
+        qm = (const bf16*)(A.src ? P.xt[1] : P.xt[0]); RQ = P.np; K = P.mp;
     }
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -490,7 +538,7 @@ __global__ __launch_bounds__(NTHR) void k_gemm_bf16(GemmArgs A) {
     __syncthreads();
     // epilogue staging: one strip per wave, each in its own slot array
     float* st = (float*)(wave == 0 ? sA0 : wave == 1 ? sA1 : wave == 2 ? sA2 : sA3);
-    epilogue<bf16, TSRC, F>(A, P, ti, tj, TS, wm0, wn0, acc, st);
+    epilogue<SYM, bf16, TSRC, F>(A, P, ti, tj, TS, wm0, wn0, acc, st);
 }
 
 // ---------------------------------------------------------------------------
@@ -508,8 +556,8 @@ __global__ __launch_bounds__(NTHR) void k_gemm_f32(GemmArgs A) {
 
     const int wg = xcd_remap(blockIdx.x, gridDim.x);
     if (wg >= A.total_tiles) return;
-    const int p = find_prob(A.prefix, A.nprobs, wg);
-    const NsProb& P = A.probs[p];
+    const int p = __builtin_amdgcn_readfirstlane(find_prob(A.prefix, A.nprobs, wg));
+    const NsProb P = A.probs[p];   // by value: held in registers, never re-read after a store
     const int local = wg - A.prefix[p];
     const int mode = A.mode;
     int ti, tj;
@@ -519,12 +567,12 @@ __global__ __launch_bounds__(NTHR) void k_gemm_f32(GemmArgs A) {
     const float *pm, *qm;
     int ldp, ldq, K;
     if (mode == GM_GRAM) {
-        pm = qm = (const float*)P.x[A.src]; ldp = ldq = P.np; K = P.np;
+        pm = qm = (const float*)(A.src ? P.x[1] : P.x[0]); ldp = ldq = P.np; K = P.np;
     } else if (mode == GM_GRAM2) {
         pm = qm = (const float*)P.a; ldp = ldq = P.mp; K = P.mp;
     } else {
         pm = (const float*)(A.use_b ? P.b : P.a); ldp = P.mp;
-        qm = (const float*)P.xt[A.src]; ldq = P.mp; K = P.mp;
+        qm = (const float*)(A.src ? P.xt[1] : P.xt[0]); ldq = P.mp; K = P.mp;
     }
     const float* pt = pm + (int64_t)ti * TS * ldp;
     const float* qt = qm + (int64_t)tj * TS * ldq;
@@ -586,7 +634,12 @@ __global__ __launch_bounds__(NTHR) void k_gemm_f32(GemmArgs A) {
         if (kt + 1 < KT) sstore((kt + 1) & 1);
         __syncthreads();
     }
-    epilogue<float, TSRC, F>(A, P, ti, tj, TS, wm0, wn0, acc, smem + wave * 16 * (WT + 4));
+    // the epilogue reads the accumulators with opaque v_accvgpr_read: give the
+    // last MFMAs their wait states
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    epilogue<SYM, float, TSRC, F>(A, P, ti, tj, TS, wm0, wn0, acc, smem + wave * 16 * (WT + 4));
 }
 
 template <int TS, bool SYM>
