@@ -131,6 +131,18 @@ def test_configurable_coefficients(ci, prec):
     assert O.rel_fro(o, ref["o"]) <= (F32_TOL if prec == "f32" else BF16_TOL)
 
 
+@pytest.mark.parametrize("shape", [(768, 1000), (1000, 768)])
+def test_quintic_on_256_tiles(shape):
+    """Quintic steps where the bf16 path picks 256x256 tiles (several tiles per
+    side): the A^2 pass, its mirrored and diagonal tiles, and an apply that reads
+    B, in both orientations, mixed with cubic steps."""
+    print(f"[quintic 256 tiles] shape={shape}", flush=True)
+    coeffs = [(1.875, -1.25, 0.375)] * 3 + [(1.5, -0.5, 0.0)] * 2
+    w0, w1, m1, o, _, ref = _step_case(shape, torch.bfloat16, "bf16", 9600, coeffs=coeffs, ns_steps=len(coeffs),
+                                       gstd=1e-3, wstd=0.02, mstd=1e-3)
+    assert O.rel_fro(o, ref["o"]) <= BF16_TOL
+
+
 @pytest.mark.parametrize("prec", ["f32", "bf16"])
 def test_zero_steps_applies_normalised_u(prec):
     dtype = torch.float32 if prec == "f32" else torch.bfloat16
