@@ -180,7 +180,10 @@ void build_plan(const std::vector<Item>& items, int ns_dt, const std::vector<Coe
             pp.d.scale = it.scale;
             pp.d.norm_out = it.norm_out ? it.norm_out + h : nullptr;
             pp.d.oout = it.oout ? it.oout + off : nullptr;
-            pp.d.nparts = (pp.d.mp / PREP_TILE) * (pp.d.np / PREP_TILE);
+            {   // prep tiles over the U-oriented buffer (X if wide, X^T if tall)
+                const int rd = pp.d.tall ? pp.d.np : pp.d.mp, kd = pp.d.tall ? pp.d.mp : pp.d.np;
+                pp.d.nparts = (rd / prep_rows_dt(ns_dt)) * (kd / prep_cols_dt(ns_dt));
+            }
             const size_t nes = ns_dt == DT_BF16 ? 2 : 4;
             pp.x_bytes = align_up((size_t)pp.d.mp * pp.d.np * nes);
             pp.a_bytes = align_up((size_t)pp.d.mp * pp.d.mp * nes);

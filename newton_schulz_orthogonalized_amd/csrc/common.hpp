@@ -64,7 +64,7 @@ struct NsProb {
     float* fold;       // 1 / (||U||_F + eps), written by the norm kernel
     float* norm_out;   // optional ||U||_F
     float* oout;       // optional float32 copy of O in U-space (step only)
-    int32_t nparts;    // number of prep tiles = (mp/64) * (np/64)
+    int32_t nparts;    // number of prep tiles (see prep_rows / prep_cols)
     int32_t pad1;
 };
 

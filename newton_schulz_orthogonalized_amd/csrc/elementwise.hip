@@ -21,21 +21,20 @@ namespace mu {
 
 namespace {
 
-constexpr int T = PREP_TILE;  // 64
 constexpr int NTHR = 256;
 
 // Four consecutive U-space elements (row r, cols c0..c0+3) of a buffer whose
 // element type is TS; out-of-range columns read as 0.
 template <typename TS>
 __device__ inline void load4(const void* base, int64_t off, int valid, bool vec, float v[4]) {
-    const TS* p = (const TS*)base + off;
+    const MU_GLOBAL TS* p = (const MU_GLOBAL TS*)base + off;
     if (vec && valid == 4) {
         if constexpr (sizeof(TS) == 2) {
-            bf16x4 q = *(const bf16x4*)p;
+            bf16x4 q = *(const MU_GLOBAL bf16x4*)p;
 #pragma unroll
             for (int e = 0; e < 4; ++e) v[e] = (float)q[e];
         } else {
-            f32x4 q = *(const f32x4*)p;
+            f32x4 q = *(const MU_GLOBAL f32x4*)p;
 #pragma unroll
             for (int e = 0; e < 4; ++e) v[e] = q[e];
         }
@@ -47,16 +46,16 @@ __device__ inline void load4(const void* base, int64_t off, int valid, bool vec,
 
 template <typename TS>
 __device__ inline void store4(void* base, int64_t off, int valid, bool vec, const float v[4]) {
-    TS* p = (TS*)base + off;
+    MU_GLOBAL TS* p = (MU_GLOBAL TS*)base + off;
     if (vec && valid == 4) {
         if constexpr (sizeof(TS) == 2) {
             bf16x4 q;
 #pragma unroll
             for (int e = 0; e < 4; ++e) q[e] = (bf16)v[e];
-            *(bf16x4*)p = q;
+            *(MU_GLOBAL bf16x4*)p = q;
         } else {
             f32x4 q = {v[0], v[1], v[2], v[3]};
-            *(f32x4*)p = q;
+            *(MU_GLOBAL f32x4*)p = q;
         }
     } else {
 #pragma unroll
@@ -72,20 +71,20 @@ __device__ inline void store_x4(TX* p, const float v[4]) {
         bf16x4 q;
 #pragma unroll
         for (int e = 0; e < 4; ++e) q[e] = (bf16)v[e];
-        *(bf16x4*)p = q;
+        *(MU_GLOBAL bf16x4*)p = q;
     } else {
         f32x4 q = {v[0], v[1], v[2], v[3]};
-        *(f32x4*)p = q;
+        *(MU_GLOBAL f32x4*)p = q;
     }
 }
 template <typename TX>
 __device__ inline void load_x4(const TX* p, float v[4]) {
     if constexpr (sizeof(TX) == 2) {
-        bf16x4 q = *(const bf16x4*)p;
+        bf16x4 q = *(const MU_GLOBAL bf16x4*)p;
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = (float)q[e];
     } else {
-        f32x4 q = *(const f32x4*)p;
+        f32x4 q = *(const MU_GLOBAL f32x4*)p;
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = q[e];
     }
@@ -102,46 +101,58 @@ __device__ inline float block_sum(float v, float* red) {
     return s;
 }
 
-// U for four consecutive elements of one U-space row. Updates momentum.
+// Gradient and momentum of four consecutive elements of one U-space row
+// (zeros outside the head block). Split from the arithmetic so that a thread
+// can issue the loads of all its rows before the first momentum store (which
+// the compiler would otherwise have to wait for, not knowing that the buffers
+// are disjoint).
 template <typename TS>
-__device__ inline void make_u(const NsProb& P, int r, int c0, bool with_m, bool nesterov, float mu,
-                              float u[4]) {
+__device__ inline void load_gm(const NsProb& P, int r, int c0, bool with_m, float g[4], float m[4]) {
     const int valid = (r < P.hr) ? max(0, min(4, P.hc - c0)) : 0;
-    if (valid == 0) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) u[e] = 0.f;
-        return;
-    }
     const int64_t off = (int64_t)r * P.ld + c0;
     const bool vec = P.vec != 0;
-    float g[4];
     load4<TS>(P.src, off, valid, vec, g);
+    if (with_m) load4<float>(P.mom, off, valid, vec, m);
+    else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) m[e] = 0.f;
+    }
+}
+
+// U from G and M; the updated momentum is stored back. (MuonClip Optimizer
+// page, "Momentum": M <- mu M + (1 - mu) G; the Nesterov blend
+// U = (1 - mu) G + mu M_new.)
+__device__ inline void make_u(const NsProb& P, int r, int c0, bool with_m, bool nesterov, float mu, const float g[4],
+                              float m[4], float u[4]) {
     if (!with_m) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) u[e] = g[e];
         return;
     }
-    float m[4];
-    load4<float>(P.mom, off, valid, vec, m);
     const float omm = 1.f - mu;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         m[e] = mu * m[e] + omm * g[e];
         u[e] = nesterov ? omm * g[e] + mu * m[e] : m[e];
     }
-    store4<float>(P.mom, off, valid, vec, m);
+    const int valid = (r < P.hr) ? max(0, min(4, P.hc - c0)) : 0;
+    if (valid > 0) store4<float>(P.mom, (int64_t)r * P.ld + c0, valid, P.vec != 0, m);
 }
 
 // Tiles run over the buffer that has U's orientation (X for wide blocks, X^T
 // for tall ones): U is computed into an LDS tile, then written into that buffer
 // and, transposed, into the other one. Out-of-range elements are written as
-// zeros, which is the padding every later step relies on. With bf16
-// Newton-Schulz both buffers are K-blocked: a 64x64 tile is 2 panels x 4 row
-// groups of 1 KB blocks, and thread q of a pass writes 16-byte chunk q, so a
-// wave stores one whole block.
+// zeros, which is the padding every later step relies on. Tile shape:
+// prep_rows(TX) x prep_cols(TX) (32 x 128 for bf16, so a tile reads 256-byte
+// gradient and 512-byte momentum runs per row). With bf16 Newton-Schulz both
+// buffers are K-blocked: a tile is 8 whole 1 KB blocks in each of them, and
+// thread q of a pass writes 16-byte chunk q, so a wave stores one whole block.
 template <typename TS, typename TX>
 __global__ __launch_bounds__(NTHR) void k_prep(PrepArgs A) {
-    __shared__ float tile[T][T + 1];
+    constexpr int TR = prep_rows<TX>(), TC = prep_cols<TX>();
+    constexpr int TPR = TC / 4;          // threads per tile row
+    constexpr int RSTEP = NTHR / TPR;    // rows between a thread's rows
+    __shared__ float tile[TR][TC + 1];
     __shared__ float red[4];
     const int t = blockIdx.x;
     const int p = __builtin_amdgcn_readfirstlane(find_prob(A.prefix, A.nprobs, t));
@@ -152,101 +163,145 @@ __global__ __launch_bounds__(NTHR) void k_prep(PrepArgs A) {
     const int KD = wide ? P.np : P.mp;   // its columns = rows of the other one
     TX* D = (TX*)(wide ? P.x[0] : P.xt[0]);
     TX* Tt = (TX*)(wide ? P.xt[0] : P.x[0]);
-    const int tiles_n = KD / T;
+    const int tiles_n = KD / TC;
     const int ti = local / tiles_n, tj = local - ti * tiles_n;
     const int tid = threadIdx.x;
-    const int rr = tid >> 4, cc = (tid & 15) * 4;
+    const int rr = tid / TPR, cc = (tid % TPR) * 4;
     const bool with_m = A.with_momentum != 0, nest = A.nesterov != 0;
+    float gk[4][4], mk[4][4];
+    // a tile wholly inside the head block, on vector-capable buffers, loads
+    // without per-lane range checks (no divergent branches between the loads)
+    const bool inside = P.vec && (ti + 1) * TR <= P.hr && (tj + 1) * TC <= P.hc;
+    if (inside) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int64_t off = (int64_t)(ti * TR + rr + RSTEP * k) * P.ld + tj * TC + cc;
+            if constexpr (sizeof(TS) == 2) {
+                const bf16x4 q = *(const MU_GLOBAL bf16x4*)((const bf16*)P.src + off);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) gk[k][e] = (float)q[e];
+            } else {
+                const f32x4 q = *(const MU_GLOBAL f32x4*)((const float*)P.src + off);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) gk[k][e] = q[e];
+            }
+            if (with_m) {
+                const f32x4 q = *(const MU_GLOBAL f32x4*)(P.mom + off);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) mk[k][e] = q[e];
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) mk[k][e] = 0.f;
+            }
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) load_gm<TS>(P, ti * TR + rr + RSTEP * k, tj * TC + cc, with_m, gk[k], mk[k]);
+    }
     float ss = 0.f;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        const int r = ti * T + rr + 16 * k, c0 = tj * T + cc;
+        const int r = ti * TR + rr + RSTEP * k, c0 = tj * TC + cc;
         float u[4];
-        make_u<TS>(P, r, c0, with_m, nest, A.mu, u);
+        make_u(P, r, c0, with_m, nest, A.mu, gk[k], mk[k], u);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             ss += u[e] * u[e];
-            tile[rr + 16 * k][cc + e] = u[e];
+            tile[rr + RSTEP * k][cc + e] = u[e];
         }
         if constexpr (sizeof(TX) == 4) store_x4<TX>(D + (int64_t)r * KD + c0, u);
     }
     __syncthreads();
     if constexpr (sizeof(TX) == 2) {
+        static_assert(TR % 32 == 0 && TC % 32 == 0, "whole K-blocks in both buffers");
 #pragma unroll
-        for (int pass = 0; pass < 2; ++pass) {
+        for (int pass = 0; pass < TR * TC / (NTHR * 8); ++pass) {
             const int q = pass * NTHR + tid;
-            const int pl = q >> 8, g = (q >> 6) & 3, c = (q >> 4) & 3, r16 = q & 15;
-            // D: row g*16 + r16, columns pl*32 + c*8 .. +7 of the tile
+            const int blk = q >> 6, c = (q >> 4) & 3, r16 = q & 15;
+            // D: block (row group g, k-panel pl) of the tile; chunk c of row r16
             {
+                const int g = blk % (TR / 16), pl = blk / (TR / 16);
                 const int row = g * 16 + r16, col = pl * 32 + c * 8;
                 bf16x8 o;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) o[e] = (bf16)tile[row][col + e];
-                *(bf16x8*)(D + kb_off(ti * T + row, tj * T + col, RD)) = o;
+                *(MU_GLOBAL bf16x8*)(D + kb_off(ti * TR + row, tj * TC + col, RD)) = o;
             }
-            // the other buffer: row (= tile column) g*16 + r16, columns (= tile
-            // rows) pl*32 + c*8 .. +7
+            // the other buffer: its rows are tile columns, its k the tile rows
             {
+                const int g = blk % (TC / 16), pl = blk / (TC / 16);
                 const int row = g * 16 + r16, col = pl * 32 + c * 8;
                 bf16x8 o;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) o[e] = (bf16)tile[col + e][row];
-                *(bf16x8*)(Tt + kb_off(tj * T + row, ti * T + col, KD)) = o;
+                *(MU_GLOBAL bf16x8*)(Tt + kb_off(tj * TC + row, ti * TR + col, KD)) = o;
             }
         }
     } else {
+        static_assert(TR == TC, "the fp32 transpose pass walks a square tile");
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            const int a = rr + 16 * k;
+            const int a = rr + RSTEP * k;
             float v[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) v[e] = tile[cc + e][a];
-            store_x4<TX>(Tt + (int64_t)(tj * T + a) * RD + ti * T + cc, v);
+            store_x4<TX>(Tt + (int64_t)(tj * TC + a) * RD + ti * TR + cc, v);
         }
     }
     const float s = block_sum(ss, red);
-    if (tid == 0) P.partials[local] = s;
+    if (tid == 0) *gp(P.partials + local) = s;
 }
 
 __global__ __launch_bounds__(NTHR) void k_norm(NormArgs A) {
     __shared__ float red[4];
     const NsProb& P = A.probs[blockIdx.x];
     float s = 0.f;
-    for (int i = threadIdx.x; i < P.nparts; i += NTHR) s += P.partials[i];
+    for (int i = threadIdx.x; i < P.nparts; i += NTHR) s += *gp(P.partials + i);
     s = block_sum(s, red);
     if (threadIdx.x == 0) {
         const float nrm = sqrtf(s);
-        P.fold[0] = 1.f / (nrm + A.eps);
-        if (P.norm_out) P.norm_out[0] = nrm;
+        *gp(P.fold) = 1.f / (nrm + A.eps);
+        if (P.norm_out) *gp(P.norm_out) = nrm;
     }
 }
 
-// O = fold * X0 written back in U-space: update (W - lr*wd*W - lr*scale*O) or output.
+// O = fold * X0 written back in U-space: update (W - lr*wd*W - lr*scale*O) or
+// output. Same tiling as k_prep, over the U-oriented buffer (X for wide
+// blocks, X^T for tall ones), which holds U in U's own orientation.
 template <typename TS, typename TX>
 __global__ __launch_bounds__(NTHR) void k_finish(FinishArgs A) {
-    __shared__ float tile[T][T + 1];
+    constexpr int TR = prep_rows<TX>(), TC = prep_cols<TX>();
+    constexpr int TPR = TC / 4, RSTEP = NTHR / TPR;
     const int t = blockIdx.x;
     const int p = __builtin_amdgcn_readfirstlane(find_prob(A.prefix, A.nprobs, t));
     const NsProb P = A.probs[p];   // by value: held in registers, never re-read after a store
     const int local = t - A.prefix[p];
-    const int tiles_n = P.np / T;
+    const bool wide = !P.tall;
+    const int RD = wide ? P.mp : P.np, KD = wide ? P.np : P.mp;
+    const TX* D = (const TX*)(wide ? P.x[0] : P.xt[0]);
+    const int tiles_n = KD / TC;
     const int ti = local / tiles_n, tj = local - ti * tiles_n;
     const int tid = threadIdx.x;
-    const int rr = tid >> 4, cc = (tid & 15) * 4;
-    const float f = P.fold[0];
-    const TX* X = (const TX*)P.x[0];
+    const int rr = tid / TPR, cc = (tid % TPR) * 4;
+    const float f = *gp(P.fold);
     const bool vec = P.vec != 0;
-    auto emit = [&](int r, int c0, const float o[4]) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int r = ti * TR + rr + RSTEP * k, c0 = tj * TC + cc;
         const int valid = (r < P.hr) ? max(0, min(4, P.hc - c0)) : 0;
-        if (valid == 0) return;
+        if (valid == 0) continue;
+        float o[4];
+        load_x4<TX>(D + op_off<TX>(r, c0, RD, KD), o);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] *= f;
         const int64_t off = (int64_t)r * P.ld + c0;
         if (P.oout) {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                if (e < valid) P.oout[off + e] = o[e];
+                if (e < valid) *gp(P.oout + off + e) = o[e];
         }
-        float w[4];
         if (A.with_update) {
+            float w[4];
             load4<TS>(P.param, off, valid, vec, w);
             const float decay = A.lr * A.wd, step = A.lr * P.scale;
 #pragma unroll
@@ -254,35 +309,6 @@ __global__ __launch_bounds__(NTHR) void k_finish(FinishArgs A) {
             store4<TS>(P.param, off, valid, vec, w);
         } else {
             store4<TS>(P.out, off, valid, vec, o);
-        }
-    };
-    if (!P.tall) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int r = ti * T + rr + 16 * k, c0 = tj * T + cc;
-            float o[4];
-            load_x4<TX>(X + op_off<TX>(r, c0, P.mp, P.np), o);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) o[e] *= f;
-            emit(r, c0, o);
-        }
-    } else {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int a = rr + 16 * k;
-            float v[4];
-            load_x4<TX>(X + op_off<TX>(ti * T + a, tj * T + cc, P.mp, P.np), v);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) tile[cc + e][a] = v[e] * f;
-        }
-        __syncthreads();
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int r = tj * T + rr + 16 * k, c0 = ti * T + cc;
-            float o[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) o[e] = tile[rr + 16 * k][cc + e];
-            emit(r, c0, o);
         }
     }
 }
@@ -294,25 +320,25 @@ __global__ __launch_bounds__(NTHR) void k_finish(FinishArgs A) {
 // ---------------------------------------------------------------------------
 template <typename TP>
 __device__ inline void adamw8(const AdamWDesc& D, int64_t i0, int cnt, const AdamWArgs& A) {
-    TP* p = (TP*)D.param + i0;
-    const TP* g = (const TP*)D.grad + i0;
-    float* m = D.m + i0;
-    float* v = D.v + i0;
+    MU_GLOBAL TP* p = (MU_GLOBAL TP*)D.param + i0;
+    const MU_GLOBAL TP* g = (const MU_GLOBAL TP*)D.grad + i0;
+    MU_GLOBAL float* m = (MU_GLOBAL float*)D.m + i0;
+    MU_GLOBAL float* v = (MU_GLOBAL float*)D.v + i0;
     float pv[8], gv[8], mv[8], vv[8];
     const bool full = (cnt == 8) && D.vec;
     if (full) {
         if constexpr (sizeof(TP) == 2) {
-            bf16x8 a = *(const bf16x8*)p, b = *(const bf16x8*)g;
+            bf16x8 a = *(const MU_GLOBAL bf16x8*)p, b = *(const MU_GLOBAL bf16x8*)g;
 #pragma unroll
             for (int e = 0; e < 8; ++e) { pv[e] = (float)a[e]; gv[e] = (float)b[e]; }
         } else {
-            f32x4 a0 = ((const f32x4*)p)[0], a1 = ((const f32x4*)p)[1];
-            f32x4 b0 = ((const f32x4*)g)[0], b1 = ((const f32x4*)g)[1];
+            f32x4 a0 = ((const MU_GLOBAL f32x4*)p)[0], a1 = ((const MU_GLOBAL f32x4*)p)[1];
+            f32x4 b0 = ((const MU_GLOBAL f32x4*)g)[0], b1 = ((const MU_GLOBAL f32x4*)g)[1];
 #pragma unroll
             for (int e = 0; e < 4; ++e) { pv[e] = a0[e]; pv[e + 4] = a1[e]; gv[e] = b0[e]; gv[e + 4] = b1[e]; }
         }
-        f32x4 m0 = ((const f32x4*)m)[0], m1 = ((const f32x4*)m)[1];
-        f32x4 v0 = ((const f32x4*)v)[0], v1 = ((const f32x4*)v)[1];
+        f32x4 m0 = ((const MU_GLOBAL f32x4*)m)[0], m1 = ((const MU_GLOBAL f32x4*)m)[1];
+        f32x4 v0 = ((const MU_GLOBAL f32x4*)v)[0], v1 = ((const MU_GLOBAL f32x4*)v)[1];
 #pragma unroll
         for (int e = 0; e < 4; ++e) { mv[e] = m0[e]; mv[e + 4] = m1[e]; vv[e] = v0[e]; vv[e + 4] = v1[e]; }
     } else {
@@ -337,15 +363,15 @@ __device__ inline void adamw8(const AdamWDesc& D, int64_t i0, int cnt, const Ada
             bf16x8 a;
 #pragma unroll
             for (int e = 0; e < 8; ++e) a[e] = (bf16)pv[e];
-            *(bf16x8*)p = a;
+            *(MU_GLOBAL bf16x8*)p = a;
         } else {
-            ((f32x4*)p)[0] = f32x4{pv[0], pv[1], pv[2], pv[3]};
-            ((f32x4*)p)[1] = f32x4{pv[4], pv[5], pv[6], pv[7]};
+            ((MU_GLOBAL f32x4*)p)[0] = f32x4{pv[0], pv[1], pv[2], pv[3]};
+            ((MU_GLOBAL f32x4*)p)[1] = f32x4{pv[4], pv[5], pv[6], pv[7]};
         }
-        ((f32x4*)m)[0] = f32x4{mv[0], mv[1], mv[2], mv[3]};
-        ((f32x4*)m)[1] = f32x4{mv[4], mv[5], mv[6], mv[7]};
-        ((f32x4*)v)[0] = f32x4{vv[0], vv[1], vv[2], vv[3]};
-        ((f32x4*)v)[1] = f32x4{vv[4], vv[5], vv[6], vv[7]};
+        ((MU_GLOBAL f32x4*)m)[0] = f32x4{mv[0], mv[1], mv[2], mv[3]};
+        ((MU_GLOBAL f32x4*)m)[1] = f32x4{mv[4], mv[5], mv[6], mv[7]};
+        ((MU_GLOBAL f32x4*)v)[0] = f32x4{vv[0], vv[1], vv[2], vv[3]};
+        ((MU_GLOBAL f32x4*)v)[1] = f32x4{vv[4], vv[5], vv[6], vv[7]};
     } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e)
@@ -362,11 +388,63 @@ __device__ inline int find_tensor(const int64_t* prefix, int n, int64_t c) {
     return lo;
 }
 
+// One AdamW element in fp32, in the order of the formula.
+__device__ __forceinline__ void adamw1(float& p, float g, float& m, float& v, const AdamWArgs& A, float lr,
+                                       float decay) {
+    m = A.beta1 * m + (1.f - A.beta1) * g;
+    v = A.beta2 * v + (1.f - A.beta2) * g * g;
+    const float mhat = m / A.bc1;
+    const float vhat = v / A.bc2;
+    p = (p - decay * p) - lr * mhat / (sqrtf(vhat) + A.eps);
+}
+
+// Whole chunk of a bf16 tensor whose buffers allow 16-byte accesses: each
+// thread owns two runs of 8 elements; every load of both is issued before any
+// arithmetic.
+__device__ __forceinline__ void adamw_chunk_bf16(const AdamWDesc& D, int64_t base, const AdamWArgs& A) {
+    constexpr int RUNS = ADAMW_CHUNK / (NTHR * 8);
+    bf16x8 pq[RUNS], gq[RUNS];
+    f32x4 mq[RUNS][2], vq[RUNS][2];
+#pragma unroll
+    for (int k = 0; k < RUNS; ++k) {
+        const int64_t i0 = base + (int64_t)k * NTHR * 8 + threadIdx.x * 8;
+        pq[k] = *(const MU_GLOBAL bf16x8*)((const bf16*)D.param + i0);
+        gq[k] = *(const MU_GLOBAL bf16x8*)((const bf16*)D.grad + i0);
+        mq[k][0] = *(const MU_GLOBAL f32x4*)(D.m + i0);
+        mq[k][1] = *(const MU_GLOBAL f32x4*)(D.m + i0 + 4);
+        vq[k][0] = *(const MU_GLOBAL f32x4*)(D.v + i0);
+        vq[k][1] = *(const MU_GLOBAL f32x4*)(D.v + i0 + 4);
+    }
+    const float lr = D.lr, decay = D.lr * D.wd;
+#pragma unroll
+    for (int k = 0; k < RUNS; ++k) {
+        const int64_t i0 = base + (int64_t)k * NTHR * 8 + threadIdx.x * 8;
+        bf16x8 po;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float p = (float)pq[k][e], m = mq[k][e >> 2][e & 3], v = vq[k][e >> 2][e & 3];
+            adamw1(p, (float)gq[k][e], m, v, A, lr, decay);
+            po[e] = (bf16)p;
+            mq[k][e >> 2][e & 3] = m;
+            vq[k][e >> 2][e & 3] = v;
+        }
+        *(MU_GLOBAL bf16x8*)((bf16*)D.param + i0) = po;
+        *(MU_GLOBAL f32x4*)(D.m + i0) = mq[k][0];
+        *(MU_GLOBAL f32x4*)(D.m + i0 + 4) = mq[k][1];
+        *(MU_GLOBAL f32x4*)(D.v + i0) = vq[k][0];
+        *(MU_GLOBAL f32x4*)(D.v + i0 + 4) = vq[k][1];
+    }
+}
+
 __global__ __launch_bounds__(NTHR) void k_adamw(AdamWArgs A) {
     const int64_t c = blockIdx.x;
-    const int i = find_tensor(A.prefix, A.n, c);
-    const AdamWDesc& D = A.descs[i];
+    const int i = __builtin_amdgcn_readfirstlane(find_tensor(A.prefix, A.n, c));
+    const AdamWDesc D = A.descs[i];   // by value: held in registers, never re-read after a store
     const int64_t base = (c - A.prefix[i]) * ADAMW_CHUNK;
+    if (D.dtype == DT_BF16 && D.vec && base + ADAMW_CHUNK <= D.numel) {
+        adamw_chunk_bf16(D, base, A);
+        return;
+    }
 #pragma unroll
     for (int pass = 0; pass < ADAMW_CHUNK / (NTHR * 8); ++pass) {
         const int64_t i0 = base + (int64_t)pass * NTHR * 8 + threadIdx.x * 8;

@@ -9,7 +9,13 @@
 namespace mu {
 
 // Prep tile edge (elements) of the momentum / transpose kernel.
-constexpr int PREP_TILE = 64;
+// Prep / finish tile over the U-oriented buffer: 32 x 128 with bf16
+// Newton-Schulz operands (whole K-blocks, long row runs), 64 x 64 with fp32
+// (buffers are padded to multiples of 64 only).
+template <typename TX> constexpr int prep_rows() { return sizeof(TX) == 2 ? 32 : 64; }
+template <typename TX> constexpr int prep_cols() { return sizeof(TX) == 2 ? 128 : 64; }
+inline int prep_rows_dt(int ns_dtype) { return ns_dtype == DT_BF16 ? 32 : 64; }
+inline int prep_cols_dt(int ns_dtype) { return ns_dtype == DT_BF16 ? 128 : 64; }
 
 struct PrepArgs {
     const NsProb* probs;
