@@ -177,6 +177,29 @@ def test_mixed_list_one_call():
         assert O.rel_fro(to_np(ms[i]), ref["m"]) <= MOM_TOL, shape
 
 
+def test_grouped_call_matches_separate_calls():
+    """One call over several matrices (grouped launches: one grid covers every
+    matrix, tiles found by search over the tile prefix) gives bitwise the same
+    parameters, momenta and O as one call per matrix."""
+    shapes = [(2048, 4608), (2048, 4608), (4608, 2048), (2048, 4608)]
+    print(f"[grouped vs separate] shapes={shapes}", flush=True)
+    ins = [make_matrix_inputs(sh, 13000 + i, torch.bfloat16, 1e-3, 0.02, 1e-3) for i, sh in enumerate(shapes)]
+    kw = dict(lr=0.02, weight_decay=0.01, mu=0.95, nesterov=True, ns_steps=5, precision="bf16")
+    w1 = [w.clone() for w, _, _ in ins]
+    m1 = [m.clone() for _, _, m in ins]
+    o1 = [torch.zeros(sh, dtype=torch.float32, device="cuda") for sh in shapes]
+    nso().muon_step(w1, [g for _, g, _ in ins], m1, ortho_outs=o1, **kw)
+    torch.cuda.synchronize()
+    for i, (w, g, m) in enumerate(ins):
+        w2, m2 = w.clone(), m.clone()
+        o2 = torch.zeros(shapes[i], dtype=torch.float32, device="cuda")
+        nso().muon_step([w2], [g], [m2], ortho_outs=[o2], **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(w1[i], w2), i
+        assert torch.equal(m1[i], m2), i
+        assert torch.equal(o1[i], o2), i
+
+
 def test_zero_gradient_and_momentum_decay_only():
     w = as_dtype(host_normal((256, 512), 13000, 0.02), torch.bfloat16).cuda()
     w0 = to_np(w)
