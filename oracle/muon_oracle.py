@@ -23,7 +23,9 @@ pages give, with no blocking, fusion or reordering:
 * AdamW with bias correction for the tensors routed away from Muon (nanochat
   optimizer page, "Parameter Grouping Strategy" and "AdamW Step
   Implementation"; the bias-correction scalars appear as runtime arguments of
-  ``_finish_kernel`` on the NeMo AutoModel muown_triton page).
+  ``_finish_kernel`` on the NeMo AutoModel muown_triton page);
+* QK-Clip, the post-update rescale of attention query/key weights (MuonClip
+  Optimizer page, "QK-Clip").
 
 Parity of each function is pinned in ``tests/test_oracle.py`` against closed
 forms, library routines (LAPACK SVD, torch's bfloat16 cast) and brute force.
@@ -243,6 +245,50 @@ def adamw_ref(param, grad, exp_avg, exp_avg_sq, *, lr: float, weight_decay: floa
 # ----------------------------------------------------------------------------
 # Routing of parameters between the two rules.
 # ----------------------------------------------------------------------------
+
+# QK-Clip threshold: MuonClip Optimizer page, "QK-Clip" and "Design Decisions".
+DEFAULT_QK_TAU = 100.0
+
+
+def qk_clip_ref(wq, wk, max_logit, *, q_heads: int, k_heads: int, tau: float = DEFAULT_QK_TAU):
+    """QK-Clip after the update (MuonClip Optimizer page, section "QK-Clip"):
+    every attention head whose largest logit magnitude exceeds tau has its
+    query and key weights multiplied by gamma = tau / max_logit; other heads are
+    left alone.
+
+    Readings where the page is silent:
+    * ``max_logit`` is given per query head (measured in the forward pass);
+    * gamma is formed in float32 and each weight becomes the float32 product
+      gamma * w (the caller rounds it to the weight's dtype);
+    * with grouped-query attention (``k_heads`` dividing ``q_heads``) a key
+      head takes the smallest gamma of the query heads that share it; with
+      ``k_heads == q_heads`` this is the page's per-head rule;
+    * a NaN max_logit never exceeds tau (no clip); +inf gives gamma = 0.
+
+    Heads are equal contiguous row blocks of ``wq`` [q_rows, cols] and ``wk``
+    [k_rows, cols]. Returns (wq_new, wk_new, gamma_q) in float32.
+    """
+    wq = np.asarray(wq, dtype=np.float32)
+    wk = np.asarray(wk, dtype=np.float32)
+    ml = np.asarray(max_logit, dtype=np.float32)
+    assert ml.shape == (q_heads,) and q_heads % k_heads == 0
+    t = np.float32(tau)
+    gamma_q = np.ones(q_heads, dtype=np.float32)
+    for h in range(q_heads):
+        if ml[h] > t:                      # False for NaN
+            with np.errstate(divide="ignore"):
+                gamma_q[h] = t / ml[h]     # float32 division; 0 for +inf
+    group = q_heads // k_heads
+    gamma_k = np.array([gamma_q[g * group:(g + 1) * group].min() for g in range(k_heads)], dtype=np.float32)
+    out_q, out_k = wq.copy(), wk.copy()
+    for h, sl in enumerate(head_blocks(wq.shape[0], q_heads)):
+        if gamma_q[h] != np.float32(1):
+            out_q[sl] = gamma_q[h] * wq[sl]      # float32 products
+    for g, sl in enumerate(head_blocks(wk.shape[0], k_heads)):
+        if gamma_k[g] != np.float32(1):
+            out_k[sl] = gamma_k[g] * wk[sl]
+    return out_q, out_k, gamma_q
+
 
 def route_ref(ndim: int, is_embedding_or_head: bool = False) -> str:
     """'muon' for hidden weights with two or more dimensions, else 'adamw'.

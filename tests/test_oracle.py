@@ -381,3 +381,84 @@ def test_golden_regression_fixture():
     assert np.allclose(r["w"], data["w_new"], rtol=0, atol=1e-15)
     assert np.allclose(r["o"], data["o"], rtol=0, atol=1e-14)
     assert np.allclose(r["m"], data["m_new"], rtol=0, atol=1e-15)
+
+
+# ---------------------------------------------------------------------------
+# QK-Clip (MuonClip Optimizer page, "QK-Clip"): per-head rescale of the query
+# and key weights when the head's largest logit magnitude exceeds tau.
+# ---------------------------------------------------------------------------
+
+def test_qk_clip_hand_values():
+    """Two heads, tau 100: max logits 50 (kept) and 200 (gamma 0.5, exact)."""
+    wq = np.arange(1, 9, dtype=np.float32).reshape(4, 2)
+    wk = -np.arange(1, 9, dtype=np.float32).reshape(4, 2)
+    q, k, g = O.qk_clip_ref(wq, wk, [50.0, 200.0], q_heads=2, k_heads=2, tau=100.0)
+    assert g.tolist() == [1.0, 0.5]
+    assert q.tolist() == [[1, 2], [3, 4], [2.5, 3], [3.5, 4]]
+    assert k.tolist() == [[-1, -2], [-3, -4], [-2.5, -3], [-3.5, -4]]
+
+
+def test_qk_clip_bounds_the_logits():
+    """With equal head counts, scaling Wq and Wk of a head by gamma scales its
+    logits (x Wq_h^T)(x Wk_h^T)^T by gamma^2: a clipped head's new largest logit
+    is tau^2 / max_logit < tau, recomputed here from synthetic activations."""
+    rng = np.random.default_rng(5)
+    heads, dh, d, tokens = 4, 8, 32, 16
+    x = rng.standard_normal((tokens, d))
+    wq = (rng.standard_normal((heads * dh, d)) * 2.0).astype(np.float32)
+    wk = (rng.standard_normal((heads * dh, d)) * 2.0).astype(np.float32)
+
+    def max_logits(a, b):
+        out = []
+        for sl in O.head_blocks(heads * dh, heads):
+            lg = (x @ a[sl].astype(np.float64).T) @ (x @ b[sl].astype(np.float64).T).T
+            out.append(np.abs(lg).max())
+        return np.array(out)
+
+    ml = max_logits(wq, wk)
+    tau = float(np.median(ml))            # about half the heads are clipped
+    q, k, g = O.qk_clip_ref(wq, wk, ml, q_heads=heads, k_heads=heads, tau=tau)
+    after = max_logits(q, k)
+    for h in range(heads):
+        if ml[h] > np.float32(tau):
+            assert after[h] == pytest.approx(float(g[h]) ** 2 * ml[h], rel=2e-6)
+            assert after[h] < tau
+        else:
+            assert after[h] == ml[h]
+
+
+def test_qk_clip_grouped_query_heads_take_the_group_minimum():
+    """Four query heads sharing two key heads: key head g takes the smallest
+    gamma of query heads 2g and 2g+1."""
+    wq = np.ones((8, 3), dtype=np.float32)
+    wk = np.ones((4, 3), dtype=np.float32)
+    ml = [125.0, 90.0, 400.0, 200.0]
+    q, k, g = O.qk_clip_ref(wq, wk, ml, q_heads=4, k_heads=2, tau=100.0)
+    f08 = np.float32(0.8)                 # 100 / 125 in float32
+    np.testing.assert_array_equal(g, np.array([f08, 1.0, 0.25, 0.5], dtype=np.float32))
+    np.testing.assert_array_equal(q[:, 0], np.array([f08, f08, 1, 1, 0.25, 0.25, 0.5, 0.5], dtype=np.float32))
+    np.testing.assert_array_equal(k[:, 0], np.array([f08, f08, 0.25, 0.25], dtype=np.float32))
+
+
+def test_qk_clip_equal_heads_is_the_page_rule():
+    """With one key head per query head every head uses its own gamma."""
+    rng = np.random.default_rng(6)
+    wq = rng.standard_normal((6, 5)).astype(np.float32)
+    wk = rng.standard_normal((6, 5)).astype(np.float32)
+    ml = np.array([30.0, 101.0, 1e4], dtype=np.float32)
+    q, k, g = O.qk_clip_ref(wq, wk, ml, q_heads=3, k_heads=3, tau=100.0)
+    for h in range(3):
+        s = slice(2 * h, 2 * h + 2)
+        want = np.float32(100.0) / ml[h] if ml[h] > 100 else np.float32(1.0)
+        assert g[h] == want
+        np.testing.assert_array_equal(q[s], want * wq[s] if want != 1 else wq[s])
+        np.testing.assert_array_equal(k[s], want * wk[s] if want != 1 else wk[s])
+
+
+def test_qk_clip_nan_keeps_and_inf_zeroes():
+    wq = np.full((2, 2), 3.0, dtype=np.float32)
+    wk = np.full((2, 2), -3.0, dtype=np.float32)
+    q, k, g = O.qk_clip_ref(wq, wk, [np.nan, np.inf], q_heads=2, k_heads=2)
+    assert g[0] == 1.0 and g[1] == 0.0
+    assert q[0].tolist() == [3.0, 3.0] and k[0].tolist() == [-3.0, -3.0]
+    assert np.all(q[1] == 0) and np.all(k[1] == 0)
