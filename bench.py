@@ -65,6 +65,42 @@ def traffic_from_profiles(kernel: str):
     return d.get("bytes_per_launch")
 
 
+def time_qk_clip(ps, mu, args, torch, head_dim: int = 128):
+    """QK-Clip (post-update per-head rescale) over the set's attention layers,
+    timed on its own after the steps: every query head is given a max logit
+    above tau, so every head is rescaled and the algorithmic traffic is one read
+    and one write of all query and key weights. None if the set has no wq/wk."""
+    import newton_schulz_orthogonalized_amd as nso
+    from newton_schulz_orthogonalized_amd import _lib
+    names = [e.name for e in ps.muon]
+    pairs = [(names.index(n), names.index(n[:-2] + "wk")) for n in names
+             if n.endswith(".wq") and n[:-2] + "wk" in names]
+    if not pairs:
+        return None
+    wqs = [mu["p"][i] for i, _ in pairs]
+    wks = [mu["p"][j] for _, j in pairs]
+    qh = [w.shape[0] // head_dim for w in wqs]
+    kh = [w.shape[0] // head_dim for w in wks]
+    gen = torch.Generator(device=wqs[0].device).manual_seed(77)
+    mls = [150.0 + 100.0 * torch.rand(h, generator=gen, device=wqs[0].device) for h in qh]
+    ws = _lib.workspace(_lib.mu_qk_clip_workspace_size(*_lib.qk_pairs(wqs, wks, mls, qh, kh)), wqs[0].device)
+    run = lambda: nso.qk_clip(wqs, wks, mls, q_heads=qh, k_heads=kh, tau=100.0, workspace=ws)
+    run()
+    torch.cuda.synchronize()
+    _lib.mu_profile_enable(True)
+    reps = max(1, args.steps)
+    for _ in range(reps):
+        run()
+    torch.cuda.synchronize()
+    _lib.mu_profile_enable(False)
+    pr = _lib.mu_profile_read(_lib.MU_K_QKCLIP)
+    nbytes = sum(2.0 * (a.numel() + b.numel()) * a.element_size() for a, b in zip(wqs, wks))
+    ms = pr["ms"] / max(1, pr["launches"])
+    gbs = nbytes / (ms * 1e-3) / 1e9 if ms > 0 else None
+    return {"layers": len(pairs), "q_heads": qh[0], "k_heads": kh[0], "ms_per_launch": ms,
+            "bytes_per_launch": nbytes, "gbs": gbs, "frac_hbm": (gbs / PEAK_HBM_GBS) if gbs else None}
+
+
 def build_set(ps, set_index, device, torch):
     from workloads import device_normal, seed_for
     dt = torch.bfloat16 if ps.dtype == "bf16" else torch.float32
@@ -239,6 +275,7 @@ def main():
         "prep_gbs": prep_gbs, "prep_frac_hbm": (prep_gbs / PEAK_HBM_GBS) if prep_gbs else None,
         "kernels": kernels, "roofline": roof, "source_digest": source_digest(),
     }
+    out["qk_clip"] = time_qk_clip(ps, mu, args, torch)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(ps, set_index, args.ns_steps)

@@ -152,6 +152,50 @@ typedef struct mu_adamw_hparams {
     int64_t step;
 } mu_adamw_hparams;
 
+/*
+ * QK-Clip after the update (MuonClip Optimizer page, section "QK-Clip"): each
+ * attention head whose largest logit magnitude exceeds tau has its query and
+ * key weight rows multiplied by gamma = tau / max_logit (gamma formed in
+ * float32; each weight becomes the float32 product rounded to nearest even to
+ * its dtype). One pair per attention layer.
+ *
+ * wq         [q_rows, cols] row-major, q_heads equal contiguous row blocks;
+ *            scaled in place
+ * wk         [k_rows, cols] row-major, k_heads row blocks; scaled in place.
+ *            With grouped-query attention (k_heads dividing q_heads) key head
+ *            g serves query heads g*G .. g*G+G-1 (G = q_heads / k_heads) and
+ *            takes the smallest gamma among them; k_heads == q_heads is the
+ *            page's per-head rule.
+ * dtype      MU_F32 | MU_BF16, both matrices
+ * max_logit  device float32 [q_heads], read only: max |q.k| of each query head
+ *            from the forward pass. NaN never exceeds tau (no clip); +inf
+ *            gives gamma = 0.
+ * gamma_out  optional device float32 [q_heads] receiving the factor applied
+ *            to each query head (1 when not clipped); may be NULL.
+ * Heads at or below tau are not written at all.
+ */
+typedef struct mu_qk_pair {
+    void* wq;
+    void* wk;
+    int64_t q_rows;
+    int64_t k_rows;
+    int64_t cols;
+    int32_t q_heads;
+    int32_t k_heads;
+    int32_t dtype;
+    int32_t pad0;
+    const float* max_logit;
+    float* gamma_out;
+} mu_qk_pair;
+
+/* Workspace bytes mu_qk_clip needs for this list (its segment table). */
+int mu_qk_clip_workspace_size(const mu_qk_pair* pairs, int32_t n, size_t* bytes);
+
+/* QK-Clip over the whole list in one launch (tau > 0 and finite). Buffers
+ * must not overlap; errors as for the other calls (nothing is enqueued). */
+int mu_qk_clip(const mu_qk_pair* pairs, int32_t n, float tau, void* workspace, size_t workspace_bytes,
+               void* stream);
+
 /* Workspace bytes mu_muon_step needs for this list (n == 0 gives 0). */
 int mu_muon_workspace_size(const mu_matrix* mats, int32_t n, const mu_muon_hparams* hp, size_t* bytes);
 
@@ -198,7 +242,8 @@ int mu_version(void);
 #define MU_K_APPLY 4     /* B X (last step fuses the update) */
 #define MU_K_FINISH 5    /* update when ns_steps == 0 */
 #define MU_K_ADAMW 6     /* AdamW */
-#define MU_K_COUNT 7
+#define MU_K_QKCLIP 7    /* QK-Clip rescale (bytes assume every head clipped) */
+#define MU_K_COUNT 8
 int mu_profile_enable(int on);
 int mu_profile_read(int kernel, double* total_ms, int64_t* launches, double* flops, double* bytes);
 const char* mu_kernel_name(int kernel);

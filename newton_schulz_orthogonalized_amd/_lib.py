@@ -30,13 +30,13 @@ MU_ERR_LAYOUT = 3
 MU_ERR_WORKSPACE = 4
 MU_ERR_HIP = 5
 
-MU_K_PREP, MU_K_NORM, MU_K_GRAM, MU_K_GRAM2, MU_K_APPLY, MU_K_FINISH, MU_K_ADAMW = range(7)
-MU_K_COUNT = 7
+MU_K_PREP, MU_K_NORM, MU_K_GRAM, MU_K_GRAM2, MU_K_APPLY, MU_K_FINISH, MU_K_ADAMW, MU_K_QKCLIP = range(8)
+MU_K_COUNT = 8
 
 EXPORTED = (
     "mu_muon_workspace_size", "mu_muon_step", "mu_ortho_workspace_size", "mu_muon_orthogonalize",
-    "mu_adamw_workspace_size", "mu_adamw_step", "mu_status_string", "mu_last_error", "mu_version",
-    "mu_profile_enable", "mu_profile_read", "mu_kernel_name",
+    "mu_adamw_workspace_size", "mu_adamw_step", "mu_qk_clip_workspace_size", "mu_qk_clip",
+    "mu_status_string", "mu_last_error", "mu_version", "mu_profile_enable", "mu_profile_read", "mu_kernel_name",
 )
 
 
@@ -78,6 +78,15 @@ class MuAdamwHparams(ctypes.Structure):
                 ("step", ctypes.c_int64)]
 
 
+class MuQkPair(ctypes.Structure):
+    _fields_ = [
+        ("wq", ctypes.c_void_p), ("wk", ctypes.c_void_p), ("q_rows", ctypes.c_int64), ("k_rows", ctypes.c_int64),
+        ("cols", ctypes.c_int64), ("q_heads", ctypes.c_int32), ("k_heads", ctypes.c_int32),
+        ("dtype", ctypes.c_int32), ("pad0", ctypes.c_int32), ("max_logit", ctypes.c_void_p),
+        ("gamma_out", ctypes.c_void_p),
+    ]
+
+
 class MuonError(RuntimeError):
     def __init__(self, status: int, detail: str):
         super().__init__(f"{_status_text(status)} (status {status}): {detail}")
@@ -100,6 +109,8 @@ def _load() -> ctypes.CDLL:
     lib.mu_adamw_workspace_size.argtypes = [ctypes.c_int32, P(sz)]
     lib.mu_adamw_step.argtypes = [P(MuTensor), ctypes.c_int32, P(MuAdamwHparams), ctypes.c_void_p, sz,
                                   ctypes.c_void_p]
+    lib.mu_qk_clip_workspace_size.argtypes = [P(MuQkPair), ctypes.c_int32, P(sz)]
+    lib.mu_qk_clip.argtypes = [P(MuQkPair), ctypes.c_int32, ctypes.c_float, ctypes.c_void_p, sz, ctypes.c_void_p]
     lib.mu_status_string.argtypes = [ctypes.c_int]
     lib.mu_status_string.restype = ctypes.c_char_p
     lib.mu_last_error.argtypes = []
@@ -261,6 +272,37 @@ def mu_adamw_step(ts, n, beta1: float, beta2: float, eps: float, step: int,
     ws = 0 if workspace is None else workspace.data_ptr()
     nb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(LIB.mu_adamw_step(ts, n, ctypes.byref(hp), ws, nb, _stream(stream)))
+
+
+def qk_pairs(wqs, wks, max_logits, q_heads, k_heads, gamma_outs=None):
+    n = len(wqs)
+    arr = (MuQkPair * max(n, 1))()
+    for i in range(n):
+        wq, wk, ml = wqs[i], wks[i], max_logits[i]
+        for t, what in ((wq, "wq"), (wk, "wk"), (ml, "max_logit")):
+            _require(t, what)
+        if wq.dim() != 2 or wk.dim() != 2 or wq.shape[1] != wk.shape[1]:
+            raise ValueError("wq and wk must be 2-D with the same number of columns")
+        if wk.dtype != wq.dtype or ml.dtype != torch.float32:
+            raise TypeError("wk must share wq's dtype and max_logit must be float32")
+        go = None if gamma_outs is None else gamma_outs[i]
+        if go is not None:
+            _require(go, "gamma_out")
+        arr[i] = MuQkPair(_ptr(wq), _ptr(wk), wq.shape[0], wk.shape[0], wq.shape[1], int(q_heads[i]),
+                          int(k_heads[i]), _dtype_code(wq), 0, _ptr(ml), _ptr(go))
+    return arr, n
+
+
+def mu_qk_clip_workspace_size(pairs, n) -> int:
+    out = ctypes.c_size_t(0)
+    _check(LIB.mu_qk_clip_workspace_size(pairs, n, ctypes.byref(out)))
+    return out.value
+
+
+def mu_qk_clip(pairs, n, tau: float, workspace: Optional[torch.Tensor], stream=None) -> None:
+    ws = 0 if workspace is None else workspace.data_ptr()
+    nb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(LIB.mu_qk_clip(pairs, n, float(tau), ws, nb, _stream(stream)))
 
 
 def mu_version() -> int:

@@ -71,3 +71,19 @@ def adamw_step(params, grads, exp_avgs, exp_avg_sqs, *, lr, weight_decay, beta1:
     if workspace is None:
         workspace = _lib.workspace(_lib.mu_adamw_workspace_size(n), params[0].device)
     _lib.mu_adamw_step(ts, n, beta1, beta2, eps, step, workspace, stream)
+
+
+def qk_clip(wqs, wks, max_logits, *, q_heads, k_heads, tau: float = 100.0, gamma_outs=None,
+            workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """QK-Clip over attention layers (one (wq, wk, max_logit) per layer): heads
+    whose max |logit| exceeds tau get their query and key rows scaled by
+    tau / max_logit, in place. q_heads / k_heads are per layer (or one int)."""
+    n = len(wqs)
+    qh = list(q_heads) if isinstance(q_heads, (list, tuple)) else [q_heads] * n
+    kh = list(k_heads) if isinstance(k_heads, (list, tuple)) else [k_heads] * n
+    pairs, n = _lib.qk_pairs(wqs, wks, max_logits, qh, kh, gamma_outs)
+    if n == 0:
+        return
+    if workspace is None:
+        workspace = _lib.workspace(_lib.mu_qk_clip_workspace_size(pairs, n), wqs[0].device)
+    _lib.mu_qk_clip(pairs, n, tau, workspace, stream)

@@ -670,6 +670,93 @@ int mu_muon_orthogonalize(const mu_ortho* xs, int32_t n, const mu_muon_hparams* 
     return run_pipeline(pl, (char*)ws, hp, dt, false, (hipStream_t)stream);
 }
 
+// ---------------------------------------------------------------------------
+// QK-Clip
+// ---------------------------------------------------------------------------
+namespace {
+int64_t qk_segments(const mu_qk_pair* pairs, int32_t n) {
+    int64_t s = 0;
+    for (int i = 0; i < n; ++i) s += (int64_t)pairs[i].q_heads + pairs[i].k_heads;
+    return s;
+}
+size_t qk_table_bytes(int64_t segs) { return sizeof(QkSeg) * (size_t)segs + sizeof(int64_t) * (size_t)(segs + 1); }
+}  // namespace
+
+int mu_qk_clip_workspace_size(const mu_qk_pair* pairs, int32_t n, size_t* bytes) {
+    g_err.clear();
+    if (!bytes) return fail(MU_ERR_INVALID_ARG, "bytes is null");
+    if (n < 0) return fail(MU_ERR_INVALID_ARG, "n must be >= 0");
+    if (n > 0 && !pairs) return fail(MU_ERR_INVALID_ARG, "pair list is null");
+    for (int i = 0; i < n; ++i)
+        if (pairs[i].q_heads < 1 || pairs[i].k_heads < 1)
+            return fail(MU_ERR_INVALID_ARG, "pair %d: head counts must be >= 1", i);
+    *bytes = n == 0 ? 0 : align_up(qk_table_bytes(qk_segments(pairs, n)));
+    return MU_OK;
+}
+
+int mu_qk_clip(const mu_qk_pair* pairs, int32_t n, float tau, void* ws, size_t ws_bytes, void* stream) {
+    g_err.clear();
+    if (n < 0) return fail(MU_ERR_INVALID_ARG, "n must be >= 0");
+    if (n > 0 && !pairs) return fail(MU_ERR_INVALID_ARG, "pair list is null");
+    if (!std::isfinite(tau) || !(tau > 0.f)) return fail(MU_ERR_INVALID_ARG, "tau must be finite and > 0");
+    std::vector<QkSeg> segs;
+    std::vector<int64_t> prefix(1, 0);
+    std::vector<Range> ranges;
+    double bytes = 0;
+    for (int i = 0; i < n; ++i) {
+        const mu_qk_pair& q = pairs[i];
+        if (q.dtype != MU_F32 && q.dtype != MU_BF16) return fail(MU_ERR_DTYPE, "pair %d: unknown dtype %d", i, q.dtype);
+        if (!q.wq || !q.wk || !q.max_logit) return fail(MU_ERR_INVALID_ARG, "pair %d: null wq/wk/max_logit", i);
+        if (q.q_rows <= 0 || q.k_rows <= 0 || q.cols <= 0) return fail(MU_ERR_INVALID_ARG, "pair %d: sizes must be > 0", i);
+        if (q.q_rows > MU_MAX_DIM || q.k_rows > MU_MAX_DIM || q.cols > MU_MAX_DIM)
+            return fail(MU_ERR_INVALID_ARG, "pair %d: dimension above %d", i, MU_MAX_DIM);
+        if (q.q_heads < 1 || q.k_heads < 1 || q.q_rows % q.q_heads != 0 || q.k_rows % q.k_heads != 0)
+            return fail(MU_ERR_INVALID_ARG, "pair %d: head counts must be >= 1 and divide the rows", i);
+        if (q.q_heads % q.k_heads != 0) return fail(MU_ERR_INVALID_ARG, "pair %d: k_heads must divide q_heads", i);
+        const size_t es = dtype_size(q.dtype);
+        if (!aligned(q.wq, es) || !aligned(q.wk, es) || !aligned(q.max_logit, 4) || (q.gamma_out && !aligned(q.gamma_out, 4)))
+            return fail(MU_ERR_LAYOUT, "pair %d: misaligned buffer", i);
+        const int64_t nq = q.q_rows * q.cols, nk = q.k_rows * q.cols;
+        ranges.push_back({(uintptr_t)q.wq, (uintptr_t)q.wq + (size_t)nq * es, i});
+        ranges.push_back({(uintptr_t)q.wk, (uintptr_t)q.wk + (size_t)nk * es, i});
+        ranges.push_back({(uintptr_t)q.max_logit, (uintptr_t)q.max_logit + 4 * (size_t)q.q_heads, i});
+        if (q.gamma_out) ranges.push_back({(uintptr_t)q.gamma_out, (uintptr_t)q.gamma_out + 4 * (size_t)q.q_heads, i});
+        const int G = q.q_heads / q.k_heads;
+        auto add = [&](void* base, int64_t rows, int heads, int h, const float* ml, int nml, float* gout) {
+            const int64_t per = rows / heads * q.cols;
+            char* w = (char*)base + (size_t)(h * per) * es;
+            segs.push_back(QkSeg{w, per, q.dtype, (int32_t)aligned(w, 16), ml, nml, 0, gout});
+            prefix.push_back(prefix.back() + (per + QK_CHUNK - 1) / QK_CHUNK);
+        };
+        for (int h = 0; h < q.q_heads; ++h)
+            add(q.wq, q.q_rows, q.q_heads, h, q.max_logit + h, 1, q.gamma_out ? q.gamma_out + h : nullptr);
+        for (int g = 0; g < q.k_heads; ++g) add(q.wk, q.k_rows, q.k_heads, g, q.max_logit + (size_t)g * G, G, nullptr);
+        bytes += 2.0 * (double)(nq + nk) * (double)es + 4.0 * (q.q_heads + (double)q.q_heads);
+    }
+    if (ranges_overlap(ranges)) return fail(MU_ERR_LAYOUT, "buffers of the pair list overlap");
+    if (n == 0 || prefix.back() == 0) return MU_OK;
+    const size_t need = align_up(qk_table_bytes((int64_t)segs.size()));
+    if (!ws) return fail(MU_ERR_WORKSPACE, "workspace is null (need %zu bytes)", need);
+    if (!aligned(ws, ALIGN)) return fail(MU_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    if (ws_bytes < need) return fail(MU_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, need);
+    if (prefix.back() > 0x7fffffffLL || segs.size() > 0x7fffffffu)
+        return fail(MU_ERR_INVALID_ARG, "too many elements for one launch");
+
+    std::vector<char> table(qk_table_bytes((int64_t)segs.size()));
+    std::memcpy(table.data(), segs.data(), sizeof(QkSeg) * segs.size());
+    std::memcpy(table.data() + sizeof(QkSeg) * segs.size(), prefix.data(), sizeof(int64_t) * prefix.size());
+    hipStream_t s = (hipStream_t)stream;
+    int rc = upload(table.data(), table.size(), ws, s);
+    if (rc) return rc;
+    QkArgs a{};
+    a.segs = (const QkSeg*)ws;
+    a.prefix = (const int64_t*)((char*)ws + sizeof(QkSeg) * segs.size());
+    a.n = (int)segs.size();
+    a.total_chunks = prefix.back();
+    a.tau = tau;
+    return timed_launch(MU_K_QKCLIP, 0.0, bytes, s, [&] { return launch_qkclip(a, s); }, "qk_clip launch");
+}
+
 int mu_adamw_workspace_size(int32_t n, size_t* bytes) {
     g_err.clear();
     if (!bytes) return fail(MU_ERR_INVALID_ARG, "bytes is null");
@@ -795,6 +882,7 @@ const char* mu_kernel_name(int k) {
         case MU_K_APPLY: return "apply";
         case MU_K_FINISH: return "finish";
         case MU_K_ADAMW: return "adamw";
+        case MU_K_QKCLIP: return "qk_clip";
         default: return "unknown";
     }
 }

@@ -7,6 +7,7 @@
 //            fold = 1/(||U||_F + eps).
 //  k_finish  ns_steps == 0: O = fold * X0, then the update (or the output).
 //  k_adamw   bias-corrected AdamW over a flat list of tensors, one launch.
+//  k_qkclip  QK-Clip: per-head rescale of attention query/key weights.
 //
 // Momentum: MuonClip Optimizer page, section "Momentum" (EMA, decay 0.95).
 // Nesterov blend: named on the nanochat optimizer page ("Muon Step
@@ -455,6 +456,52 @@ __global__ __launch_bounds__(NTHR) void k_adamw(AdamWArgs A) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// QK-Clip (MuonClip Optimizer page, "QK-Clip"). Workgroup c scales elements
+// [k*CHUNK, (k+1)*CHUNK) of segment i (a head's row block) by the segment's
+// gamma: the smallest tau / max_logit over the query heads it follows that
+// exceed tau, 1 if none does (then nothing is written).
+// ---------------------------------------------------------------------------
+template <typename TW>
+__device__ __forceinline__ void qk_scale8(MU_GLOBAL TW* w, int cnt, bool vec, float g) {
+    if (vec && cnt == 8) {
+        if constexpr (sizeof(TW) == 2) {
+            bf16x8 q = *(const MU_GLOBAL bf16x8*)w;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) q[e] = (bf16)(g * (float)q[e]);
+            *(MU_GLOBAL bf16x8*)w = q;
+        } else {
+            f32x4 a = ((const MU_GLOBAL f32x4*)w)[0], b = ((const MU_GLOBAL f32x4*)w)[1];
+            ((MU_GLOBAL f32x4*)w)[0] = g * a;
+            ((MU_GLOBAL f32x4*)w)[1] = g * b;
+        }
+    } else {
+        for (int e = 0; e < cnt; ++e) w[e] = from_f32<TW>(g * to_f32<TW>(w[e]));
+    }
+}
+
+__global__ __launch_bounds__(NTHR) void k_qkclip(QkArgs A) {
+    const int64_t c = blockIdx.x;
+    const int i = __builtin_amdgcn_readfirstlane(find_tensor(A.prefix, A.n, c));
+    const QkSeg S = A.segs[i];   // by value: held in registers, never re-read after a store
+    const int64_t base = (c - A.prefix[i]) * QK_CHUNK;
+    float g = 1.f;
+    for (int j = 0; j < S.nml; ++j) {
+        const float ml = *gp(S.ml + j);
+        if (ml > A.tau) g = fminf(g, A.tau / ml);   // false for NaN; 0 for +inf
+    }
+    if (base == 0 && S.gamma_out && threadIdx.x == 0) *gp(S.gamma_out) = g;
+    if (g == 1.f) return;
+#pragma unroll
+    for (int pass = 0; pass < QK_CHUNK / (NTHR * 8); ++pass) {
+        const int64_t i0 = base + (int64_t)pass * NTHR * 8 + threadIdx.x * 8;
+        if (i0 >= S.numel) break;
+        const int cnt = (int)min<int64_t>(8, S.numel - i0);
+        if (S.dtype == DT_BF16) qk_scale8<bf16>((MU_GLOBAL bf16*)S.w + i0, cnt, S.vec != 0, g);
+        else qk_scale8<float>((MU_GLOBAL float*)S.w + i0, cnt, S.vec != 0, g);
+    }
+}
+
 }  // namespace
 
 hipError_t launch_prep(const PrepArgs& a, hipStream_t s) {
@@ -492,6 +539,12 @@ hipError_t launch_finish(const FinishArgs& a, hipStream_t s) {
 hipError_t launch_adamw(const AdamWArgs& a, hipStream_t s) {
     if (a.total_chunks <= 0) return hipSuccess;
     hipLaunchKernelGGL(k_adamw, dim3((unsigned)a.total_chunks), dim3(NTHR), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_qkclip(const QkArgs& a, hipStream_t s) {
+    if (a.total_chunks <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_qkclip, dim3((unsigned)a.total_chunks), dim3(NTHR), 0, s, a);
     return hipGetLastError();
 }
 

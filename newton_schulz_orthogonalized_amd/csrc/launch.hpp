@@ -95,4 +95,25 @@ struct AdamWArgs {
 constexpr int ADAMW_CHUNK = 4096;  // elements per workgroup
 hipError_t launch_adamw(const AdamWArgs& a, hipStream_t s);
 
+// QK-Clip: one segment per (layer, query or key matrix, head) row block.
+struct QkSeg {
+    void* w;             // first element of the head's rows
+    int64_t numel;
+    int32_t dtype;
+    int32_t vec;         // 16-byte aligned start: vector path
+    const float* ml;     // max logits of the query heads this block follows
+    int32_t nml;         // 1 for a query head, G for a key head
+    int32_t pad;
+    float* gamma_out;    // query heads: optional per-head gamma output
+};
+struct QkArgs {
+    const QkSeg* segs;
+    const int64_t* prefix;  // n+1 cumulative chunks
+    int n;
+    int64_t total_chunks;
+    float tau;
+};
+constexpr int QK_CHUNK = 8192;  // elements per workgroup
+hipError_t launch_qkclip(const QkArgs& a, hipStream_t s);
+
 }  // namespace mu

@@ -131,3 +131,43 @@ def test_ortho_validation(lib):
     x = lib.MuOrtho(A, A, 10, 20, lib.MU_BF16, 1, None)
     arr = (lib.MuOrtho * 1)(x)
     assert lib.LIB.mu_muon_orthogonalize(arr, 1, ctypes.byref(_hp(lib)), None, 0, None) == lib.MU_ERR_LAYOUT
+
+
+def _qk(lib, **kw):
+    d = dict(wq=A, wk=A + (1 << 24), q_rows=64, k_rows=16, cols=32, q_heads=8, k_heads=2, dtype=lib.MU_BF16,
+             pad0=0, max_logit=A + (2 << 24), gamma_out=None)
+    d.update(kw)
+    return lib.MuQkPair(**d)
+
+
+def _clip(lib, pairs, tau=100.0, ws=None, nbytes=0):
+    arr = (lib.MuQkPair * max(len(pairs), 1))(*pairs)
+    return lib.LIB.mu_qk_clip(arr, len(pairs), tau, ws, nbytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q_heads=3), 1), (dict(k_heads=3), 1), (dict(q_heads=4, k_heads=8, k_rows=16), 1), (dict(cols=0), 1),
+    (dict(wq=None), 1), (dict(max_logit=None), 1), (dict(dtype=5), 2), (dict(wk=A + 2), 3),
+    (dict(max_logit=A + 3), 3), (dict(gamma_out=A + (2 << 24) + 16), 3),
+])
+def test_qk_clip_bad_pair_rejected(lib, kw, code):
+    assert _clip(lib, [_qk(lib, **kw)]) == code
+    assert lib.mu_last_error() != ""
+
+
+def test_qk_clip_tau_and_workspace_checks(lib):
+    for tau in (0.0, -1.0, float("nan"), float("inf")):
+        assert _clip(lib, [_qk(lib)], tau=tau) == lib.MU_ERR_INVALID_ARG
+    assert _clip(lib, [_qk(lib)]) == lib.MU_ERR_WORKSPACE
+    arr = (lib.MuQkPair * 2)(_qk(lib), _qk(lib, wq=A + (4 << 24), wk=A + (5 << 24), max_logit=A + (6 << 24)))
+    need = ctypes.c_size_t(0)
+    assert lib.LIB.mu_qk_clip_workspace_size(arr, 2, ctypes.byref(need)) == 0
+    assert need.value >= 2 * (8 + 2) * 8   # one segment per head of each matrix
+    assert lib.LIB.mu_qk_clip(arr, 2, 100.0, A + (9 << 24), need.value - 1, None) == lib.MU_ERR_WORKSPACE
+    assert _clip(lib, []) == 0                               # empty list: no-op without a device
+
+
+def test_qk_clip_overlapping_pairs_rejected(lib):
+    a = _qk(lib)
+    b = _qk(lib, wq=A + (1 << 24) + 64, wk=A + (4 << 24), max_logit=A + (6 << 24))   # b.wq inside a.wk
+    assert _clip(lib, [a, b]) == lib.MU_ERR_LAYOUT
