@@ -132,26 +132,22 @@ def cpu_baseline(ps, set_index, ns_steps):
         cores = max([int(i.get("num_threads", 1)) for i in threadpool_info()] + [1])
     except Exception:  # pragma: no cover
         cores = os.cpu_count() or 1
-    # sample: layer 0's distinct Muon shapes, smallest first, up to three
-    # (about 10 s of float64 work on the 8B set) + 8M AdamW elements
-    shapes, picked = [], []
-    for e in ps.muon:
-        key = (e.shape, e.heads)
-        if key not in shapes:
-            shapes.append(key)
-            picked.append(e)
-    picked.sort(key=lambda e: e.shape[0] * e.shape[1] * min(e.shape) // e.heads)
-    picked = picked[:3]
+    # sample: the set's Muon matrices in order (layer 0 first) until about 15 s
+    # of float64 work (all seven of layer 0 but the last on the 8B set), plus
+    # 8M AdamW elements
     from workloads import MuonEntry, ParamSet
-    sample = ParamSet("sample", [MuonEntry(e.name, e.shape, e.heads) for e in picked])
-    t_muon = 0.0
-    for k, e in enumerate(picked):
+    budget_s, t_muon, picked = 15.0, 0.0, []
+    for k, e in enumerate(ps.muon):
+        if t_muon >= budget_s:
+            break
         w = host_normal(e.shape, 777 + k, ps.weight_std)
         g = host_normal(e.shape, 778 + k, ps.grad_std)
         m = host_normal(e.shape, 779 + k, ps.mom_std)
         t0 = time.perf_counter()
         O.muon_step_ref(w, g, m, lr=0.02, weight_decay=0.01, heads=e.heads, coeffs=O.default_coeffs(ns_steps))
         t_muon += time.perf_counter() - t0
+        picked.append(e)
+    sample = ParamSet("sample", [MuonEntry(e.name, e.shape, e.heads) for e in picked])
     n_aw = min(8 << 20, max(1, ps.adamw_elems()))
     t_aw = 0.0
     if ps.adamw:
@@ -163,7 +159,12 @@ def cpu_baseline(ps, set_index, ns_steps):
     muon_scale = ps.ns_flops(ns_steps) / sample.ns_flops(ns_steps)
     aw_scale = ps.adamw_elems() / n_aw if ps.adamw else 0.0
     est_ms = 1e3 * (t_muon * muon_scale + t_aw * aw_scale)
-    desc = ", ".join(f"{e.shape[0]}x{e.shape[1]}" + (f"/{e.heads}h" if e.heads > 1 else "") for e in picked)
+    counts = {}
+    for e in picked:
+        key = f"{e.shape[0]}x{e.shape[1]}" + (f"/{e.heads}h" if e.heads > 1 else "")
+        counts[key] = counts.get(key, 0) + 1
+    desc = ", ".join(f"{c} x {k}" for k, c in counts.items())
+    desc = f"the first {len(picked)} of {len(ps.muon)}: {desc}"
     return {"value": est_ms, "unit": "ms", "cores": cores, "kind": "oracle",
             "sample": (f"float64 numpy oracle on Muon matrices [{desc}] ({t_muon:.2f} s) scaled by Newton-Schulz "
                        f"flops x{muon_scale:.1f}, plus AdamW on {n_aw} elements ({t_aw:.2f} s) scaled by "
