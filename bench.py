@@ -39,6 +39,7 @@ def parse():
     ap.add_argument("--ns-steps", type=int, default=5)
     ap.add_argument("--precision", default="bf16", choices=["bf16", "f32"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceilings", action="store_true", help="skip the copy / library-GEMM ceiling measurement")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run a plain device copy of this many MiB first (counter calibration)")
     return ap.parse_args()
@@ -63,6 +64,44 @@ def traffic_from_profiles(kernel: str):
     if d.get("source_digest") != source_digest():
         return None
     return d.get("bytes_per_launch")
+
+
+def measure_ceilings(torch, device):
+    """Measured ceilings on this GPU, next to the spec peaks: the HBM rate of a
+    plain 2 GiB device-to-device copy (read + write bytes), and the vendor
+    library's dense bf16 GEMM (torch.matmul, hipBLASLt) on the two product
+    shapes of one Newton-Schulz step on a 4096 x 14336 matrix (the Gram
+    X X^T counted as a full 2 m^2 n product here; operands contiguous)."""
+    out = {}
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        ev0.record()
+        for _ in range(reps):
+            fn()
+        ev1.record()
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / reps
+
+    a = torch.empty(1 << 30, dtype=torch.bfloat16, device=device)
+    b = torch.empty_like(a)
+    a.fill_(1)
+    ms = timed(lambda: b.copy_(a), 10)
+    out["hbm_copy_gbs"] = 2 * a.numel() * 2 / (ms * 1e-3) / 1e9
+    del a, b
+    m, n = 4096, 14336
+    x = torch.randn(m, n, device=device).to(torch.bfloat16)
+    xt = x.t().contiguous()
+    bm = torch.randn(m, m, device=device).to(torch.bfloat16)
+    ms_g = timed(lambda: torch.matmul(x, xt), 10)
+    ms_a = timed(lambda: torch.matmul(bm, x), 10)
+    out["library_gemm_tflops"] = {"gram_4096x14336": 2.0 * m * m * n / (ms_g * 1e-3) / 1e12,
+                                  "apply_4096x4096x14336": 2.0 * m * m * n / (ms_a * 1e-3) / 1e12}
+    del x, xt, bm
+    torch.cuda.empty_cache()
+    return out
 
 
 def time_qk_clip(ps, mu, args, torch, head_dim: int = 128):
@@ -277,6 +316,9 @@ def main():
         "kernels": kernels, "roofline": roof, "source_digest": source_digest(),
     }
     out["qk_clip"] = time_qk_clip(ps, mu, args, torch)
+    if not args.no_ceilings:
+        print("[bench] measuring copy and library-GEMM ceilings", file=sys.stderr, flush=True)
+        out["ceilings"] = measure_ceilings(torch, device)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(ps, set_index, args.ns_steps)
