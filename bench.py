@@ -46,10 +46,16 @@ def parse():
 
 
 def source_digest() -> str:
+    """Digest of the kernel sources with comments and whitespace removed, so
+    that recorded counter figures stay attached to the code they measured."""
+    import re
     h = hashlib.sha256()
-    for f in ("ns_gemm.hip", "elementwise.hip", "common.hpp"):
-        with open(os.path.join(ROOT, "newton_schulz_orthogonalized_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+    for f in ("ns_gemm.hip", "elementwise.hip", "common.hpp", "launch.hpp"):
+        with open(os.path.join(ROOT, "newton_schulz_orthogonalized_amd", "csrc", f)) as fh:
+            src = fh.read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        h.update(" ".join(src.split()).encode())
     return h.hexdigest()[:16]
 
 

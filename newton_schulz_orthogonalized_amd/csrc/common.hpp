@@ -105,23 +105,12 @@ __device__ inline int64_t op_off(int r, int k, int R, int K) {
     else return (int64_t)r * K + k;
 }
 
-__device__ inline float bf2f(bf16 v) { return (float)v; }
-__device__ inline bf16 f2bf(float v) { return (bf16)v; }  // v_cvt_pk_bf16_f32, round to nearest even
-
 template <typename T> __device__ inline float to_f32(T v);
 template <> __device__ inline float to_f32<float>(float v) { return v; }
 template <> __device__ inline float to_f32<bf16>(bf16 v) { return (float)v; }
 template <typename T> __device__ inline T from_f32(float v);
 template <> __device__ inline float from_f32<float>(float v) { return v; }
 template <> __device__ inline bf16 from_f32<bf16>(float v) { return (bf16)v; }
-
-// Load/store an element of a buffer whose element type is chosen at run time.
-__device__ inline float load_dt(const void* p, int64_t i, int dt) {
-    return dt == DT_BF16 ? (float)((const bf16*)p)[i] : ((const float*)p)[i];
-}
-__device__ inline void store_dt(void* p, int64_t i, int dt, float v) {
-    if (dt == DT_BF16) ((bf16*)p)[i] = (bf16)v; else ((float*)p)[i] = v;
-}
 
 // Wavefront sum in a fixed order (butterfly over 64 lanes): every lane ends
 // with the same value, and the order does not depend on timing.

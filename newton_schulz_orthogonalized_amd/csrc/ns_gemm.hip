@@ -26,12 +26,13 @@
 // four LDS slots.
 // fp32: v_mfma_f32_16x16x4_f32, 64x64 tiles, BK = 32, row-major operands.
 //
-// Epilogue: accumulators are staged per wave through LDS in 16-row strips,
-// then stored with 16-byte accesses in a row pass and, for transposed outputs
-// (Gram mirror, X'^T, or a tall weight), a column pass. It applies the fold
-// 1/||U||_F of the first step (so the normalised X0 is never materialised), the
-// step coefficients, and on the last step the decoupled-weight-decay update
-// W <- W - lr*wd*W - lr*scale*O straight into the parameter.
+// Epilogue: row-major outputs are staged per wave through LDS in 16-row strips
+// and stored as 16-byte chunks; transposed outputs (Gram mirror, X'^T, or a
+// tall weight) are formed in registers with v_permlane16_swap. It applies the
+// fold 1/||U||_F of the first step (so the normalised X0 is never
+// materialised), the step coefficients, and on the last step the
+// decoupled-weight-decay update W <- W - lr*wd*W - lr*scale*O straight into
+// the parameter.
 #include "common.hpp"
 #include "launch.hpp"
 
