@@ -130,6 +130,29 @@ __device__ __forceinline__ void emit_u8(const GemmArgs& A, const NsProb& P, int 
     }
 }
 
+// The update of emit_u8's vector path with the 8 parameter values already in
+// registers (loaded ahead, see the last-apply epilogue); same arithmetic.
+__device__ __forceinline__ void update8_pre(const GemmArgs& A, const NsProb& P, int ur, int uc0, const float* v,
+                                            const bf16x4 (&q)[2]) {
+    const int64_t off = (int64_t)ur * P.ld + uc0;
+    const float decay = A.lr * A.wd, step = A.lr * P.scale;
+    if (P.oout) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) P.oout[off + e] = v[e];
+    }
+    bf16* dst = (bf16*)P.param + off;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        bf16x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float x = (float)q[h][e];
+            o[e] = (bf16)((x - decay * x) - step * v[4 * h + e]);
+        }
+        *gp((bf16x4*)(dst + 4 * h)) = o;
+    }
+}
+
 template <typename TX>
 __device__ __forceinline__ void load8(const TX* p, float* v) {
     if constexpr (sizeof(TX) == 2) {
@@ -190,11 +213,23 @@ __device__ __forceinline__ void wave_lds_sync() { asm volatile("" ::: "memory");
 // floats: lane -> row idx%16 and 8 consecutive columns, so with the K-blocked
 // layout a wave writes whole 1 KB blocks. Each wave stages only its own strip,
 // so syncs are wave-local.
+// A tall block's parameter update is the exception to going straight from
+// registers: there a 16-row strip is only 16 consecutive elements of each of
+// 128 parameter rows, and updating 32-byte pieces of rows 8 KB apart makes the
+// L2 fetch the same lines many times over. The bf16 kernel gives each wave a
+// second slot array (`st2`): four strips are collected there as an F*16 x 64
+// f32 block (first half of the rows in `st`, second half in `st2`; 16-byte
+// chunk q of row c stored at chunk q ^ (c % 16), which keeps both the column
+// writes and the row reads free of bank conflicts) and then written back as
+// one 128-byte run of bf16 per parameter row.
 // ---------------------------------------------------------------------------
 template <int MODE, typename TX, typename TS, int F>
 __device__ __forceinline__ void epilogue_mode(const GemmArgs& A, const NsProb& P, int ti, int tj, int TS_, int wm0,
-                                              int wn0, f32x4 (&acc)[F][F], float* st) {
+                                              int wn0, f32x4 (&acc)[F][F], float* st, float* st2) {
     static_assert(F % 2 == 0, "fragments are paired for the transposed stores");
+    // staged tall update: four 16-row strips per WT x 64 block, in two halves
+    // of WT/2 rows (one slot array each)
+    constexpr bool staged_tall = MODE == GM_APPLY_LAST && F % 4 == 0;
     constexpr int WT = F * 16;
     constexpr int SP = WT + 4;
     constexpr int PASSES = WT / 32;            // row pass: 16 rows x 32 columns per pass
@@ -209,6 +244,38 @@ __device__ __forceinline__ void epilogue_mode(const GemmArgs& A, const NsProb& P
     const bool trans_out = mirror || (!gram && !last) || (last && P.tall);
     const bool row_out = !(last && P.tall);
     const int row_base = ti * TS_ + wm0, col_base = tj * TS_ + wn0;
+
+    // Last apply with bf16 parameters: with one wave per SIMD nothing hides the
+    // latency of a read-modify-write, so when the wave's whole WT x WT block is
+    // in bounds its parameter values are all loaded up front (F*F/2 runs of 8
+    // per lane, in the order the writes below consume them) and only the
+    // stores remain in the strip loop.
+    constexpr bool pre_ok = last && sizeof(TS) == 2 && F % 4 == 0;
+    constexpr int NPRE = pre_ok ? F * F / 2 : 1;
+    bf16x4 pre[NPRE][2];
+    bool fast = false;
+    if constexpr (pre_ok) {
+        const int br = P.tall ? col_base : row_base;   // first parameter row of the block
+        const int bc = P.tall ? row_base : col_base;   // first parameter column
+        fast = A.with_update && P.vec && br + WT <= P.hr && bc + WT <= P.hc;
+        if (fast) {
+            const bf16* par = (const bf16*)P.param;
+            static_for<0, NPRE>([&](auto ic) {
+                constexpr int idx = decltype(ic)::value;
+                int ur, uc0;
+                if (P.tall) {   // staged block (idx / (WT/8)), row group idx % (WT/8)
+                    ur = br + (idx % (WT / 8)) * 8 + (lane >> 3);
+                    uc0 = bc + (idx / (WT / 8)) * 64 + 8 * (lane & 7);
+                } else {        // strip idx / PASSES, pass idx % PASSES
+                    ur = br + (idx / PASSES) * 16 + l16;
+                    uc0 = bc + (idx % PASSES) * 32 + g4 * 8;
+                }
+                const bf16* src = par + (int64_t)ur * P.ld + uc0;
+                pre[idx][0] = *gp((const bf16x4*)src);
+                pre[idx][1] = *gp((const bf16x4*)(src + 4));
+            });
+        }
+    }
     const int mp = P.mp, np = P.np;
     // Gram scale and diagonal term
     float gs = f * f, gd = 0.f;
@@ -257,8 +324,53 @@ __device__ __forceinline__ void epilogue_mode(const GemmArgs& A, const NsProb& P
                 } else {
 #pragma unroll
                     for (int e = 0; e < 8; ++e) v[e] = f * w[e];
-                    if constexpr (!last) store8<TX>(xtdst + op_off<TX>(c, r0, np, mp), v);
-                    else emit_u8<TS>(A, P, c, r0, v);
+                    if constexpr (!last) {
+                        store8<TX>(xtdst + op_off<TX>(c, r0, np, mp), v);
+                    } else if constexpr (staged_tall) {
+                        // block row cl = c - col_base, columns rl .. rl+7
+                        const int cl = (fp + (g4 & 1)) * 16 + l16;
+                        const int q = ((fm & 3) * 16 + 8 * (g4 >> 1)) >> 2;
+                        float* row = (fp < F / 2 ? st : st2) + (cl & (WT / 2 - 1)) * 64;
+                        *(f32x4*)(row + ((q ^ l16) << 2)) = f32x4{v[0], v[1], v[2], v[3]};
+                        *(f32x4*)(row + (((q + 1) ^ l16) << 2)) = f32x4{v[4], v[5], v[6], v[7]};
+                    } else {
+                        emit_u8<TS>(A, P, c, r0, v);
+                    }
+                }
+            }
+            if constexpr (staged_tall) {
+                if ((fm & 3) == 3) {
+                    // block complete: lane -> row it*8 + lane/8, columns 8*(lane%8) .. +7
+                    wave_lds_sync();
+                    const int j = lane & 7;
+                    auto block_row = [&](int it, float* v) {
+                        const int cl = it * 8 + (lane >> 3);
+                        const float* row = (it < WT / 16 ? st : st2) + (cl & (WT / 2 - 1)) * 64;
+                        const f32x4 lo = *(const f32x4*)(row + (((2 * j) ^ (cl & 15)) << 2));
+                        const f32x4 hi = *(const f32x4*)(row + (((2 * j + 1) ^ (cl & 15)) << 2));
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) { v[e] = lo[e]; v[4 + e] = hi[e]; }
+                    };
+                    const int uc0 = row_base + (fm >> 2) * 64 + 8 * j;
+                    if (fast) {
+                        if constexpr (pre_ok) {
+#pragma unroll
+                            for (int it = 0; it < WT / 8; ++it) {
+                                float v[8];
+                                block_row(it, v);
+                                update8_pre(A, P, col_base + it * 8 + (lane >> 3), uc0, v,
+                                            pre[(fm >> 2) * (WT / 8) + it]);
+                            }
+                        }
+                    } else {
+#pragma clang loop unroll(disable)
+                        for (int it = 0; it < WT / 8; ++it) {
+                            float v[8];
+                            block_row(it, v);
+                            emit_u8<TS>(A, P, col_base + it * 8 + (lane >> 3), uc0, v);
+                        }
+                    }
+                    wave_lds_sync();
                 }
             }
         }
@@ -299,8 +411,16 @@ __device__ __forceinline__ void epilogue_mode(const GemmArgs& A, const NsProb& P
             } else {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) v[e] *= f;
-                if constexpr (!last) store8<TX>(xdst + op_off<TX>(r, c, mp, np), v);
-                else emit_u8<TS>(A, P, r, c, v);
+                if constexpr (!last) {
+                    store8<TX>(xdst + op_off<TX>(r, c, mp, np), v);
+                } else {
+                    if constexpr (pre_ok) {
+                        if (fast) update8_pre(A, P, r, c, v, pre[fm * PASSES + pass]);
+                        else emit_u8<TS>(A, P, r, c, v);
+                    } else {
+                        emit_u8<TS>(A, P, r, c, v);
+                    }
+                }
             }
         }
     }
@@ -310,13 +430,13 @@ __device__ __forceinline__ void epilogue_mode(const GemmArgs& A, const NsProb& P
 // mode's code unrolled over the strips outgrows the instruction cache.
 template <bool SYM, typename TX, typename TS, int F>
 __device__ __forceinline__ void epilogue(const GemmArgs& A, const NsProb& P, int ti, int tj, int TS_, int wm0,
-                                         int wn0, f32x4 (&acc)[F][F], float* st) {
+                                         int wn0, f32x4 (&acc)[F][F], float* st, float* st2) {
     if constexpr (SYM) {
-        if (A.mode == GM_GRAM) epilogue_mode<GM_GRAM, TX, TS, F>(A, P, ti, tj, TS_, wm0, wn0, acc, st);
-        else epilogue_mode<GM_GRAM2, TX, TS, F>(A, P, ti, tj, TS_, wm0, wn0, acc, st);
+        if (A.mode == GM_GRAM) epilogue_mode<GM_GRAM, TX, TS, F>(A, P, ti, tj, TS_, wm0, wn0, acc, st, st2);
+        else epilogue_mode<GM_GRAM2, TX, TS, F>(A, P, ti, tj, TS_, wm0, wn0, acc, st, st2);
     } else {
-        if (A.mode == GM_APPLY) epilogue_mode<GM_APPLY, TX, TS, F>(A, P, ti, tj, TS_, wm0, wn0, acc, st);
-        else epilogue_mode<GM_APPLY_LAST, TX, TS, F>(A, P, ti, tj, TS_, wm0, wn0, acc, st);
+        if (A.mode == GM_APPLY) epilogue_mode<GM_APPLY, TX, TS, F>(A, P, ti, tj, TS_, wm0, wn0, acc, st, st2);
+        else epilogue_mode<GM_APPLY_LAST, TX, TS, F>(A, P, ti, tj, TS_, wm0, wn0, acc, st, st2);
     }
 }
 
@@ -537,9 +657,11 @@ __global__ __launch_bounds__(NTHR) void k_gemm_bf16(GemmArgs A) {
     __builtin_amdgcn_sched_barrier(0);
     MU_WAIT_VMCNT(0);
     __syncthreads();
-    // epilogue staging: one strip per wave, each in its own slot array
+    // epilogue staging: two slot arrays per wave
+    static_assert(LS * sizeof(bf16) == (WT / 2) * 64 * sizeof(float), "a staging half is WT/2 x 64 floats");
     float* st = (float*)(wave == 0 ? sA0 : wave == 1 ? sA1 : wave == 2 ? sA2 : sA3);
-    epilogue<SYM, bf16, TSRC, F>(A, P, ti, tj, TS, wm0, wn0, acc, st);
+    float* st2 = (float*)(wave == 0 ? sB0 : wave == 1 ? sB1 : wave == 2 ? sB2 : sB3);
+    epilogue<SYM, bf16, TSRC, F>(A, P, ti, tj, TS, wm0, wn0, acc, st, st2);
 }
 
 // ---------------------------------------------------------------------------
@@ -640,7 +762,7 @@ __global__ __launch_bounds__(NTHR) void k_gemm_f32(GemmArgs A) {
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
-    epilogue<SYM, float, TSRC, F>(A, P, ti, tj, TS, wm0, wn0, acc, smem + wave * 16 * (WT + 4));
+    epilogue<SYM, float, TSRC, F>(A, P, ti, tj, TS, wm0, wn0, acc, smem + wave * 16 * (WT + 4), nullptr);
 }
 
 template <int TS, bool SYM>

@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_util import need_gpu, to_np
+from gpu_util import bf16_ulp, need_gpu, to_np
 from oracle import muon_oracle as O
 from workloads import PARAM_SETS, device_normal, seed_for
 
@@ -60,8 +60,13 @@ def test_full_set_muon_step(set_name):
         e = ps.muon[j]
         print(f"  oracle for {e.name} {e.shape} heads={e.heads}", flush=True)
         ref = O.muon_step_ref(w0, g0, m0, lr=0.02, weight_decay=0.01, heads=e.heads)
-        assert O.rel_fro(to_np(oo[j]), ref["o"]) <= BF16_TOL, e.name
+        o = to_np(oo[j])
+        assert O.rel_fro(o, ref["o"]) <= BF16_TOL, e.name
         assert O.rel_fro(to_np(ms[j]), ref["m"]) <= MOM_TOL, e.name
+        # the update: W1 is the bf16 rounding of W0 - lr wd W0 - lr O, with the GPU's O
+        want = w0 - 0.02 * 0.01 * w0 - 0.02 * o
+        tol = bf16_ulp(want) * 0.5 + 8 * 2.0 ** -24 * (np.abs(w0) + 0.02 * np.abs(o))
+        assert np.all(np.abs(to_np(ws[j]) - want) <= tol), e.name
     # every matrix moved and stayed finite
     for j, w in enumerate(ws):
         assert torch.isfinite(w).all(), ps.muon[j].name

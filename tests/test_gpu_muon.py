@@ -99,6 +99,13 @@ def test_bf16_step(shape):
     # the update arithmetic: W1 is the bf16 rounding of W0 - lr wd W0 - lr O (with the GPU's O)
     want = w0 - 0.02 * 0.01 * w0 - 0.02 * o
     assert np.all(np.abs(w1 - want) <= bf16_ulp(want) * 0.5 + 8 * 2.0 ** -24 * (np.abs(w0) + 0.02 * np.abs(o)))
+    # without the O copy (the usual call) the parameter comes out bit for bit the same
+    w, g, m = make_matrix_inputs(shape, 8000, torch.bfloat16, 1e-3, 0.02, 1e-3)
+    nso().muon_step([w], [g], [m], lr=0.02, weight_decay=0.01, mu=0.95, nesterov=True, heads=[1], scales=[1.0],
+                    precision="bf16")
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(w), w1)
+    assert np.array_equal(to_np(m), m1)
 
 
 @pytest.mark.parametrize("shape,heads", [((512, 256), 4), ((256, 64), 8), ((1024, 128), 2), ((4096, 4096), 32)])
