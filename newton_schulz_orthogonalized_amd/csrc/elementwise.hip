@@ -400,8 +400,8 @@ __device__ __forceinline__ void adamw1(float& p, float g, float& m, float& v, co
 }
 
 // Whole chunk of a bf16 tensor whose buffers allow 16-byte accesses: each
-// thread owns two runs of 8 elements; every load of both is issued before any
-// arithmetic.
+// thread owns ADAMW_CHUNK / (256 * 8) runs of 8 elements; every load of all of
+// them is issued before any arithmetic.
 __device__ __forceinline__ void adamw_chunk_bf16(const AdamWDesc& D, int64_t base, const AdamWArgs& A) {
     constexpr int RUNS = ADAMW_CHUNK / (NTHR * 8);
     bf16x8 pq[RUNS], gq[RUNS];

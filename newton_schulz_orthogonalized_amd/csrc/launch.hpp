@@ -38,9 +38,9 @@ struct NormArgs {
 hipError_t launch_norm(const NormArgs& a, hipStream_t s);
 
 enum GemmMode : int {
-    GM_GRAM = 0,        // A = f^2 * X X^T          (upper tiles, mirrored store)
-    GM_GRAM2 = 1,       // B = b*A + c*A A^T        (upper tiles, mirrored store)
-    GM_APPLY = 2,       // X' = f*(a*X + b*A X)  or  f*(a*X + B X)
+    GM_GRAM = 0,        // a I + b f^2 X X^T, or A = f^2 X X^T when a quintic step follows  (upper tiles, mirrored)
+    GM_GRAM2 = 1,       // B = a I + b A + c A A^T                                             (upper tiles, mirrored)
+    GM_APPLY = 2,       // X' = f (B X), B the matrix the Gram pass(es) left
     GM_APPLY_LAST = 3,  // as GM_APPLY, result O goes to the update or to `out`
 };
 
@@ -92,7 +92,7 @@ struct AdamWArgs {
     float beta1, beta2, eps;
     float bc1, bc2;         // 1 - beta^t
 };
-constexpr int ADAMW_CHUNK = 4096;  // elements per workgroup
+constexpr int ADAMW_CHUNK = 8192;  // elements per workgroup
 hipError_t launch_adamw(const AdamWArgs& a, hipStream_t s);
 
 // QK-Clip: one segment per (layer, query or key matrix, head) row block.

@@ -42,7 +42,19 @@ namespace {
 
 constexpr int NTHR = 256;
 
+template <int N>
+struct Stage {
+    static constexpr int value = N;
+};
 
+// fn(Stage<i>{}) for i = B .. E-1, every index a compile-time constant
+template <int B, int E, typename Fn>
+__device__ __forceinline__ void static_for(Fn&& fn) {
+    if constexpr (B < E) {
+        fn(Stage<B>{});
+        static_for<B + 1, E>(fn);
+    }
+}
 
 // ---------------------------------------------------------------------------
 // Tile enumeration
@@ -468,20 +480,6 @@ __device__ __forceinline__ void epilogue(const GemmArgs& A, const NsProb& P, int
 
 // Word 3 of a raw buffer resource: 32-bit data format, no swizzle, no stride.
 constexpr int BUF_RAW32 = 0x00020000;
-
-template <int N>
-struct Stage {
-    static constexpr int value = N;
-};
-
-// fn(Stage<i>{}) for i = B .. E-1, every index a compile-time constant
-template <int B, int E, typename Fn>
-__device__ __forceinline__ void static_for(Fn&& fn) {
-    if constexpr (B < E) {
-        fn(Stage<B>{});
-        static_for<B + 1, E>(fn);
-    }
-}
 
 // s_waitcnt with only vmcnt (gfx9 encoding: vmcnt[3:0] bits 3:0, [5:4] bits 15:14)
 #define MU_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14))
