@@ -473,7 +473,7 @@ int run_pipeline(Plan& pl, char* ws, const mu_muon_hparams* hp, int src_dt, bool
                 g2.mode = GM_GRAM2;
                 g2.prefix = gram_pf[gi];
                 g2.total_tiles = g.gram_prefix.back();
-                g2.first = 0;
+                g2.first = first ? 1 : 0;
                 rc = timed_launch(MU_K_GRAM2, g2flops, 0.0, s, [&] { return launch(g2); }, "gram2 launch");
                 if (rc) return rc;
             }

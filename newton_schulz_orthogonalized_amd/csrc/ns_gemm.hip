@@ -28,11 +28,11 @@
 //
 // Epilogue: row-major outputs are staged per wave through LDS in 16-row strips
 // and stored as 16-byte chunks; transposed outputs (Gram mirror, X'^T, or a
-// tall weight) are formed in registers with v_permlane16_swap. It applies the
-// fold 1/||U||_F of the first step (so the normalised X0 is never
-// materialised), the step coefficients, and on the last step the
-// decoupled-weight-decay update W <- W - lr*wd*W - lr*scale*O straight into
-// the parameter.
+// tall weight) are formed in registers with v_permlane16_swap. The Gram
+// epilogue applies the step coefficients and, on the first step, the fold
+// f = 1/||U||_F (so the normalised X0 is never materialised); the last apply
+// writes the decoupled-weight-decay update W <- W - lr*wd*W - lr*scale*O
+// straight into the parameter.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -209,13 +209,15 @@ __device__ __forceinline__ void wave_lds_sync() { asm volatile("" ::: "memory");
 // 16x16 MFMA one: lane l holds C[4*(l>>4) + e][l & 15] of each fragment.
 //
 // What each mode stores (f = 1/(||U||_F + eps) on the first step, else 1):
-//   Gram, cubic step     B = a I + b f^2 (X X^T)      -> P.a (mirrored)
-//   Gram, quintic step   A = f^2 (X X^T)              -> P.a (mirrored)
-//   A^2 pass             B = a I + b A + c A A^T      -> P.b (mirrored)
-//   apply                X' = f (B X)                 -> X', X'^T
-//   last apply           O = f (B X) -> parameter update (or output)
-// Folding a I into B keeps X itself out of the apply epilogue; padding stays
-// zero because a padded row of X' is a*0 + (rows of A that are zero).
+//   Gram, cubic step     B = f (a I + b f^2 X X^T)    -> P.a (mirrored)
+//   Gram, quintic step   A = f^2 X X^T                -> P.a (mirrored)
+//   A^2 pass             B = f (a I + b A + c A A^T)  -> P.b (mirrored)
+//   apply                X' = B X                     -> X', X'^T
+//   last apply           O = B X -> parameter update (or output)
+// On the first step X holds U itself, and f (a X0 + b (X0 X0^T) X0) with
+// X0 = f U is exactly B U for these B. Folding a I and f into B keeps X and
+// any scaling out of the apply epilogue; padding stays zero because a padded
+// row of X' is f*a*0 + (rows of A that are zero).
 //
 // Transposed outputs (Gram mirror, X'^T, a tall block's parameter) come
 // straight from registers: v_permlane16_swap on the accumulators of two
@@ -248,8 +250,8 @@ __device__ __forceinline__ void epilogue_mode(const GemmArgs& A, const NsProb& P
     const int lane = threadIdx.x & 63;
     const int g4 = lane >> 4, l16 = lane & 15;
     constexpr int mode = MODE;
-    const float f = A.first ? P.fold[0] : 1.f;
     constexpr bool gram = mode == GM_GRAM || mode == GM_GRAM2;
+    const float f = gram && A.first ? P.fold[0] : 1.f;   // the apply takes it through B
     const bool diag = gram && ti == tj;
     const bool mirror = gram && ti != tj;
     constexpr bool last = mode == GM_APPLY_LAST;
@@ -290,9 +292,10 @@ __device__ __forceinline__ void epilogue_mode(const GemmArgs& A, const NsProb& P
     }
     const int mp = P.mp, np = P.np;
     // Gram scale and diagonal term
-    float gs = f * f, gd = 0.f;
-    if (mode == GM_GRAM && !A.use_b) { gs = A.cb * f * f; gd = A.ca; }
-    if (mode == GM_GRAM2) { gs = A.cc; gd = A.ca; }
+    // Gram scale gs, diagonal term gd, and (A^2 pass) the factor on A
+    float gs = f * f, gd = 0.f, ga = A.cb;
+    if (mode == GM_GRAM && !A.use_b) { gs = A.cb * f * f * f; gd = A.ca * f; }
+    if (mode == GM_GRAM2) { gs = A.cc * f; gd = A.ca * f; ga = A.cb * f; }
     TX* gdst = (TX*)(mode == GM_GRAM2 ? P.b : P.a);
     TX* xdst = (TX*)(A.src ? P.x[0] : P.x[1]);
     TX* xtdst = (TX*)(A.src ? P.xt[0] : P.xt[1]);
@@ -327,7 +330,7 @@ __device__ __forceinline__ void epilogue_mode(const GemmArgs& A, const NsProb& P
                         float a8[8];   // A[r0+e][c] = A[c][r0+e]
                         load8<TX>((const TX*)P.a + op_off<TX>(c, r0, mp, mp), a8);
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) v[e] = A.cb * a8[e] + gs * w[e];
+                        for (int e = 0; e < 8; ++e) v[e] = ga * a8[e] + gs * w[e];
                     } else {
 #pragma unroll
                         for (int e = 0; e < 8; ++e) v[e] = gs * w[e];
@@ -335,7 +338,7 @@ __device__ __forceinline__ void epilogue_mode(const GemmArgs& A, const NsProb& P
                     store8<TX>(gdst + op_off<TX>(c, r0, mp, mp), v);
                 } else {
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) v[e] = f * w[e];
+                    for (int e = 0; e < 8; ++e) v[e] = w[e];
                     if constexpr (!last) {
                         store8<TX>(xtdst + op_off<TX>(c, r0, np, mp), v);
                     } else if constexpr (staged_tall) {
@@ -409,7 +412,7 @@ __device__ __forceinline__ void epilogue_mode(const GemmArgs& A, const NsProb& P
                     float a8[8];
                     load8<TX>((const TX*)P.a + op_off<TX>(r, c, mp, mp), a8);
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) v[e] = A.cb * a8[e] + gs * v[e];
+                    for (int e = 0; e < 8; ++e) v[e] = ga * a8[e] + gs * v[e];
                 } else {
 #pragma unroll
                     for (int e = 0; e < 8; ++e) v[e] *= gs;
@@ -421,8 +424,6 @@ __device__ __forceinline__ void epilogue_mode(const GemmArgs& A, const NsProb& P
                 }
                 store8<TX>(gdst + op_off<TX>(r, c, mp, mp), v);
             } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) v[e] *= f;
                 if constexpr (!last) {
                     store8<TX>(xdst + op_off<TX>(r, c, mp, np), v);
                 } else {
