@@ -299,6 +299,31 @@ __device__ __forceinline__ void epilogue_mode(const GemmArgs& A, const NsProb& P
     TX* gdst = (TX*)(mode == GM_GRAM2 ? P.b : P.a);
     TX* xdst = (TX*)(A.src ? P.x[0] : P.x[1]);
     TX* xtdst = (TX*)(A.src ? P.xt[0] : P.xt[1]);
+    // Where this lane's run of 8 goes in a workspace operand with R rows and
+    // K columns (element (row, k)). The bf16 operands are K-blocked: the 1 KB
+    // block of a store is wave-uniform (row_base, col_base are multiples of
+    // 64) and the place inside it a per-lane constant, so the address is a
+    // scalar base plus a 32-bit lane offset. fp32 operands are row-major.
+    //   transposed run: column c of C as operand row, C rows r0 .. r0+7 as k
+    //   row run:        C row r, columns c .. c+7 as k
+    const uint32_t lane_t = (uint32_t)(((g4 & 1) * 512 + (g4 >> 1) * 128 + l16 * 8) * sizeof(TX));
+    const uint32_t lane_r = (uint32_t)((g4 * 128 + l16 * 8) * sizeof(TX));
+    auto tdst = [&](TX* base, int R, int K, int c, int r0, int fm, int fp) -> TX* {
+        if constexpr (sizeof(TX) == 2) {
+            const int64_t blk = (int64_t)(row_base / 32 + (fm >> 1)) * (R >> 4) + col_base / 16 + fp;
+            return (TX*)((char*)(base + blk * 512 + (fm & 1) * 256) + lane_t);
+        } else {
+            return base + op_off<TX>(c, r0, R, K);
+        }
+    };
+    auto rdst = [&](TX* base, int R, int K, int r, int c, int fm, int pass) -> TX* {
+        if constexpr (sizeof(TX) == 2) {
+            const int64_t blk = (int64_t)(col_base / 32 + pass) * (R >> 4) + row_base / 16 + fm;
+            return (TX*)((char*)(base + blk * 512) + lane_r);
+        } else {
+            return base + op_off<TX>(r, c, R, K);
+        }
+    };
 
 #pragma clang loop unroll(full)
     for (int fm = 0; fm < F; ++fm) {
@@ -309,6 +334,15 @@ __device__ __forceinline__ void epilogue_mode(const GemmArgs& A, const NsProb& P
         for (int fn = 0; fn < F; ++fn)
 #pragma unroll
             for (int e = 0; e < 4; ++e) av[fn][e] = agpr_read(acc[fm][fn][e]);
+        // the row-major copy is staged first: the swaps below then consume
+        // the accumulator values in place instead of copying them
+        if (row_out) {
+            wave_lds_sync();
+#pragma unroll
+            for (int fn = 0; fn < F; ++fn)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) st[(4 * g4 + e) * SP + fn * 16 + l16] = av[fn][e];
+        }
         if (trans_out) {
 #pragma unroll
             for (int fp = 0; fp < F; fp += 2) {
@@ -328,19 +362,19 @@ __device__ __forceinline__ void epilogue_mode(const GemmArgs& A, const NsProb& P
                 if constexpr (gram) {
                     if constexpr (mode == GM_GRAM2) {
                         float a8[8];   // A[r0+e][c] = A[c][r0+e]
-                        load8<TX>((const TX*)P.a + op_off<TX>(c, r0, mp, mp), a8);
+                        load8<TX>(tdst((TX*)P.a, mp, mp, c, r0, fm, fp), a8);
 #pragma unroll
                         for (int e = 0; e < 8; ++e) v[e] = ga * a8[e] + gs * w[e];
                     } else {
 #pragma unroll
                         for (int e = 0; e < 8; ++e) v[e] = gs * w[e];
                     }
-                    store8<TX>(gdst + op_off<TX>(c, r0, mp, mp), v);
+                    store8<TX>(tdst(gdst, mp, mp, c, r0, fm, fp), v);
                 } else {
 #pragma unroll
                     for (int e = 0; e < 8; ++e) v[e] = w[e];
                     if constexpr (!last) {
-                        store8<TX>(xtdst + op_off<TX>(c, r0, np, mp), v);
+                        store8<TX>(tdst(xtdst, np, mp, c, r0, fm, fp), v);
                     } else if constexpr (staged_tall) {
                         // block row cl = c - col_base, columns rl .. rl+7
                         const int cl = (fp + (g4 & 1)) * 16 + l16;
@@ -392,11 +426,6 @@ __device__ __forceinline__ void epilogue_mode(const GemmArgs& A, const NsProb& P
         if (!row_out) continue;
         wave_lds_sync();
 #pragma unroll
-        for (int fn = 0; fn < F; ++fn)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) st[(4 * g4 + e) * SP + fn * 16 + l16] = av[fn][e];
-        wave_lds_sync();
-#pragma unroll
         for (int pass = 0; pass < PASSES; ++pass) {
             const int rr = l16, c8 = pass * 32 + g4 * 8;
             float v[8];
@@ -410,7 +439,7 @@ __device__ __forceinline__ void epilogue_mode(const GemmArgs& A, const NsProb& P
             if constexpr (gram) {
                 if constexpr (mode == GM_GRAM2) {
                     float a8[8];
-                    load8<TX>((const TX*)P.a + op_off<TX>(r, c, mp, mp), a8);
+                    load8<TX>(rdst((TX*)P.a, mp, mp, r, c, fm, pass), a8);
 #pragma unroll
                     for (int e = 0; e < 8; ++e) v[e] = ga * a8[e] + gs * v[e];
                 } else {
@@ -422,10 +451,10 @@ __device__ __forceinline__ void epilogue_mode(const GemmArgs& A, const NsProb& P
                     for (int e = 0; e < 8; ++e)
                         if (r == c + e) v[e] += gd;
                 }
-                store8<TX>(gdst + op_off<TX>(r, c, mp, mp), v);
+                store8<TX>(rdst(gdst, mp, mp, r, c, fm, pass), v);
             } else {
                 if constexpr (!last) {
-                    store8<TX>(xdst + op_off<TX>(r, c, mp, np), v);
+                    store8<TX>(rdst(xdst, mp, np, r, c, fm, pass), v);
                 } else {
                     if constexpr (pre_ok) {
                         if (fast) update8_pre(A, P, r, c, v, pre[fm * PASSES + pass]);
