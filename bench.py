@@ -284,8 +284,9 @@ def main():
 
     ms_step = 1e3 * elapsed / max(1, args.steps)
     K = max(1, args.steps)
-    ns_ms = (prof["gram"]["ms"] + prof["gram2"]["ms"] + prof["apply"]["ms"]) / K
-    ns_flops = (prof["gram"]["flops"] + prof["gram2"]["flops"] + prof["apply"]["flops"]) / K
+    ns_kinds = ("gram", "gram2", "apply", "ns_fused")
+    ns_ms = sum(prof[k]["ms"] for k in ns_kinds) / K
+    ns_flops = sum(prof[k]["flops"] for k in ns_kinds) / K
     peak = PEAK_BF16_TFLOPS if precision == "bf16" else PEAK_F32_TFLOPS
     ns_tflops = ns_flops / (ns_ms * 1e-3) / 1e12 if ns_ms > 0 else 0.0
     adamw_gbs = prof["adamw"]["bytes"] / (prof["adamw"]["ms"] * 1e-3) / 1e9 if prof["adamw"]["ms"] > 0 else None
@@ -293,7 +294,7 @@ def main():
     kernels = {k: {"ms_per_launch": (v["ms"] / v["launches"]) if v["launches"] else None,
                    "launches_per_step": v["launches"] / K, "ms_per_step": v["ms"] / K} for k, v in prof.items()}
     # dominant kernel: the class with the most time
-    dom = max(("gram", "apply", "gram2", "prep", "adamw"), key=lambda k: prof[k]["ms"])
+    dom = max(("gram", "apply", "gram2", "ns_fused", "prep", "adamw"), key=lambda k: prof[k]["ms"])
     d = prof[dom]
     if dom in ("gram", "apply", "gram2"):
         achieved = d["flops"] / (d["ms"] * 1e-3) / 1e12
@@ -314,7 +315,7 @@ def main():
                                f"AdamW over {len(ps.adamw)} tensors ({ps.adamw_elems()} elements)",
                    "muon_matrices": len(ps.muon), "adamw_tensors": len(ps.adamw),
                    "ns_steps": args.ns_steps, "ns_precision": precision, "parallelism": "single-gpu"},
-        "muon_ms_per_step": sum(prof[k]["ms"] for k in ("prep", "norm", "gram", "gram2", "apply", "finish")) / K,
+        "muon_ms_per_step": sum(prof[k]["ms"] for k in ("prep", "norm", "gram", "gram2", "apply", "finish", "ns_fused")) / K,
         "adamw_ms_per_step": prof["adamw"]["ms"] / K,
         "ns_ms_per_step": ns_ms, "ns_tflops": ns_tflops, "ns_frac_peak": ns_tflops / peak,
         "adamw_gbs": adamw_gbs, "adamw_frac_hbm": (adamw_gbs / PEAK_HBM_GBS) if adamw_gbs else None,

@@ -243,7 +243,8 @@ int mu_version(void);
 #define MU_K_FINISH 5    /* update when ns_steps == 0 */
 #define MU_K_ADAMW 6     /* AdamW */
 #define MU_K_QKCLIP 7    /* QK-Clip rescale (bytes assume every head clipped) */
-#define MU_K_COUNT 8
+#define MU_K_FUSED 8     /* every step but the last apply of mp == 128 problems (>= 256 in a call) */
+#define MU_K_COUNT 9
 int mu_profile_enable(int on);
 int mu_profile_read(int kernel, double* total_ms, int64_t* launches, double* flops, double* bytes);
 const char* mu_kernel_name(int kernel);

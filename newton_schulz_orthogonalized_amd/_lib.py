@@ -30,8 +30,8 @@ MU_ERR_LAYOUT = 3
 MU_ERR_WORKSPACE = 4
 MU_ERR_HIP = 5
 
-MU_K_PREP, MU_K_NORM, MU_K_GRAM, MU_K_GRAM2, MU_K_APPLY, MU_K_FINISH, MU_K_ADAMW, MU_K_QKCLIP = range(8)
-MU_K_COUNT = 8
+MU_K_PREP, MU_K_NORM, MU_K_GRAM, MU_K_GRAM2, MU_K_APPLY, MU_K_FINISH, MU_K_ADAMW, MU_K_QKCLIP, MU_K_FUSED = range(9)
+MU_K_COUNT = 9
 
 EXPORTED = (
     "mu_muon_workspace_size", "mu_muon_step", "mu_ortho_workspace_size", "mu_muon_orthogonalize",

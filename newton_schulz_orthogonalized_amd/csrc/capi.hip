@@ -113,8 +113,16 @@ struct ProbPlan {
 struct Group {
     int tile;
     int first, count;  // range in the problem array
+    bool fused;        // mp == 128 problems run by k_ns_small up to the last apply
     std::vector<int> gram_prefix, apply_prefix;
 };
+
+// Problems with mp == 128 go through the fused kernel (one workgroup per
+// problem, every step but the last in one launch) when a call has at least
+// this many of them; with fewer, the tiled path spreads each problem over more
+// workgroups and wins. A fixed count, so that the workspace query and the call
+// always plan alike.
+constexpr int FUSED_MIN_PROBS = 256;
 
 struct Plan {
     std::vector<ProbPlan> probs;
@@ -190,15 +198,24 @@ void build_plan(const std::vector<Item>& items, int ns_dt, const std::vector<Coe
             all.push_back(pp);
         }
     }
-    // stable order: tile 256 first, then 128, then 64
+    // stable order: tile 256 first, then 128 (fused problems last), then 64
+    const bool fuse_ok = ns_dt == DT_BF16 && !pl.quintic && !co.empty() && co.size() <= (size_t)SMALL_MAX_STEPS;
+    int n_fused = 0;
+    for (auto& pp : all)
+        if (fuse_ok && pp.tile == 128 && pp.d.mp == 128) ++n_fused;
+    const bool fuse = n_fused >= FUSED_MIN_PROBS;
+    auto is_fused = [&](const ProbPlan& pp) { return fuse && pp.tile == 128 && pp.d.mp == 128; };
     pl.probs.clear();
     pl.groups.clear();
-    for (int t : {256, 128, 64}) {
+    for (int gi = 0; gi < 4; ++gi) {
+        const int t = gi == 0 ? 256 : gi == 3 ? 64 : 128;
+        const bool fused = gi == 2;
         Group g;
         g.tile = t;
+        g.fused = fused;
         g.first = (int)pl.probs.size();
         for (auto& pp : all)
-            if (pp.tile == t) pl.probs.push_back(pp);
+            if (pp.tile == t && is_fused(pp) == fused) pl.probs.push_back(pp);
         g.count = (int)pl.probs.size() - g.first;
         if (g.count == 0) continue;
         g.gram_prefix.assign(1, 0);
@@ -431,12 +448,34 @@ int run_pipeline(Plan& pl, char* ws, const mu_muon_hparams* hp, int src_dt, bool
             o += sizeof(int) * g.apply_prefix.size();
         }
     }
+    // fused problems: every step but the last apply in one launch
+    for (const Group& g : pl.groups) {
+        if (!g.fused) continue;
+        SmallArgs sa{};
+        sa.probs = dprobs + g.first;
+        sa.nprobs = g.count;
+        sa.ns_steps = hp->ns_steps;
+        for (int k = 0; k < hp->ns_steps; ++k) {
+            sa.ca[k] = co[k].a;
+            sa.cb[k] = co[k].b;
+        }
+        double fl = 0, by = 0;
+        for (int i = g.first; i < g.first + g.count; ++i) {
+            const double m = pl.probs[i].d.m, n = pl.probs[i].d.n;
+            const double xb = (double)pl.probs[i].d.mp * pl.probs[i].d.np * ns_es;
+            fl += m * (m + 1) * n + (hp->ns_steps - 1) * (2 * m * m * n + 3 * m * n + m * (m + 1) * n);
+            by += xb * (1 + 2 * (hp->ns_steps - 1));   // X0 once, then X^T in and X'^T out per step
+        }
+        rc = timed_launch(MU_K_FUSED, fl, by, s, [&] { return launch_ns_small(sa, s); }, "fused launch");
+        if (rc) return rc;
+    }
     int src = 0;
     for (int k = 0; k < hp->ns_steps; ++k) {
         const bool first = k == 0, last = k + 1 == hp->ns_steps;
         const bool quint = co[k].c != 0.f;
         for (size_t gi = 0; gi < pl.groups.size(); ++gi) {
             const Group& g = pl.groups[gi];
+            if (g.fused && !last) continue;   // done by the fused launch
             double gflops = 0, g2flops = 0, aflops = 0, abytes = 0;
             for (int i = g.first; i < g.first + g.count; ++i) {
                 const double m = pl.probs[i].d.m, n = pl.probs[i].d.n;
@@ -460,7 +499,16 @@ int run_pipeline(Plan& pl, char* ws, const mu_muon_hparams* hp, int src_dt, bool
             auto launch = [&](const GemmArgs& a) {
                 return ns_dt == DT_BF16 ? launch_gemm_bf16(a, g.tile, s) : launch_gemm_f32(a, s);
             };
-            // Gram
+            // Gram (the fused launch left a fused group's last B in `a`)
+            if (g.fused) {
+                GemmArgs ap = ga;
+                ap.mode = GM_APPLY_LAST;
+                ap.prefix = apply_pf[gi];
+                ap.total_tiles = g.apply_prefix.back();
+                rc = timed_launch(MU_K_APPLY, aflops, abytes, s, [&] { return launch(ap); }, "apply launch");
+                if (rc) return rc;
+                continue;
+            }
             GemmArgs gg = ga;
             gg.mode = GM_GRAM;
             gg.prefix = gram_pf[gi];
@@ -883,6 +931,7 @@ const char* mu_kernel_name(int k) {
         case MU_K_FINISH: return "finish";
         case MU_K_ADAMW: return "adamw";
         case MU_K_QKCLIP: return "qk_clip";
+        case MU_K_FUSED: return "ns_fused";
         default: return "unknown";
     }
 }

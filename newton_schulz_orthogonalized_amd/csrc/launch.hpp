@@ -38,9 +38,9 @@ struct NormArgs {
 hipError_t launch_norm(const NormArgs& a, hipStream_t s);
 
 enum GemmMode : int {
-    GM_GRAM = 0,        // a I + b f^2 X X^T, or A = f^2 X X^T when a quintic step follows  (upper tiles, mirrored)
-    GM_GRAM2 = 1,       // B = a I + b A + c A A^T                                             (upper tiles, mirrored)
-    GM_APPLY = 2,       // X' = f (B X), B the matrix the Gram pass(es) left
+    GM_GRAM = 0,        // B = f (a I + b f^2 X X^T), or A = f^2 X X^T when a quintic step follows  (upper, mirrored)
+    GM_GRAM2 = 1,       // B = f (a I + b A + c A A^T)                                               (upper, mirrored)
+    GM_APPLY = 2,       // X' = B X, B the matrix the Gram pass(es) left (f = 1/||U|| on the first step, else 1)
     GM_APPLY_LAST = 3,  // as GM_APPLY, result O goes to the update or to `out`
 };
 
@@ -61,6 +61,20 @@ struct GemmArgs {
 // tile: 256 or 128 (square tiles, bf16) ; float32 uses 64.
 hipError_t launch_gemm_bf16(const GemmArgs& a, int tile, hipStream_t s);
 hipError_t launch_gemm_f32(const GemmArgs& a, hipStream_t s);
+
+// Newton-Schulz for problems with mp == 128 (bf16, cubic steps) up to the last
+// apply, in one launch, one workgroup per problem. X0 is in x[0] and X0^T in
+// xt[0]; the steps ping-pong between xt[0] and xt[1], so X of the last step is
+// in xt[(ns_steps - 1) & 1], and that step's B is left in `a` for the tiled
+// last apply (GM_APPLY_LAST), which writes the update.
+constexpr int SMALL_MAX_STEPS = 16;
+struct SmallArgs {
+    const NsProb* probs;
+    int nprobs;
+    int ns_steps;          // 1 .. SMALL_MAX_STEPS
+    float ca[SMALL_MAX_STEPS], cb[SMALL_MAX_STEPS];
+};
+hipError_t launch_ns_small(const SmallArgs& a, hipStream_t s);
 
 struct FinishArgs {      // ns_steps == 0: O = fold * X0
     const NsProb* probs;

@@ -793,6 +793,230 @@ __global__ __launch_bounds__(NTHR) void k_gemm_f32(GemmArgs A) {
     epilogue<SYM, float, TSRC, F>(A, P, ti, tj, TS, wm0, wn0, acc, smem + wave * 16 * (WT + 4), nullptr);
 }
 
+// ---------------------------------------------------------------------------
+// Newton-Schulz for one problem with mp == 128 (a 128-row head block, or any
+// matrix whose short side is at most 128) in one workgroup, up to the last
+// apply. Such short, wide problems are bound by HBM, and the tiled path moves X
+// through it three times per step (the Gram reads X, the apply reads X^T and
+// writes X' and X'^T). Here B (128 x 128) stays in LDS and each step streams
+// X^T once, in blocks of 128 columns of X:
+//   X'_j = B X_j            (B and X^T_j from LDS)
+//   X'^T_j -> HBM           (the next step's input)
+//   A' += X'_j X'_j^T       (from a K-blocked LDS copy of X'_j, bf16 as stored)
+// and the next step's B = a' I + b' A' is written into LDS from the symmetric
+// A'. The first B = f (a I + b f^2 X0 X0^T) comes from one pass over X0. The
+// B of the last step is copied to the problem's `a` buffer, and the tiled last
+// apply (which fuses the parameter update) finishes the run.
+// X blocks are double-buffered with direct-to-LDS loads. The wait at a block
+// boundary covers the previous block's stores too: loads and stores share
+// vmcnt, which does not order one against the other.
+// 4 waves in 2 x 2, each 64 x 64 of X'_j (64 AGPRs) and of A' (64 AGPRs).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(NTHR) void k_ns_small(SmallArgs A) {
+    constexpr int M = 128, BK = 32, WT = 64, F = 4, SP = WT + 4;
+    constexpr int SLICE = M * BK;   // a 32-wide k-slice of a 128-row K-blocked operand (8 KB)
+    constexpr int OPB = 4 * SLICE;  // a 128 x 128 operand (32 KB)
+    constexpr int PASSES = WT / 32;
+    __shared__ __attribute__((aligned(1024))) bf16 sB[OPB];   // B, left operand of the apply
+    __shared__ __attribute__((aligned(1024))) bf16 sX0[OPB];  // X^T (or X0) blocks, even j
+    __shared__ __attribute__((aligned(1024))) bf16 sX1[OPB];  // odd j
+    __shared__ __attribute__((aligned(1024))) bf16 sG[OPB];   // X'_j, both operands of the Gram
+    __shared__ __attribute__((aligned(16))) float sT[4 * 16 * SP];
+    __shared__ float sCo[2 * SMALL_MAX_STEPS];   // a_k, b_k: indexed by the step at run time
+
+    if ((int)blockIdx.x >= A.nprobs) return;
+    const NsProb P = A.probs[blockIdx.x];   // by value: held in registers
+    const int np = P.np, NB = np / M;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm0 = (wave >> 1) * WT, wn0 = (wave & 1) * WT;
+    const int g4 = lane >> 4, l16 = lane & 15;
+    float* st = sT + wave * 16 * SP;
+    if (tid == 0) {
+#pragma unroll
+        for (int i = 0; i < SMALL_MAX_STEPS; ++i) {
+            sCo[i] = A.ca[i];
+            sCo[SMALL_MAX_STEPS + i] = A.cb[i];
+        }
+    }
+
+    // 32 KB operand block -> LDS buffer: k-slice s (8 KB) is the run starting
+    // at element run0 + s * stride of base; wave w moves 1 KB blocks w, w+4, ..
+    const uint32_t lane_off = (uint32_t)lane * 16u;
+    auto dma_block = [&](bf16* dst, const bf16* base, int64_t run0, int64_t stride) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int b = i * 4 + wave;
+            const int sl = b >> 3, g = b & 7;
+            const __amdgpu_buffer_rsrc_t rs =
+                __builtin_amdgcn_make_buffer_rsrc((void*)(base + run0 + sl * stride), 0, SLICE * 2, BUF_RAW32);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDSP void*)(dst + sl * SLICE + g * 512), 16, lane_off,
+                                                     (uint32_t)g * 1024u, 0, 0);
+        }
+    };
+    auto frag = [&](const bf16* buf, int sl, int row) -> bf16x8 {
+        return *(const bf16x8*)(buf + sl * SLICE + row * BK + lane * 8);
+    };
+    f32x4 acc[F][F], accg[F][F];
+    // one MFMA on accumulator tile ij, written out so that the accumulators
+    // stay pinned in AGPRs
+    auto mma_ij = [](auto ij, f32x4 (&c)[F][F], const bf16x8 (&a)[F], const bf16x8 (&b)[F]) {
+        constexpr int i = decltype(ij)::value / F, j = decltype(ij)::value % F;
+        asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c[i][j]) : "v"(a[i]), "v"(b[j]));
+    };
+    // C (this wave's 64 x 64) += P Q^T over one 128-wide K block; P rows
+    // wm0.., Q rows wn0.., both K-blocked 128-row operands in LDS
+    auto block_mma = [&](f32x4 (&c)[F][F], const bf16* Pb, const bf16* Qb) {
+#pragma unroll
+        for (int sl = 0; sl < 4; ++sl) {
+            bf16x8 a[F], b[F];
+#pragma unroll
+            for (int i = 0; i < F; ++i) {
+                a[i] = frag(Pb, sl, wm0 + i * 16);
+                b[i] = frag(Qb, sl, wn0 + i * 16);
+            }
+            static_for<0, F * F>([&](auto ij) { mma_ij(ij, c, a, b); });
+        }
+    };
+    auto zero = [&](f32x4 (&c)[F][F]) {
+#pragma unroll
+        for (int i = 0; i < F; ++i)
+#pragma unroll
+            for (int j = 0; j < F; ++j) c[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // two wait states before an MFMA reads the cleared accumulators
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_nop 1");
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // the inline-asm MFMAs are opaque to the hazard recognizer: wait states
+    // before their accumulators are read back
+    auto mfma_drain = [&]() {
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // transposed view of strip fm for the fragment pair (fp, fp+1): w[e] =
+    // C[r0 + e][col], col = wn0 + (fp + (g4&1))*16 + l16, r0 = wm0 + fm*16 + 8*(g4>>1)
+    auto swap_pair = [&](float (&av)[F][4], int fp, float* w) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(av[fp][e]),
+                                                             __float_as_uint(av[fp + 1][e]), false, false);
+            w[e] = __uint_as_float(sw[0]);
+            w[4 + e] = __uint_as_float(sw[1]);
+        }
+    };
+    // B = gd I + gs A' into sB from the symmetric A' (row col of B is column
+    // col of A')
+    auto build_b = [&](float gs, float gd) {
+        mfma_drain();
+#pragma unroll
+        for (int fm = 0; fm < F; ++fm) {
+            float av[F][4];
+#pragma unroll
+            for (int fn = 0; fn < F; ++fn)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) av[fn][e] = agpr_read(accg[fm][fn][e]);
+#pragma unroll
+            for (int fp = 0; fp < F; fp += 2) {
+                float w[8];
+                swap_pair(av, fp, w);
+                const int col = wn0 + (fp + (g4 & 1)) * 16 + l16, r0 = wm0 + fm * 16 + 8 * (g4 >> 1);
+                bf16x8 q;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) q[e] = (bf16)(gs * w[e] + (col == r0 + e ? gd : 0.f));
+                *(bf16x8*)(sB + kb_off(col, r0, M)) = q;
+            }
+        }
+    };
+
+    const int64_t xt_stride = (int64_t)(np >> 4) * 512;   // one k-slice of X^T
+    const bf16* x0 = (const bf16*)P.x[0];
+    const float f = P.fold[0];
+
+    // A0 = X0 X0^T, one pass over X0 (block j of X0 is 32 KB contiguous)
+    zero(accg);
+    dma_block(sX0, x0, 0, SLICE);
+    auto gram0 = [&](int j, bf16* cur, bf16* nxt) {
+        __syncthreads();   // block j landed; everyone is done with `nxt`
+        if (j + 1 < NB) dma_block(nxt, x0, (int64_t)(j + 1) * OPB, SLICE);
+        block_mma(accg, cur, cur);
+    };
+    for (int j = 0; j < NB; j += 2) {
+        gram0(j, sX0, sX1);
+        if (j + 1 < NB) gram0(j + 1, sX1, sX0);
+    }
+    __syncthreads();
+    build_b(A.cb[0] * f * f * f, A.ca[0] * f);
+
+    // every step but the last: X'^T -> the other xt buffer, next B in sB
+    for (int k = 0; k + 1 < A.ns_steps; ++k) {
+        const bf16* xin = (const bf16*)((k & 1) ? P.xt[1] : P.xt[0]);
+        bf16* xout = (bf16*)((k & 1) ? P.xt[0] : P.xt[1]);
+        __syncthreads();   // B written by every wave
+        zero(accg);
+        dma_block(sX0, xin, 0, xt_stride);
+        auto step_block = [&](int j, bf16* cur, bf16* nxt) {
+            __syncthreads();   // block j landed, the previous block's stores done; `nxt` and sG free
+            if (j + 1 < NB) dma_block(nxt, xin, (int64_t)(j + 1) * 4096, xt_stride);
+            const int c0 = j * M + wn0;   // first X column of this wave's part
+            zero(acc);
+            block_mma(acc, sB, cur);
+            mfma_drain();
+#pragma unroll
+            for (int fm = 0; fm < F; ++fm) {
+                float av[F][4];
+#pragma unroll
+                for (int fn = 0; fn < F; ++fn)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) av[fn][e] = agpr_read(acc[fm][fn][e]);
+                // row copy staged first, so that the swaps consume av in place
+                wave_lds_sync();
+#pragma unroll
+                for (int fn = 0; fn < F; ++fn)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) st[(4 * g4 + e) * SP + fn * 16 + l16] = av[fn][e];
+#pragma unroll
+                for (int fp = 0; fp < F; fp += 2) {
+                    float w[8];
+                    swap_pair(av, fp, w);
+                    const int col = c0 + (fp + (g4 & 1)) * 16 + l16, r0 = wm0 + fm * 16 + 8 * (g4 >> 1);
+                    store8<bf16>(xout + kb_off(col, r0, np), w);
+                }
+                wave_lds_sync();
+#pragma unroll
+                for (int pass = 0; pass < PASSES; ++pass) {
+                    const int rr = l16, c8 = pass * 32 + g4 * 8;
+                    const f32x4 lo = *(const f32x4*)(st + rr * SP + c8);
+                    const f32x4 hi = *(const f32x4*)(st + rr * SP + c8 + 4);
+                    bf16x8 q;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        q[e] = (bf16)lo[e];
+                        q[4 + e] = (bf16)hi[e];
+                    }
+                    *(bf16x8*)(sG + kb_off(wm0 + fm * 16 + rr, wn0 + c8, M)) = q;
+                }
+            }
+            __syncthreads();   // X'_j complete in sG
+            block_mma(accg, sG, sG);
+        };
+        for (int j = 0; j < NB; j += 2) {
+            step_block(j, sX0, sX1);
+            if (j + 1 < NB) step_block(j + 1, sX1, sX0);
+        }
+        build_b(sCo[SMALL_MAX_STEPS + k + 1], sCo[k + 1]);
+    }
+    // the last step's B -> the problem's `a` buffer (same K-blocked layout)
+    __syncthreads();
+    bf16* ad = (bf16*)P.a;
+#pragma unroll
+    for (int i = 0; i < OPB / (NTHR * 8); ++i) {
+        const int o = (i * NTHR + tid) * 8;
+        *gp((bf16x8*)(ad + o)) = *(const bf16x8*)(sB + o);
+    }
+}
+
 template <int TS, bool SYM>
 hipError_t launch_bf16_t(const GemmArgs& a, hipStream_t s) {
     const unsigned grid = (unsigned)((a.total_tiles + 7) / 8 * 8);
@@ -822,6 +1046,13 @@ hipError_t launch_gemm_f32(const GemmArgs& a, hipStream_t s) {
         if (sym) hipLaunchKernelGGL((k_gemm_f32<true, float>), dim3(grid), dim3(NTHR), 0, s, a);
         else hipLaunchKernelGGL((k_gemm_f32<false, float>), dim3(grid), dim3(NTHR), 0, s, a);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_ns_small(const SmallArgs& a, hipStream_t s) {
+    if (a.nprobs <= 0) return hipSuccess;
+    if (a.ns_steps < 1 || a.ns_steps > SMALL_MAX_STEPS) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_ns_small, dim3(a.nprobs), dim3(NTHR), 0, s, a);
     return hipGetLastError();
 }
 
