@@ -237,8 +237,9 @@ int mu_version(void);
  */
 #define MU_K_PREP 0      /* momentum + Nesterov + U write + norm partials */
 #define MU_K_NORM 1      /* per-head norm finalisation */
-#define MU_K_GRAM 2      /* X X^T (upper tiles, mirrored); writes B = aI + bA on cubic steps */
+#define MU_K_GRAM 2      /* A = X X^T (upper tiles, mirrored); writes B = aI + bA on cubic steps */
 #define MU_K_GRAM2 3     /* A A^T for the quintic term; writes B = aI + bA + cA^2 */
+                         /* (on the first step B also carries the factor 1/||U||) */
 #define MU_K_APPLY 4     /* B X (last step fuses the update) */
 #define MU_K_FINISH 5    /* update when ns_steps == 0 */
 #define MU_K_ADAMW 6     /* AdamW */

@@ -25,6 +25,8 @@
 // K-blocked operands moved with direct-to-LDS buffer loads through a ring of
 // four LDS slots.
 // fp32: v_mfma_f32_16x16x4_f32, 64x64 tiles, BK = 32, row-major operands.
+// Short blocks (mp == 128) of a call with many of them: k_ns_small runs every
+// step but the last apply in one workgroup per block, with B kept in LDS.
 //
 // Epilogue: row-major outputs are staged per wave through LDS in 16-row strips
 // and stored as 16-byte chunks; transposed outputs (Gram mirror, X'^T, or a
