@@ -6,8 +6,10 @@
 // "Newton-Schulz Orthogonalization"; Qwen training-details page, "Confirmed",
 // for per-head blocks):
 //   prep (all problems) -> norm (all problems) ->
+//   [fused short blocks: every step but the last apply, one launch] ->
 //   for each step: Gram [-> Gram2 for a quintic term] -> apply
-//   (the last apply writes the updated parameter; ns_steps == 0 uses finish).
+//   (the last apply writes the updated parameter, for the fused blocks too;
+//   ns_steps == 0 uses finish).
 // AdamW: one launch over the flat tensor list (nanochat optimizer page,
 // "AdamW Step Implementation").
 #include <hip/hip_runtime.h>
