@@ -80,6 +80,23 @@ class MuonAdamW(torch.optim.Optimizer):
         super().__init__(groups, {})
         self._workspaces: Dict[tuple, torch.Tensor] = {}
 
+    # float32 state of both rules (the library reads and writes it as float32)
+    _F32_STATE = ("momentum_buffer", "exp_avg", "exp_avg_sq")
+
+    def load_state_dict(self, state_dict):
+        """torch's load_state_dict, except that the momentum and moment buffers
+        stay float32: torch casts floating-point state to each parameter's dtype
+        (bfloat16 for bf16 weights), which would lose their precision."""
+        saved = state_dict["state"]
+        super().load_state_dict(state_dict)
+        params = [p for g in self.param_groups for p in g["params"]]
+        for idx, st in saved.items():
+            p = params[idx]
+            for key in self._F32_STATE:
+                v = st.get(key)
+                if torch.is_tensor(v):
+                    self.state[p][key] = v.to(device=p.device, dtype=torch.float32, copy=True).contiguous()
+
     def _ws(self, key, nbytes, device):
         if nbytes == 0:
             return None
