@@ -1,6 +1,13 @@
 """Builds libmuon_mi355x.so (gfx950) in the package directory with hipcc.
 
     python -m newton_schulz_orthogonalized_amd.build
+    python -m newton_schulz_orthogonalized_amd.build --host-asan OUT.so
+
+The second form builds a debugging variant whose host code (the C ABI:
+validation, planning, table upload) is compiled with AddressSanitizer; the
+device code is the same. Load it with the clang ASan runtime preloaded, e.g.
+LD_PRELOAD=<rocm>/lib/llvm/lib/clang/<ver>/lib/linux/libclang_rt.asan-x86_64.so
+ASAN_OPTIONS=detect_leaks=0, in place of the regular library.
 """
 import os
 import subprocess
@@ -51,19 +58,31 @@ def _run(cmd, verbose):
         print(out, flush=True)
 
 
-def build(verbose: bool = True) -> str:
+def build(verbose: bool = True, out: str = LIB, host_asan: bool = False) -> str:
     import tempfile
     with tempfile.TemporaryDirectory(prefix="mu_build_") as objdir:
         cmds = compile_commands(objdir)
+        if host_asan:   # the host half of the C ABI only; the sanitizer never reaches device code
+            for c in cmds:
+                if c[c.index("-c") + 1].endswith("capi.hip"):
+                    c[1:1] = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer"]
         for c in cmds:
             _run(c, verbose)
-        tmp = LIB + ".tmp"
+        tmp = out + ".tmp"
         objs = [c[c.index("-o") + 1] for c in cmds]
-        _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs, verbose)
-        os.replace(tmp, LIB)
-    return LIB
+        link = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
+        if host_asan:
+            link[1:1] = ["-Xarch_host", "-fsanitize=address", "-shared-libasan"]
+        _run(link, verbose)
+        os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    if len(sys.argv) == 3 and sys.argv[1] == "--host-asan":
+        build(verbose=True, out=os.path.abspath(sys.argv[2]), host_asan=True)
+    elif len(sys.argv) == 1:
+        build(verbose=True)
+    else:
+        sys.exit("usage: python -m newton_schulz_orthogonalized_amd.build [--host-asan OUT.so]")
     sys.exit(0)
