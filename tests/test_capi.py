@@ -40,6 +40,21 @@ def test_every_declared_symbol_is_exported(lib):
     assert set(lib.EXPORTED) == set(_declared())
 
 
+def test_header_constants_match_the_binding(lib):
+    """The kernel-class ids, status codes and dtypes the binding uses are the
+    header's, and every kernel class has a name in the library."""
+    text = open(HEADER).read()
+    defs = {k: int(v) for k, v in re.findall(r"^#define\s+(MU_\w+)\s+\(?(-?\d+)\)?", text, re.M)}
+    for k, v in defs.items():
+        if k.startswith("MU_K_") or k.startswith("MU_ERR_") or k in ("MU_OK", "MU_F32", "MU_BF16"):
+            if hasattr(lib, k):
+                assert getattr(lib, k) == v, k
+    assert lib.MU_K_COUNT == defs["MU_K_COUNT"]
+    names = [lib.mu_kernel_name(k) for k in range(lib.MU_K_COUNT)]
+    assert "unknown" not in names and len(set(names)) == len(names)
+    assert lib.mu_kernel_name(lib.MU_K_COUNT) == "unknown"
+
+
 def test_version_and_status_strings(lib):
     assert lib.mu_version() == 1
     assert lib.mu_status_string(0) == "ok"
