@@ -207,6 +207,9 @@ void build_plan(const std::vector<Item>& items, int ns_dt, const std::vector<Coe
         if (fuse_ok && pp.tile == 128 && pp.d.mp == 128) ++n_fused;
     const bool fuse = n_fused >= FUSED_MIN_PROBS;
     auto is_fused = [&](const ProbPlan& pp) { return fuse && pp.tile == 128 && pp.d.mp == 128; };
+    // X^T buffers: read by the fp32 apply, the fused kernel and the finish
+    // kernel (ns_steps == 0, tall blocks); the bf16 tiled path reads X only
+    for (auto& pp : all) pp.d.xt_used = (ns_dt == DT_F32 || is_fused(pp) || co.empty()) ? 1 : 0;
     pl.probs.clear();
     pl.groups.clear();
     for (int gi = 0; gi < 4; ++gi) {
@@ -252,7 +255,7 @@ void build_plan(const std::vector<Item>& items, int ns_dt, const std::vector<Coe
     pl.off_fold = o;
     o = align_up(o + sizeof(float) * P);
     pl.off_bufs = o;
-    for (auto& pp : pl.probs) o += 4 * pp.x_bytes + pp.a_bytes * (pl.quintic ? 2 : 1);
+    for (auto& pp : pl.probs) o += (pp.d.xt_used ? 4 : 2) * pp.x_bytes + pp.a_bytes * (pl.quintic ? 2 : 1);
     pl.total = o;
 }
 
@@ -268,10 +271,14 @@ void carve(Plan& pl, char* ws, std::vector<char>& host_table) {
         o += pl.probs[i].x_bytes;
         d.x[1] = ws + o;
         o += pl.probs[i].x_bytes;
-        d.xt[0] = ws + o;
-        o += pl.probs[i].x_bytes;
-        d.xt[1] = ws + o;
-        o += pl.probs[i].x_bytes;
+        if (d.xt_used) {
+            d.xt[0] = ws + o;
+            o += pl.probs[i].x_bytes;
+            d.xt[1] = ws + o;
+            o += pl.probs[i].x_bytes;
+        } else {
+            d.xt[0] = d.xt[1] = nullptr;
+        }
         d.a = ws + o;
         o += pl.probs[i].a_bytes;
         if (pl.quintic) {

@@ -34,11 +34,14 @@ __device__ __forceinline__ MU_GLOBAL T* gp(T* p) {
 // U-space is the head block as stored: hr rows x hc cols, row pitch ld. X-space
 // is the wide orientation the iteration runs in: m = min(hr, hc) rows and
 // n = max(hr, hc) cols, X = U when hr <= hc and X = U^T otherwise ("tall").
-// The workspace keeps X (mp x np) and its transpose X^T (np x mp), so both
-// products of a step contract over the K dimension of both operands stored
-// K-contiguously: the Gram X X^T reads X twice, the apply B X reads B and X^T.
-// Buffers are padded with zeros to multiples of the GEMM tile; zero padding is
-// preserved by every step, so the GEMM kernels need no bounds checks.
+// The workspace keeps X (mp x np). The bf16 Gram X X^T reads it as both
+// operands and the bf16 apply B X reads it as its right operand through
+// transposing LDS reads. A transposed copy X^T (np x mp) exists only where a
+// kernel reads X with its k down the columns from memory: the fp32 apply, the
+// fused short-block kernel (k_ns_small) and the ns_steps == 0 finish of a tall
+// block (xt_used). Buffers are padded with zeros to multiples of the GEMM tile;
+// zero padding is preserved by every step, so the GEMM kernels need no bounds
+// checks.
 //
 // Storage of the workspace operands (X, X^T, A, B): with bf16 Newton-Schulz
 // they are K-blocked (see kb_off), with fp32 Newton-Schulz plain row-major.
@@ -55,9 +58,9 @@ struct NsProb {
     int32_t tall;      // X = U^T
     int32_t vec;       // 16-byte vector path is legal for the U-space buffers
     float scale;       // update scale
-    int32_t pad0;
+    int32_t xt_used;   // the X^T buffers exist (else xt[] are null)
     void* x[2];        // ping-pong X buffers, mp x np, NS element type
-    void* xt[2];       // their transposes, np x mp
+    void* xt[2];       // their transposes, np x mp, when xt_used
     void* a;           // a I + b A (cubic steps) or A = X X^T (quintic steps), mp x mp
     void* b;           // a I + b A + c A^2 (quintic steps), mp x mp, or null
     float* partials;   // per prep-tile sums of squares

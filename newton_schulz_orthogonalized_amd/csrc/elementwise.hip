@@ -140,10 +140,11 @@ __device__ inline void make_u(const NsProb& P, int r, int c0, bool with_m, bool 
     if (valid > 0) store4<float>(P.mom, (int64_t)r * P.ld + c0, valid, P.vec != 0, m);
 }
 
-// Tiles run over the buffer that has U's orientation (X for wide blocks, X^T
-// for tall ones): U is computed into an LDS tile, then written into that buffer
-// and, transposed, into the other one. Out-of-range elements are written as
-// zeros, which is the padding every later step relies on. Tile shape:
+// Tiles run over U's orientation (X for wide blocks, X^T for tall ones): U is
+// computed into an LDS tile and written into X, straight for a wide block and
+// transposed for a tall one, and into X^T too where the problem keeps it
+// (xt_used). Out-of-range elements are written as zeros, which is the padding
+// every later step relies on. Tile shape:
 // prep_rows(TX) x prep_cols(TX) (32 x 128 for bf16, so a tile reads 256-byte
 // gradient and 512-byte momentum runs per row). With bf16 Newton-Schulz both
 // buffers are K-blocked: a tile is 8 whole 1 KB blocks in each of them, and
@@ -162,8 +163,9 @@ __global__ __launch_bounds__(NTHR) void k_prep(PrepArgs A) {
     const bool wide = !P.tall;
     const int RD = wide ? P.mp : P.np;   // rows of the U-oriented buffer
     const int KD = wide ? P.np : P.mp;   // its columns = rows of the other one
-    TX* D = (TX*)(wide ? P.x[0] : P.xt[0]);
-    TX* Tt = (TX*)(wide ? P.xt[0] : P.x[0]);
+    TX* D = (TX*)(wide ? P.x[0] : P.xt[0]);    // U's orientation
+    TX* Tt = (TX*)(wide ? P.xt[0] : P.x[0]);   // transposed
+    const bool wr_d = wide || P.xt_used, wr_t = !wide || P.xt_used;
     const int tiles_n = KD / TC;
     const int ti = local / tiles_n, tj = local - ti * tiles_n;
     const int tid = threadIdx.x;
@@ -210,7 +212,9 @@ __global__ __launch_bounds__(NTHR) void k_prep(PrepArgs A) {
             ss += u[e] * u[e];
             tile[rr + RSTEP * k][cc + e] = u[e];
         }
-        if constexpr (sizeof(TX) == 4) store_x4<TX>(D + (int64_t)r * KD + c0, u);
+        if constexpr (sizeof(TX) == 4) {
+            if (wr_d) store_x4<TX>(D + (int64_t)r * KD + c0, u);
+        }
     }
     __syncthreads();
     if constexpr (sizeof(TX) == 2) {
@@ -220,7 +224,7 @@ __global__ __launch_bounds__(NTHR) void k_prep(PrepArgs A) {
             const int q = pass * NTHR + tid;
             const int blk = q >> 6, c = (q >> 4) & 3, r16 = q & 15;
             // D: block (row group g, k-panel pl) of the tile; chunk c of row r16
-            {
+            if (wr_d) {
                 const int g = blk % (TR / 16), pl = blk / (TR / 16);
                 const int row = g * 16 + r16, col = pl * 32 + c * 8;
                 bf16x8 o;
@@ -229,7 +233,7 @@ __global__ __launch_bounds__(NTHR) void k_prep(PrepArgs A) {
                 *(MU_GLOBAL bf16x8*)(D + kb_off(ti * TR + row, tj * TC + col, RD)) = o;
             }
             // the other buffer: its rows are tile columns, its k the tile rows
-            {
+            if (wr_t) {
                 const int g = blk % (TC / 16), pl = blk / (TC / 16);
                 const int row = g * 16 + r16, col = pl * 32 + c * 8;
                 bf16x8 o;
@@ -241,7 +245,7 @@ __global__ __launch_bounds__(NTHR) void k_prep(PrepArgs A) {
     } else {
         static_assert(TR == TC, "the fp32 transpose pass walks a square tile");
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
+        for (int k = 0; k < 4 && wr_t; ++k) {
             const int a = rr + RSTEP * k;
             float v[4];
 #pragma unroll

@@ -14,11 +14,13 @@
 // by binary search over a tile prefix, and workgroup ids are remapped so that
 // neighbouring tiles run on the same XCD (shared L2).
 //
-// Every product is "NT", C = P Q^T with both operands K-contiguous: the Gram
-// X X^T reads X twice; the apply B X reads B (symmetric) and the transposed
-// copy X^T that the previous step's epilogue (or the prep kernel) wrote. Gram
-// products only compute tiles on or above the diagonal and also store the
-// transposed tile.
+// The Gram X X^T is "NT" (C = P Q^T, both operands K-contiguous) and reads X
+// twice. The bf16 apply B X reads B (symmetric, K-contiguous) and X itself,
+// whose k runs down its rows: fragments of X come out of LDS through
+// ds_read_b64_tr_b16, so no transposed copy of X is ever written. (The fp32
+// kernel reads a transposed copy X^T that the previous epilogue or the prep
+// kernel wrote.) Gram products only compute tiles on or above the diagonal and
+// also store the transposed tile.
 //
 // bf16: v_mfma_f32_16x16x32_bf16, fp32 accumulation, 256x256 or 128x128
 // workgroup tiles, BK = 32, 4 waves in 2x2 (128x128 per wave for 256 tiles),
@@ -29,8 +31,9 @@
 // step but the last apply in one workgroup per block, with B kept in LDS.
 //
 // Epilogue: row-major outputs are staged per wave through LDS in 16-row strips
-// and stored as 16-byte chunks; transposed outputs (Gram mirror, X'^T, or a
-// tall weight) are formed in registers with v_permlane16_swap. The Gram
+// and stored as 16-byte chunks; transposed outputs (Gram mirror, a tall
+// weight, X'^T of the fp32 path) are formed in registers with
+// v_permlane16_swap. The Gram
 // epilogue applies the step coefficients and, on the first step, the fold
 // f = 1/||U||_F (so the normalised X0 is never materialised); the last apply
 // writes the decoupled-weight-decay update W <- W - lr*wd*W - lr*scale*O
@@ -214,14 +217,14 @@ __device__ __forceinline__ void wave_lds_sync() { asm volatile("" ::: "memory");
 //   Gram, cubic step     B = f (a I + b f^2 X X^T)    -> P.a (mirrored)
 //   Gram, quintic step   A = f^2 X X^T                -> P.a (mirrored)
 //   A^2 pass             B = f (a I + b A + c A A^T)  -> P.b (mirrored)
-//   apply                X' = B X                     -> X', X'^T
+//   apply                X' = B X                     -> X' (and X'^T, fp32 only)
 //   last apply           O = B X -> parameter update (or output)
 // On the first step X holds U itself, and f (a X0 + b (X0 X0^T) X0) with
 // X0 = f U is exactly B U for these B. Folding a I and f into B keeps X and
 // any scaling out of the apply epilogue; padding stays zero because a padded
 // row of X' is f*a*0 + (rows of A that are zero).
 //
-// Transposed outputs (Gram mirror, X'^T, a tall block's parameter) come
+// Transposed outputs (Gram mirror, fp32 X'^T, a tall block's parameter) come
 // straight from registers: v_permlane16_swap on the accumulators of two
 // neighbouring fragments leaves every lane with 8 consecutive rows of one
 // column, one 16-byte chunk of the transposed (K-blocked) output.
@@ -257,7 +260,8 @@ __device__ __forceinline__ void epilogue_mode(const GemmArgs& A, const NsProb& P
     const bool diag = gram && ti == tj;
     const bool mirror = gram && ti != tj;
     constexpr bool last = mode == GM_APPLY_LAST;
-    const bool trans_out = mirror || (!gram && !last) || (last && P.tall);
+    // X'^T is kept only for the fp32 kernel; the bf16 apply reads X itself
+    const bool trans_out = mirror || (!gram && !last && sizeof(TX) == 4) || (last && P.tall);
     const bool row_out = !(last && P.tall);
     const int row_base = ti * TS_ + wm0, col_base = tj * TS_ + wn0;
 
@@ -376,7 +380,7 @@ __device__ __forceinline__ void epilogue_mode(const GemmArgs& A, const NsProb& P
 #pragma unroll
                     for (int e = 0; e < 8; ++e) v[e] = w[e];
                     if constexpr (!last) {
-                        store8<TX>(tdst(xtdst, np, mp, c, r0, fm, fp), v);
+                        if constexpr (sizeof(TX) == 4) store8<TX>(tdst(xtdst, np, mp, c, r0, fm, fp), v);
                     } else if constexpr (staged_tall) {
                         // block row cl = c - col_base, columns rl .. rl+7
                         const int cl = (fp + (g4 & 1)) * 16 + l16;
@@ -548,7 +552,10 @@ __global__ __launch_bounds__(NTHR) void k_gemm_bf16(GemmArgs A) {
     if (SYM) upper_tile(local, P.mp / TS, ti, tj);
     else apply_tile(local, P.mp / TS, P.np / TS, ti, tj);
 
-    // C = P Q^T over K; P has RP rows, Q has RQ rows, both K-blocked
+    // Gram modes: C = P Q^T over K, P and Q K-blocked with RP and RQ rows.
+    // Apply: C = B X, B K-blocked (mp rows, k = mp) and X itself (mp rows,
+    // k = np) as the right operand, whose k runs down X's rows (see dma_slice
+    // and read_b).
     const bf16 *pm, *qm;
     int RP, RQ, K;
     if (mode == GM_GRAM) {
@@ -557,7 +564,7 @@ __global__ __launch_bounds__(NTHR) void k_gemm_bf16(GemmArgs A) {
         pm = qm = (const bf16*)P.a; RP = RQ = P.mp; K = P.mp;
     } else {
         pm = (const bf16*)(A.use_b ? P.b : P.a); RP = P.mp;
-        qm = (const bf16*)(A.src ? P.xt[1] : P.xt[0]); RQ = P.np; K = P.mp;
+        qm = (const bf16*)(A.src ? P.x[1] : P.x[0]); RQ = P.mp; K = P.mp;
     }
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -579,36 +586,75 @@ __global__ __launch_bounds__(NTHR) void k_gemm_bf16(GemmArgs A) {
         else return sB3;
     };
 
-    // Direct loads. The TS x 32 slice kt of an operand tile is NBLK contiguous
-    // 1 KB blocks starting at block kt*R/16 + tile*TS/16; a buffer resource
-    // covering exactly that run (an offset outside it reads zeros instead of
-    // faulting) is built per step from the wave-uniform address. Block b of
-    // the slice goes to block b of the slot, lane l moving bytes 16l..16l+15:
-    // a plain 1 KB copy, eight whole 128-byte lines per instruction.
+    // Direct loads. The TS x 32 slice kt of a K-blocked operand tile is NBLK
+    // contiguous 1 KB blocks starting at block kt*R/16 + tile*TS/16; a buffer
+    // resource covering exactly that run (an offset outside it reads zeros
+    // instead of faulting) is built per step from the wave-uniform address.
+    // Block b of the slice goes to block b of the slot, lane l moving bytes
+    // 16l..16l+15: a plain 1 KB copy, eight whole 128-byte lines per
+    // instruction.
+    // The apply's right operand is X: slice kt is rows 32kt .. 32kt+31 of the
+    // tile's TS columns, i.e. row groups 2kt and 2kt+1 of TS/32 k-panels, two
+    // adjacent blocks per panel with panels mp/16 blocks apart. Slot block
+    // 2*panel + group holds it, its 16-byte chunks permuted: chunk (c, r) of
+    // the X block (k chunk c, row r) sits at slot chunk (c, r ^ 4*(c&1)),
+    // which keeps the transposed fragment reads below free of bank conflicts.
     const uint32_t lane_off = (uint32_t)lane * 16u;
+    const uint32_t lane_xoff = (uint32_t)(256 * (lane >> 4) + 16 * ((lane & 15) ^ (4 * ((lane >> 4) & 1))));
+    const uint32_t x_pan = (uint32_t)(RQ >> 4) * 1024u;   // bytes between k-panels of X
     auto slice = [&](const bf16* base, int R, int tile, int kt) {
         return __builtin_amdgcn_make_buffer_rsrc(
             (void*)(base + ((int64_t)kt * (R >> 4) + (int64_t)tile * (TS >> 4)) * 512), 0, NBLK * 1024, BUF_RAW32);
     };
+    auto slice_x = [&](int kt) {
+        return __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(qm + ((int64_t)tj * (TS / 32) * (RQ >> 4) + 2 * kt) * 512), 0, (TS / 32 - 1) * x_pan + 2048u,
+            BUF_RAW32);
+    };
     auto dma_slice = [&](auto st, int kt, auto first, auto count) {
         constexpr int I0 = decltype(first)::value, NI = decltype(count)::value;
         const __amdgpu_buffer_rsrc_t ra = slice(pm, RP, ti, kt);
-        const __amdgpu_buffer_rsrc_t rb = slice(qm, RQ, tj, kt);
+        __amdgpu_buffer_rsrc_t rb;
+        if constexpr (SYM) rb = slice(qm, RQ, tj, kt);
+        else rb = slice_x(kt);
         static_for<I0, I0 + NI>([&](auto ic) {
             constexpr int i = decltype(ic)::value;
             constexpr bool isA = i < BPW;
             const int b = (isA ? i : i - BPW) * 4 + wave;
             bf16* dst = (isA ? slot_a(st) : slot_b(st)) + b * 512;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(isA ? ra : rb, (LDSP void*)dst, 16, lane_off, (uint32_t)b * 1024u,
-                                                     0, 0);
+            if (isA || SYM)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(isA ? ra : rb, (LDSP void*)dst, 16, lane_off,
+                                                         (uint32_t)b * 1024u, 0, 0);
+            else
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (LDSP void*)dst, 16, lane_xoff,
+                                                         (uint32_t)(b >> 1) * x_pan + (uint32_t)(b & 1) * 1024u, 0, 0);
         });
     };
     auto dma = [&](auto st, int kt) { dma_slice(st, kt, Stage<0>{}, Stage<NDMA>{}); };
     auto read_a = [&](auto st, int fm) -> bf16x8 {
         return *(const bf16x8*)(slot_a(st) + (wm0 + fm * 16) * BK + lane * 8);
     };
+    // Apply fragment fn (X columns wn0 + 16fn ..): lane l needs rows
+    // 8(l>>4) .. +7 of column l&15. ds_read_b64_tr_b16 hands lane i of each
+    // 16-lane group element i%4 of the 4-element run addressed by lane
+    // 4j + i/4 as its element j; lane i addresses row r0 + i/4, columns
+    // 4(i%4) .. +3 (r0 = 8(l>>4), then r0 + 4), so it receives column i of
+    // those four rows. Slot block 2*(wn0/32 + fn/2) + (l>>5), k chunk
+    // 2(fn&1) + ((i>>1)&1).
+    const int trs = (lane >> 1) & 1;
+    const int tr_row = 8 * ((lane >> 4) & 1) + ((lane & 15) >> 2);
+    const uint32_t tr_lane = (uint32_t)(1024 * (lane >> 5) + 256 * trs + 8 * (lane & 1));
+    const uint32_t tr0 = tr_lane + 16u * (uint32_t)(tr_row + 4 * trs);
+    const uint32_t tr1 = tr_lane + 16u * (uint32_t)(tr_row + 4 * (trs ^ 1));
     auto read_b = [&](auto st, int fn) -> bf16x8 {
-        return *(const bf16x8*)(slot_b(st) + (wn0 + fn * 16) * BK + lane * 8);
+        if constexpr (SYM) {
+            return *(const bf16x8*)(slot_b(st) + (wn0 + fn * 16) * BK + lane * 8);
+        } else {
+            const char* blk = (const char*)slot_b(st) + (wn0 / 32 + fn / 2) * 2048 + (fn & 1) * 512;
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDSP i16x4*)(blk + tr0));
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDSP i16x4*)(blk + tr1));
+            return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
     };
 
     f32x4 acc[F][F];
@@ -799,16 +845,18 @@ __global__ __launch_bounds__(NTHR) void k_gemm_f32(GemmArgs A) {
 // Newton-Schulz for one problem with mp == 128 (a 128-row head block, or any
 // matrix whose short side is at most 128) in one workgroup, up to the last
 // apply. Such short, wide problems are bound by HBM, and the tiled path moves X
-// through it three times per step (the Gram reads X, the apply reads X^T and
-// writes X' and X'^T). Here B (128 x 128) stays in LDS and each step streams
-// X^T once, in blocks of 128 columns of X:
+// through it three times per step (the Gram reads X, the apply reads X and
+// writes X'). Here B (128 x 128) stays in LDS and each step streams X^T once,
+// in blocks of 128 columns of X:
 //   X'_j = B X_j            (B and X^T_j from LDS)
 //   X'^T_j -> HBM           (the next step's input)
 //   A' += X'_j X'_j^T       (from a K-blocked LDS copy of X'_j, bf16 as stored)
 // and the next step's B = a' I + b' A' is written into LDS from the symmetric
 // A'. The first B = f (a I + b f^2 X0 X0^T) comes from one pass over X0. The
-// B of the last step is copied to the problem's `a` buffer, and the tiled last
-// apply (which fuses the parameter update) finishes the run.
+// B of the last step is copied to the problem's `a` buffer and the X it
+// multiplies is written in X's own layout (copied from the LDS copy of X'_j),
+// and the tiled last apply (which fuses the parameter update) finishes the
+// run.
 // X blocks are double-buffered with direct-to-LDS loads. The wait at a block
 // boundary covers the previous block's stores too: loads and stores share
 // vmcnt, which does not order one against the other.
@@ -951,10 +999,14 @@ __global__ __launch_bounds__(NTHR) void k_ns_small(SmallArgs A) {
     __syncthreads();
     build_b(A.cb[0] * f * f * f, A.ca[0] * f);
 
-    // every step but the last: X'^T -> the other xt buffer, next B in sB
+    // every step but the last: X'^T -> the other xt buffer, next B in sB; the
+    // X that the last apply reads goes to x[(ns_steps - 1) & 1] instead, in
+    // X's own layout
     for (int k = 0; k + 1 < A.ns_steps; ++k) {
+        const bool final_x = k + 2 == A.ns_steps;
         const bf16* xin = (const bf16*)((k & 1) ? P.xt[1] : P.xt[0]);
         bf16* xout = (bf16*)((k & 1) ? P.xt[0] : P.xt[1]);
+        bf16* xfin = (bf16*)((k & 1) ? P.x[0] : P.x[1]);
         __syncthreads();   // B written by every wave
         zero(accg);
         dma_block(sX0, xin, 0, xt_stride);
@@ -978,12 +1030,14 @@ __global__ __launch_bounds__(NTHR) void k_ns_small(SmallArgs A) {
                 for (int fn = 0; fn < F; ++fn)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) st[(4 * g4 + e) * SP + fn * 16 + l16] = av[fn][e];
+                if (!final_x) {
 #pragma unroll
-                for (int fp = 0; fp < F; fp += 2) {
-                    float w[8];
-                    swap_pair(av, fp, w);
-                    const int col = c0 + (fp + (g4 & 1)) * 16 + l16, r0 = wm0 + fm * 16 + 8 * (g4 >> 1);
-                    store8<bf16>(xout + kb_off(col, r0, np), w);
+                    for (int fp = 0; fp < F; fp += 2) {
+                        float w[8];
+                        swap_pair(av, fp, w);
+                        const int col = c0 + (fp + (g4 & 1)) * 16 + l16, r0 = wm0 + fm * 16 + 8 * (g4 >> 1);
+                        store8<bf16>(xout + kb_off(col, r0, np), w);
+                    }
                 }
                 wave_lds_sync();
 #pragma unroll
@@ -1001,6 +1055,16 @@ __global__ __launch_bounds__(NTHR) void k_ns_small(SmallArgs A) {
                 }
             }
             __syncthreads();   // X'_j complete in sG
+            if (final_x) {
+                // sG is X'_j K-blocked with 128 rows, which is exactly the
+                // 32 KB run of X (mp = 128) holding columns 128j .. 128j+127
+                bf16* xd = xfin + (int64_t)j * OPB;
+#pragma unroll
+                for (int i = 0; i < OPB / (NTHR * 8); ++i) {
+                    const int o = (i * NTHR + tid) * 8;
+                    *gp((bf16x8*)(xd + o)) = *(const bf16x8*)(sG + o);
+                }
+            }
             block_mma(accg, sG, sG);
         };
         for (int j = 0; j < NB; j += 2) {
