@@ -310,6 +310,7 @@ void carve(Plan& pl, char* ws, std::vector<char>& host_table) {
 // ---------------------------------------------------------------------------
 struct Slot {
     void* host = nullptr;
+    void* host_dev = nullptr;   // the device's address of `host`
     size_t cap = 0;
     hipEvent_t ev = nullptr;
     bool pending = false;
@@ -350,6 +351,12 @@ int upload(const void* src, size_t bytes, void* dst, hipStream_t s) {
         size_t cap = std::max<size_t>(bytes, 64 << 10);
         e = hipHostMalloc(&sl.host, cap, hipHostMallocDefault);
         if (e != hipSuccess) return hip_fail(e, "hipHostMalloc(staging)");
+        e = hipHostGetDevicePointer(&sl.host_dev, sl.host, 0);
+        if (e != hipSuccess) {
+            (void)hipHostFree(sl.host);
+            sl.host = nullptr;
+            return hip_fail(e, "hipHostGetDevicePointer(staging)");
+        }
         sl.cap = cap;
     }
     if (!sl.ev) {
@@ -357,8 +364,8 @@ int upload(const void* src, size_t bytes, void* dst, hipStream_t s) {
         if (e != hipSuccess) return hip_fail(e, "hipEventCreate(staging)");
     }
     std::memcpy(sl.host, src, bytes);
-    e = hipMemcpyAsync(dst, sl.host, bytes, hipMemcpyHostToDevice, s);
-    if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(table)");
+    e = launch_table_copy(sl.host_dev, dst, bytes, s);
+    if (e != hipSuccess) return hip_fail(e, "table copy launch");
     e = hipEventRecord(sl.ev, s);
     if (e != hipSuccess) return hip_fail(e, "hipEventRecord(staging)");
     sl.pending = true;

@@ -1,13 +1,16 @@
 // HBM-bound kernels of the Muon step and the AdamW step (gfx950).
 //
 //  k_prep    momentum EMA + Nesterov blend, write U into the workspace as X
-//            (wide orientation) and X^T with zero padding, through an LDS
-//            tile, and one sum of squares per 64x64 tile (fixed order).
+//            (wide orientation; and X^T where a problem keeps it) with zero
+//            padding, through an LDS tile, and one sum of squares per tile
+//            (fixed order).
 //  k_norm    per (matrix, head): fixed-order sum of the tile partials,
 //            fold = 1/(||U||_F + eps).
 //  k_finish  ns_steps == 0: O = fold * X0, then the update (or the output).
 //  k_adamw   bias-corrected AdamW over a flat list of tensors, one launch.
 //  k_qkclip  QK-Clip: per-head rescale of attention query/key weights.
+//  k_table   copy of a call's descriptor table from pinned host memory into
+//            the workspace.
 //
 // Momentum: MuonClip Optimizer page, section "Momentum" (EMA, decay 0.95).
 // Nesterov blend: named on the nanochat optimizer page ("Muon Step
@@ -484,6 +487,18 @@ __device__ __forceinline__ void qk_scale8(MU_GLOBAL TW* w, int cnt, bool vec, fl
     }
 }
 
+// Descriptor table upload: n16 16-byte chunks, then `tail` bytes, from
+// pinned host memory (read over the host link) into the workspace. A kernel
+// on the call's stream instead of an asynchronous host-to-device copy: on this
+// platform the copy engine adds tens of microseconds to every call, which is
+// most of a call on small parameter sets.
+__global__ __launch_bounds__(NTHR) void k_table(const u32x4* src, u32x4* dst, int64_t n16, int tail) {
+    const int64_t stride = (int64_t)gridDim.x * NTHR;
+    for (int64_t i = (int64_t)blockIdx.x * NTHR + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
+    if (blockIdx.x == 0 && (int)threadIdx.x < tail)
+        ((unsigned char*)(dst + n16))[threadIdx.x] = ((const unsigned char*)(src + n16))[threadIdx.x];
+}
+
 __global__ __launch_bounds__(NTHR) void k_qkclip(QkArgs A) {
     const int64_t c = blockIdx.x;
     const int i = __builtin_amdgcn_readfirstlane(find_tensor(A.prefix, A.n, c));
@@ -507,6 +522,15 @@ __global__ __launch_bounds__(NTHR) void k_qkclip(QkArgs A) {
 }
 
 }  // namespace
+
+hipError_t launch_table_copy(const void* src, void* dst, size_t bytes, hipStream_t s) {
+    if (bytes == 0) return hipSuccess;
+    const size_t n16 = bytes / 16;
+    const unsigned grid = (unsigned)std::min<size_t>(64, std::max<size_t>(1, (n16 + NTHR - 1) / NTHR));
+    hipLaunchKernelGGL(k_table, dim3(grid), dim3(NTHR), 0, s, (const u32x4*)src, (u32x4*)dst, (int64_t)n16,
+                       (int)(bytes % 16));
+    return hipGetLastError();
+}
 
 hipError_t launch_prep(const PrepArgs& a, hipStream_t s) {
     if (a.total_tiles <= 0) return hipSuccess;

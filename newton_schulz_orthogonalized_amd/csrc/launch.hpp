@@ -131,4 +131,8 @@ struct QkArgs {
 constexpr int QK_CHUNK = 8192;  // elements per workgroup
 hipError_t launch_qkclip(const QkArgs& a, hipStream_t s);
 
+// Copy `bytes` from device-visible pinned host memory `src` (16-byte aligned)
+// to device memory `dst` (16-byte aligned) on stream s.
+hipError_t launch_table_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
+
 }  // namespace mu
