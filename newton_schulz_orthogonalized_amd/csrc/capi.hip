@@ -207,9 +207,9 @@ void build_plan(const std::vector<Item>& items, int ns_dt, const std::vector<Coe
         if (fuse_ok && pp.tile == 128 && pp.d.mp == 128) ++n_fused;
     const bool fuse = n_fused >= FUSED_MIN_PROBS;
     auto is_fused = [&](const ProbPlan& pp) { return fuse && pp.tile == 128 && pp.d.mp == 128; };
-    // X^T buffers: read by the fp32 apply, the fused kernel and the finish
-    // kernel (ns_steps == 0, tall blocks); the bf16 tiled path reads X only
-    for (auto& pp : all) pp.d.xt_used = (ns_dt == DT_F32 || is_fused(pp) || co.empty()) ? 1 : 0;
+    // X^T buffers: read by the fp32 apply and by the finish kernel
+    // (ns_steps == 0, tall blocks); the bf16 kernels read X only
+    for (auto& pp : all) pp.d.xt_used = (ns_dt == DT_F32 || co.empty()) ? 1 : 0;
     pl.probs.clear();
     pl.groups.clear();
     for (int gi = 0; gi < 4; ++gi) {
@@ -480,7 +480,7 @@ int run_pipeline(Plan& pl, char* ws, const mu_muon_hparams* hp, int src_dt, bool
             const double m = pl.probs[i].d.m, n = pl.probs[i].d.n;
             const double xb = (double)pl.probs[i].d.mp * pl.probs[i].d.np * ns_es;
             fl += m * (m + 1) * n + (hp->ns_steps - 1) * (2 * m * m * n + 3 * m * n + m * (m + 1) * n);
-            by += xb * (1 + 2 * (hp->ns_steps - 1));   // X0 once, then X^T in and X'^T out per step
+            by += xb * (1 + 2 * (hp->ns_steps - 1));   // X0 once, then X in and X' out per step
         }
         rc = timed_launch(MU_K_FUSED, fl, by, s, [&] { return launch_ns_small(sa, s); }, "fused launch");
         if (rc) return rc;

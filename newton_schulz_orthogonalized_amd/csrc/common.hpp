@@ -36,9 +36,9 @@ __device__ __forceinline__ MU_GLOBAL T* gp(T* p) {
 // n = max(hr, hc) cols, X = U when hr <= hc and X = U^T otherwise ("tall").
 // The workspace keeps X (mp x np). The bf16 Gram X X^T reads it as both
 // operands and the bf16 apply B X reads it as its right operand through
-// transposing LDS reads. A transposed copy X^T (np x mp) exists only where a
-// kernel reads X with its k down the columns from memory: the fp32 apply, the
-// fused short-block kernel (k_ns_small) and the ns_steps == 0 finish of a tall
+// transposing LDS reads (as does the fused short-block kernel). A transposed
+// copy X^T (np x mp) exists only where a kernel reads X with its k down the
+// columns from memory: the fp32 apply and the ns_steps == 0 finish of a tall
 // block (xt_used). Buffers are padded with zeros to multiples of the GEMM tile;
 // zero padding is preserved by every step, so the GEMM kernels need no bounds
 // checks.

@@ -63,11 +63,10 @@ hipError_t launch_gemm_bf16(const GemmArgs& a, int tile, hipStream_t s);
 hipError_t launch_gemm_f32(const GemmArgs& a, hipStream_t s);
 
 // Newton-Schulz for problems with mp == 128 (bf16, cubic steps) up to the last
-// apply, in one launch, one workgroup per problem. X0 is in x[0] and X0^T in
-// xt[0]; the steps ping-pong between xt[0] and xt[1], except that the X of the
-// last step is written to x[(ns_steps - 1) & 1] (X's own layout), and that
-// step's B is left in `a` for the tiled last apply (GM_APPLY_LAST), which
-// writes the update.
+// apply, in one launch, one workgroup per problem. X0 is in x[0]; the steps
+// ping-pong between x[0] and x[1] as on the tiled path, so the X of the last
+// step is in x[(ns_steps - 1) & 1], and that step's B is left in `a` for the
+// tiled last apply (GM_APPLY_LAST), which writes the update.
 constexpr int SMALL_MAX_STEPS = 16;
 struct SmallArgs {
     const NsProb* probs;

@@ -846,17 +846,16 @@ __global__ __launch_bounds__(NTHR) void k_gemm_f32(GemmArgs A) {
 // matrix whose short side is at most 128) in one workgroup, up to the last
 // apply. Such short, wide problems are bound by HBM, and the tiled path moves X
 // through it three times per step (the Gram reads X, the apply reads X and
-// writes X'). Here B (128 x 128) stays in LDS and each step streams X^T once,
-// in blocks of 128 columns of X:
-//   X'_j = B X_j            (B and X^T_j from LDS)
-//   X'^T_j -> HBM           (the next step's input)
+// writes X'). Here B (128 x 128) stays in LDS and each step streams X once,
+// in blocks of 128 columns (one contiguous 32 KB run each):
+//   X'_j = B X_j            (B from LDS, X_j through transposed LDS reads)
 //   A' += X'_j X'_j^T       (from a K-blocked LDS copy of X'_j, bf16 as stored)
+//   X'_j -> HBM             (that LDS copy, which has X's layout: the next
+//                            step's input)
 // and the next step's B = a' I + b' A' is written into LDS from the symmetric
 // A'. The first B = f (a I + b f^2 X0 X0^T) comes from one pass over X0. The
-// B of the last step is copied to the problem's `a` buffer and the X it
-// multiplies is written in X's own layout (copied from the LDS copy of X'_j),
-// and the tiled last apply (which fuses the parameter update) finishes the
-// run.
+// B of the last step is copied to the problem's `a` buffer, and the tiled last
+// apply (which fuses the parameter update) finishes the run.
 // X blocks are double-buffered with direct-to-LDS loads. The wait at a block
 // boundary covers the previous block's stores too: loads and stores share
 // vmcnt, which does not order one against the other.
@@ -890,22 +889,41 @@ __global__ __launch_bounds__(NTHR) void k_ns_small(SmallArgs A) {
         }
     }
 
-    // 32 KB operand block -> LDS buffer: k-slice s (8 KB) is the run starting
-    // at element run0 + s * stride of base; wave w moves 1 KB blocks w, w+4, ..
+    // Block j of X (columns 128j .. 128j+127) is one contiguous 32 KB run of
+    // X's K-blocked layout (mp = 128): k-panel p (columns 32p ..) is the 8 KB
+    // at 4096p, row group g the 1 KB at 512g inside it. It is copied into LDS
+    // in that order; wave w moves 1 KB blocks w, w+4, .. With `permute`, each
+    // block's 16-byte chunks are permuted as for the tiled apply (chunk (c, r)
+    // at (c, r ^ 4(c&1))) for the transposed reads of the apply below.
     const uint32_t lane_off = (uint32_t)lane * 16u;
-    auto dma_block = [&](bf16* dst, const bf16* base, int64_t run0, int64_t stride) {
+    const uint32_t lane_xoff = (uint32_t)(256 * (lane >> 4) + 16 * ((lane & 15) ^ (4 * ((lane >> 4) & 1))));
+    auto dma_block = [&](bf16* dst, const bf16* base, int j, bool permute) {
+        const __amdgpu_buffer_rsrc_t rs =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(base + (int64_t)j * OPB), 0, OPB * 2, BUF_RAW32);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int b = i * 4 + wave;
-            const int sl = b >> 3, g = b & 7;
-            const __amdgpu_buffer_rsrc_t rs =
-                __builtin_amdgcn_make_buffer_rsrc((void*)(base + run0 + sl * stride), 0, SLICE * 2, BUF_RAW32);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDSP void*)(dst + sl * SLICE + g * 512), 16, lane_off,
-                                                     (uint32_t)g * 1024u, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDSP void*)(dst + b * 512), 16, permute ? lane_xoff : lane_off,
+                                                     (uint32_t)b * 1024u, 0, 0);
         }
     };
+    // fragment of a K-blocked 128-row operand: rows row .. row+15, k-panel sl
     auto frag = [&](const bf16* buf, int sl, int row) -> bf16x8 {
         return *(const bf16x8*)(buf + sl * SLICE + row * BK + lane * 8);
+    };
+    // fragment of a permuted X block as the right operand of B X: rows
+    // 32sl + 8(lane>>4) .. +7 (k) of column col0 + (lane&15); two transposed
+    // reads, lane addressing as in the tiled apply
+    const int trs = (lane >> 1) & 1;
+    const int tr_row = 8 * ((lane >> 4) & 1) + ((lane & 15) >> 2);
+    const uint32_t tr_lane = (uint32_t)(1024 * (lane >> 5) + 256 * trs + 8 * (lane & 1));
+    const uint32_t tr0 = tr_lane + 16u * (uint32_t)(tr_row + 4 * trs);
+    const uint32_t tr1 = tr_lane + 16u * (uint32_t)(tr_row + 4 * (trs ^ 1));
+    auto frag_x = [&](const bf16* buf, int sl, int col0) -> bf16x8 {
+        const char* blk = (const char*)buf + ((col0 >> 5) * 8 + 2 * sl) * 1024 + ((col0 >> 4) & 1) * 512;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDSP i16x4*)(blk + tr0));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDSP i16x4*)(blk + tr1));
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     };
     f32x4 acc[F][F], accg[F][F];
     // one MFMA on accumulator tile ij, written out so that the accumulators
@@ -924,6 +942,20 @@ __global__ __launch_bounds__(NTHR) void k_ns_small(SmallArgs A) {
             for (int i = 0; i < F; ++i) {
                 a[i] = frag(Pb, sl, wm0 + i * 16);
                 b[i] = frag(Qb, sl, wn0 + i * 16);
+            }
+            static_for<0, F * F>([&](auto ij) { mma_ij(ij, c, a, b); });
+        }
+    };
+    // C (this wave's 64 x 64 of B X_j) += over the 128 rows of X_j: B from
+    // sB, X_j a permuted block
+    auto apply_mma = [&](f32x4 (&c)[F][F], const bf16* Xb) {
+#pragma unroll
+        for (int sl = 0; sl < 4; ++sl) {
+            bf16x8 a[F], b[F];
+#pragma unroll
+            for (int i = 0; i < F; ++i) {
+                a[i] = frag(sB, sl, wm0 + i * 16);
+                b[i] = frag_x(Xb, sl, wn0 + i * 16);
             }
             static_for<0, F * F>([&](auto ij) { mma_ij(ij, c, a, b); });
         }
@@ -980,16 +1012,15 @@ __global__ __launch_bounds__(NTHR) void k_ns_small(SmallArgs A) {
         }
     };
 
-    const int64_t xt_stride = (int64_t)(np >> 4) * 512;   // one k-slice of X^T
     const bf16* x0 = (const bf16*)P.x[0];
     const float f = P.fold[0];
 
-    // A0 = X0 X0^T, one pass over X0 (block j of X0 is 32 KB contiguous)
+    // A0 = X0 X0^T, one pass over X0
     zero(accg);
-    dma_block(sX0, x0, 0, SLICE);
+    dma_block(sX0, x0, 0, false);
     auto gram0 = [&](int j, bf16* cur, bf16* nxt) {
         __syncthreads();   // block j landed; everyone is done with `nxt`
-        if (j + 1 < NB) dma_block(nxt, x0, (int64_t)(j + 1) * OPB, SLICE);
+        if (j + 1 < NB) dma_block(nxt, x0, j + 1, false);
         block_mma(accg, cur, cur);
     };
     for (int j = 0; j < NB; j += 2) {
@@ -999,23 +1030,19 @@ __global__ __launch_bounds__(NTHR) void k_ns_small(SmallArgs A) {
     __syncthreads();
     build_b(A.cb[0] * f * f * f, A.ca[0] * f);
 
-    // every step but the last: X'^T -> the other xt buffer, next B in sB; the
-    // X that the last apply reads goes to x[(ns_steps - 1) & 1] instead, in
-    // X's own layout
+    // every step but the last: X' from x[k&1] into x[(k+1)&1], next B in sB
+    // (the X of the last step is then in x[(ns_steps - 1) & 1])
     for (int k = 0; k + 1 < A.ns_steps; ++k) {
-        const bool final_x = k + 2 == A.ns_steps;
-        const bf16* xin = (const bf16*)((k & 1) ? P.xt[1] : P.xt[0]);
-        bf16* xout = (bf16*)((k & 1) ? P.xt[0] : P.xt[1]);
-        bf16* xfin = (bf16*)((k & 1) ? P.x[0] : P.x[1]);
+        const bf16* xin = (const bf16*)((k & 1) ? P.x[1] : P.x[0]);
+        bf16* xout = (bf16*)((k & 1) ? P.x[0] : P.x[1]);
         __syncthreads();   // B written by every wave
         zero(accg);
-        dma_block(sX0, xin, 0, xt_stride);
+        dma_block(sX0, xin, 0, true);
         auto step_block = [&](int j, bf16* cur, bf16* nxt) {
             __syncthreads();   // block j landed, the previous block's stores done; `nxt` and sG free
-            if (j + 1 < NB) dma_block(nxt, xin, (int64_t)(j + 1) * 4096, xt_stride);
-            const int c0 = j * M + wn0;   // first X column of this wave's part
+            if (j + 1 < NB) dma_block(nxt, xin, j + 1, true);
             zero(acc);
-            block_mma(acc, sB, cur);
+            apply_mma(acc, cur);
             mfma_drain();
 #pragma unroll
             for (int fm = 0; fm < F; ++fm) {
@@ -1024,21 +1051,11 @@ __global__ __launch_bounds__(NTHR) void k_ns_small(SmallArgs A) {
                 for (int fn = 0; fn < F; ++fn)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) av[fn][e] = agpr_read(acc[fm][fn][e]);
-                // row copy staged first, so that the swaps consume av in place
                 wave_lds_sync();
 #pragma unroll
                 for (int fn = 0; fn < F; ++fn)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) st[(4 * g4 + e) * SP + fn * 16 + l16] = av[fn][e];
-                if (!final_x) {
-#pragma unroll
-                    for (int fp = 0; fp < F; fp += 2) {
-                        float w[8];
-                        swap_pair(av, fp, w);
-                        const int col = c0 + (fp + (g4 & 1)) * 16 + l16, r0 = wm0 + fm * 16 + 8 * (g4 >> 1);
-                        store8<bf16>(xout + kb_off(col, r0, np), w);
-                    }
-                }
                 wave_lds_sync();
 #pragma unroll
                 for (int pass = 0; pass < PASSES; ++pass) {
@@ -1055,10 +1072,10 @@ __global__ __launch_bounds__(NTHR) void k_ns_small(SmallArgs A) {
                 }
             }
             __syncthreads();   // X'_j complete in sG
-            if (final_x) {
+            {
                 // sG is X'_j K-blocked with 128 rows, which is exactly the
                 // 32 KB run of X (mp = 128) holding columns 128j .. 128j+127
-                bf16* xd = xfin + (int64_t)j * OPB;
+                bf16* xd = xout + (int64_t)j * OPB;
 #pragma unroll
                 for (int i = 0; i < OPB / (NTHR * 8); ++i) {
                     const int o = (i * NTHR + tid) * 8;
