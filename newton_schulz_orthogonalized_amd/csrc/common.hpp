@@ -89,6 +89,19 @@ __device__ inline int xcd_remap(int wg, int grid) {
     if ((grid & 7) != 0) return wg;
     return (wg & 7) * (grid >> 3) + (wg >> 3);
 }
+// The same in windows: the grid is cut into windows of 8*W logical tiles and
+// XCD x receives the contiguous block [x*W, (x+1)*W) of each window (the last
+// window splits its remainder evenly), so the XCDs move through the logical
+// order together. For the Gram launches (long K, each tile reading two strips
+// of X) this keeps the X of only a few matrices in flight at a time.
+template <int W>
+__device__ inline int xcd_remap_window(int wg, int grid) {
+    if ((grid & 7) != 0) return wg;
+    const int x = wg & 7, n = wg >> 3, nper = grid >> 3;
+    const int base = (n / W) * W;
+    const int c = min(W, nper - base);
+    return base * 8 + x * c + (n - base);
+}
 
 // Element (r, k) of a K-blocked operand with R rows (R a multiple of 16, K a
 // multiple of 32): 1 KB blocks of 16 rows x 32 k, ordered panel-major (block
