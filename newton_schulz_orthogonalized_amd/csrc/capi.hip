@@ -116,8 +116,26 @@ struct Group {
     int tile;
     int first, count;  // range in the problem array
     bool fused;        // mp == 128 problems run by k_ns_small up to the last apply
+    int gram_window;   // GemmArgs::xcd_window of the Gram launches
     std::vector<int> gram_prefix, apply_prefix;
 };
+
+// Gram tiles go to the XCDs in windows of 64 per XCD when the group's work is
+// dominated by long K: there a tile's two strips of X (tile rows x K bf16)
+// exceed an XCD's 4 MB L2 well, tiles sharing a strip drift apart, and keeping
+// all XCDs on the same few matrices measured 2 % faster (K = 14336). With
+// strips up to about the L2 size (K = 2048 .. 8192) the plain contiguous split
+// measured 3.5 % faster. Windows are used when most of the Gram flops come
+// from problems with K >= 12288 (strips of 6 MB and more).
+int gram_window_for(const std::vector<ProbPlan>& probs, int first, int count) {
+    double all = 0, long_k = 0;
+    for (int i = first; i < first + count; ++i) {
+        const double m = probs[i].d.mp, k = probs[i].d.np;
+        all += m * m * k;
+        if (k >= 12288) long_k += m * m * k;
+    }
+    return (all > 0 && long_k > 0.5 * all) ? 64 : 0;
+}
 
 // Problems with mp == 128 go through the fused kernel (one workgroup per
 // problem, every step but the last in one launch) when a call has at least
@@ -223,6 +241,7 @@ void build_plan(const std::vector<Item>& items, int ns_dt, const std::vector<Coe
             if (pp.tile == t && is_fused(pp) == fused) pl.probs.push_back(pp);
         g.count = (int)pl.probs.size() - g.first;
         if (g.count == 0) continue;
+        g.gram_window = gram_window_for(pl.probs, g.first, g.count);
         g.gram_prefix.assign(1, 0);
         g.apply_prefix.assign(1, 0);
         for (int i = g.first; i < g.first + g.count; ++i) {
@@ -530,6 +549,7 @@ int run_pipeline(Plan& pl, char* ws, const mu_muon_hparams* hp, int src_dt, bool
             gg.prefix = gram_pf[gi];
             gg.total_tiles = g.gram_prefix.back();
             gg.first = first ? 1 : 0;
+            gg.xcd_window = g.gram_window;
             rc = timed_launch(MU_K_GRAM, gflops, 0.0, s, [&] { return launch(gg); }, "gram launch");
             if (rc) return rc;
             if (quint) {
@@ -538,6 +558,7 @@ int run_pipeline(Plan& pl, char* ws, const mu_muon_hparams* hp, int src_dt, bool
                 g2.prefix = gram_pf[gi];
                 g2.total_tiles = g.gram_prefix.back();
                 g2.first = first ? 1 : 0;
+                g2.xcd_window = g.gram_window;
                 rc = timed_launch(MU_K_GRAM2, g2flops, 0.0, s, [&] { return launch(g2); }, "gram2 launch");
                 if (rc) return rc;
             }

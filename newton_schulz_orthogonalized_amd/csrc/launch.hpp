@@ -55,6 +55,7 @@ struct GemmArgs {
     int use_b;           // quintic step: Gram writes A, the A^2 pass writes B, apply reads b
     int with_update;     // last step: 1 updates param, 0 writes out
     int src_dtype;       // element type of param/out
+    int xcd_window;      // Gram tiles per XCD per window of the tile order (0: contiguous split)
     float ca, cb, cc;    // step coefficients
     float lr, wd;
 };

@@ -542,9 +542,8 @@ __global__ __launch_bounds__(NTHR) void k_gemm_bf16(GemmArgs A) {
     __shared__ __attribute__((aligned(1024))) bf16 sB2[LS];
     __shared__ __attribute__((aligned(1024))) bf16 sB3[LS];
 
-    // Gram: 64-tile windows per XCD (measured best of 8 .. 256 and of the
-    // plain contiguous split, by 2 % on the 8B-shaped set); apply: contiguous
-    const int wg = SYM ? xcd_remap_window<64>(blockIdx.x, gridDim.x) : xcd_remap(blockIdx.x, gridDim.x);
+    // Gram: the window the host chose (xcd_window); apply: contiguous
+    const int wg = SYM ? xcd_remap_window(blockIdx.x, gridDim.x, A.xcd_window) : xcd_remap(blockIdx.x, gridDim.x);
     if (wg >= A.total_tiles) return;
     const int p = __builtin_amdgcn_readfirstlane(find_prob(A.prefix, A.nprobs, wg));
     const NsProb P = A.probs[p];   // by value: held in registers, never re-read after a store
