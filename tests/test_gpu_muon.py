@@ -207,6 +207,33 @@ def test_grouped_call_matches_separate_calls():
         assert torch.equal(o1[i], o2), i
 
 
+def test_long_k_gram_windows():
+    """A call dominated by long-K problems (K >= 12288), whose Gram tiles are
+    dealt to the XCDs in windows: parity with the oracle, ragged shapes and a
+    tall block included, and bitwise the same result as one call per matrix
+    (a tile's arithmetic does not depend on the order tiles run in)."""
+    shapes = [(1024, 12288), (12800, 512), (256, 16384), (300, 13000)]
+    print(f"[long-K Gram windows] shapes={shapes}", flush=True)
+    ins = [make_matrix_inputs(sh, 13500 + i, torch.bfloat16, 1e-3, 0.02, 1e-3) for i, sh in enumerate(shapes)]
+    host = [(to_np(w), to_np(g), to_np(m)) for w, g, m in ins]
+    kw = dict(lr=0.02, weight_decay=0.01, precision="bf16")
+    w1 = [w.clone() for w, _, _ in ins]
+    m1 = [m.clone() for _, _, m in ins]
+    o1 = [torch.zeros(sh, dtype=torch.float32, device="cuda") for sh in shapes]
+    nso().muon_step(w1, [g for _, g, _ in ins], m1, ortho_outs=o1, **kw)
+    torch.cuda.synchronize()
+    for i, sh in enumerate(shapes):
+        ref = O.muon_step_ref(*host[i], lr=0.02, weight_decay=0.01)
+        assert O.rel_fro(to_np(o1[i]), ref["o"]) <= BF16_TOL, sh
+        assert O.rel_fro(to_np(m1[i]), ref["m"]) <= MOM_TOL, sh
+        w, g, m = ins[i]
+        w2, m2 = w.clone(), m.clone()
+        o2 = torch.zeros(sh, dtype=torch.float32, device="cuda")
+        nso().muon_step([w2], [g], [m2], ortho_outs=[o2], **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(w1[i], w2) and torch.equal(o1[i], o2), sh
+
+
 def test_zero_gradient_and_momentum_decay_only():
     w = as_dtype(host_normal((256, 512), 13000, 0.02), torch.bfloat16).cuda()
     w0 = to_np(w)
