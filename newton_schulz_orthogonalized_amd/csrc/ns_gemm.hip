@@ -249,14 +249,17 @@ __device__ __forceinline__ void epilogue_mode(const GemmArgs& A, const NsProb& P
     // staged tall update: four 16-row strips per WT x 64 block, in two halves
     // of WT/2 rows (one slot array each)
     constexpr bool staged_tall = MODE == GM_APPLY_LAST && F % 4 == 0;
+    // staged wide update: four 16-row strips (64 rows x WT) at a time, rows
+    // 0..31 in `st` and 32..63 in `st2`
+    constexpr bool staged_wide = staged_tall;
     constexpr int WT = F * 16;
     constexpr int SP = WT + 4;
     constexpr int PASSES = WT / 32;            // row pass: 16 rows x 32 columns per pass
-    // The last apply's row passes instead give each parameter row LPR lanes
-    // of 8 columns (RPP whole rows of the strip per pass): a wave then reads
-    // and writes whole WT-wide runs of parameter rows, where 16 x 32 passes
-    // cut every row into 64-byte pieces (the update epilogue took 17.6 us per
-    // 256 x 256 tile that way, against 3.8 us for the plain apply's).
+    // The last apply's passes give each parameter row LPR lanes of 8 columns
+    // (RPP whole rows per pass): a wave then reads and writes whole WT-wide
+    // runs of parameter rows, where 16 x 32 passes cut every row into 64-byte
+    // pieces (the update epilogue took 17.6 us per 256 x 256 tile that way,
+    // against 3.8 us for the plain apply's).
     constexpr int LPR = WT / 8, RPP = 64 / LPR;
     const int lane = threadIdx.x & 63;
     const int g4 = lane >> 4, l16 = lane & 15;
@@ -268,7 +271,7 @@ __device__ __forceinline__ void epilogue_mode(const GemmArgs& A, const NsProb& P
     constexpr bool last = mode == GM_APPLY_LAST;
     // X'^T is kept only for the fp32 kernel; the bf16 apply reads X itself
     const bool trans_out = mirror || (!gram && !last && sizeof(TX) == 4) || (last && P.tall);
-    const bool row_out = !(last && P.tall);
+    const bool row_out = !(last && (P.tall || staged_wide));
     const int row_base = ti * TS_ + wm0, col_base = tj * TS_ + wn0;
 
     // Last apply with bf16 parameters: with one wave per SIMD nothing hides the
@@ -292,8 +295,8 @@ __device__ __forceinline__ void epilogue_mode(const GemmArgs& A, const NsProb& P
                 if (P.tall) {   // staged block (idx / (WT/8)), row group idx % (WT/8)
                     ur = br + (idx % (WT / 8)) * 8 + (lane >> 3);
                     uc0 = bc + (idx / (WT / 8)) * 64 + 8 * (lane & 7);
-                } else {        // strip idx / PASSES, pass idx % PASSES (row pass mapping below)
-                    ur = br + (idx / PASSES) * 16 + (idx % PASSES) * RPP + lane / LPR;
+                } else {        // staged half idx / LPR, pass idx % LPR
+                    ur = br + (idx / LPR) * 64 + (idx % LPR) * RPP + lane / LPR;
                     uc0 = bc + (lane % LPR) * 8;
                 }
                 const bf16* src = par + (int64_t)ur * P.ld + uc0;
@@ -354,6 +357,52 @@ __device__ __forceinline__ void epilogue_mode(const GemmArgs& A, const NsProb& P
             for (int fn = 0; fn < F; ++fn)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) st[(4 * g4 + e) * SP + fn * 16 + l16] = av[fn][e];
+        }
+        if constexpr (staged_wide) {
+            if (!P.tall) {
+                // strip fm -> rows (fm%4)*16 .. of the staged half; 4-float
+                // chunk k of row h sits at chunk k ^ 4((h/4)%4), so the four
+                // row groups of a write land in different banks
+#pragma unroll
+                for (int fn = 0; fn < F; ++fn)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int h = (fm & 3) * 16 + 4 * g4 + e, col = fn * 16 + l16;
+                        float* row = (h < 32 ? st : st2) + (h & 31) * WT;
+                        row[(((col >> 2) ^ (4 * g4)) << 2) | (col & 3)] = av[fn][e];
+                    }
+                if ((fm & 3) == 3) {
+                    wave_lds_sync();
+                    auto half_row = [&](int pass, float* v) {
+                        const int h = pass * RPP + lane / LPR, k = (lane % LPR) * 2;
+                        const float* row = (h < 32 ? st : st2) + (h & 31) * WT;
+                        const int sw = 4 * ((h >> 2) & 3);
+                        const f32x4 lo = *(const f32x4*)(row + ((k ^ sw) << 2));
+                        const f32x4 hi = *(const f32x4*)(row + (((k + 1) ^ sw) << 2));
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) { v[e] = lo[e]; v[4 + e] = hi[e]; }
+                    };
+                    const int ur0 = row_base + (fm >> 2) * 64, uc0 = col_base + (lane % LPR) * 8;
+                    if (fast) {
+                        if constexpr (pre_ok) {
+#pragma unroll
+                            for (int pass = 0; pass < LPR; ++pass) {
+                                float v[8];
+                                half_row(pass, v);
+                                update8_pre(A, P, ur0 + pass * RPP + lane / LPR, uc0, v, pre[(fm >> 2) * LPR + pass]);
+                            }
+                        }
+                    } else {
+#pragma clang loop unroll(disable)
+                        for (int pass = 0; pass < LPR; ++pass) {
+                            float v[8];
+                            half_row(pass, v);
+                            emit_u8<TS>(A, P, ur0 + pass * RPP + lane / LPR, uc0, v);
+                        }
+                    }
+                    wave_lds_sync();
+                }
+            }
         }
         if (trans_out) {
 #pragma unroll
