@@ -241,6 +241,10 @@ __device__ __forceinline__ void wave_lds_sync() { asm volatile("" ::: "memory");
 // chunk q of row c stored at chunk q ^ (c % 16), which keeps both the column
 // writes and the row reads free of bank conflicts) and then written back as
 // one 128-byte run of bf16 per parameter row.
+// A wide block's update is staged the same way, four strips (64 rows x F*16)
+// at a time in `st` and `st2`, and written back as whole F*16-wide runs of
+// parameter rows. Besides the long runs, staging puts four strips of work
+// between the load of the parameter values and their first use.
 // ---------------------------------------------------------------------------
 template <int MODE, typename TX, typename TS, int F>
 __device__ __forceinline__ void epilogue_mode(const GemmArgs& A, const NsProb& P, int ti, int tj, int TS_, int wm0,
@@ -255,11 +259,11 @@ __device__ __forceinline__ void epilogue_mode(const GemmArgs& A, const NsProb& P
     constexpr int WT = F * 16;
     constexpr int SP = WT + 4;
     constexpr int PASSES = WT / 32;            // row pass: 16 rows x 32 columns per pass
-    // The last apply's passes give each parameter row LPR lanes of 8 columns
-    // (RPP whole rows per pass): a wave then reads and writes whole WT-wide
-    // runs of parameter rows, where 16 x 32 passes cut every row into 64-byte
-    // pieces (the update epilogue took 17.6 us per 256 x 256 tile that way,
-    // against 3.8 us for the plain apply's).
+    // The last apply's update passes (the staged wide blocks, and the fp32
+    // kernel's row passes) give each parameter row LPR lanes of 8 columns,
+    // RPP whole rows per pass: a wave then reads and writes whole WT-wide
+    // runs of parameter rows, where 16 x 32 passes would cut every row into
+    // 64-byte pieces.
     constexpr int LPR = WT / 8, RPP = 64 / LPR;
     const int lane = threadIdx.x & 63;
     const int g4 = lane >> 4, l16 = lane & 15;
