@@ -96,10 +96,12 @@ __device__ __forceinline__ void upper_tile(int local, int T, int& ti, int& tj) {
     ti = tj = 0;   // not reached: local < T (T + 1) / 2
 }
 
-// Groups of four tile rows, column-major inside a group: 4 A panels and a
-// run of X panels are shared by the workgroups running together.
+// Groups of eight tile rows, column-major inside a group: 8 panels of B and a
+// run of X panels are shared by the workgroups running together (32 tiles of
+// an XCD: 8 B and 4 X panels). Same-box sweep on the 8B-shaped set, apply ms
+// per launch: groups of 2: 45.4, 4: 42.0, 6: 41.9, 8: 41.4, 12: 42.3, 16: 45.0.
 __device__ __forceinline__ void apply_tile(int local, int TM, int TN, int& ti, int& tj) {
-    constexpr int G = 4;
+    constexpr int G = 8;
     const int per_group = G * TN;
     const int g = local / per_group;
     const int w = local - g * per_group;
