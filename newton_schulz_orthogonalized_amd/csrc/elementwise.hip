@@ -159,7 +159,8 @@ __global__ __launch_bounds__(NTHR) void k_prep(PrepArgs A) {
     constexpr int RSTEP = NTHR / TPR;    // rows between a thread's rows
     __shared__ float tile[TR][TC + 1];
     __shared__ float red[4];
-    const int t = blockIdx.x;
+    const int t = xcd_remap(blockIdx.x, gridDim.x);   // each XCD streams one contiguous run of tiles
+    if (t >= A.total_tiles) return;
     const int p = __builtin_amdgcn_readfirstlane(find_prob(A.prefix, A.nprobs, t));
     const NsProb P = A.probs[p];   // by value: held in registers, never re-read after a store
     const int local = t - A.prefix[p];
@@ -280,7 +281,8 @@ template <typename TS, typename TX>
 __global__ __launch_bounds__(NTHR) void k_finish(FinishArgs A) {
     constexpr int TR = prep_rows<TX>(), TC = prep_cols<TX>();
     constexpr int TPR = TC / 4, RSTEP = NTHR / TPR;
-    const int t = blockIdx.x;
+    const int t = xcd_remap(blockIdx.x, gridDim.x);
+    if (t >= A.total_tiles) return;
     const int p = __builtin_amdgcn_readfirstlane(find_prob(A.prefix, A.nprobs, t));
     const NsProb P = A.probs[p];   // by value: held in registers, never re-read after a store
     const int local = t - A.prefix[p];
@@ -445,7 +447,8 @@ __device__ __forceinline__ void adamw_chunk_bf16(const AdamWDesc& D, int64_t bas
 }
 
 __global__ __launch_bounds__(NTHR) void k_adamw(AdamWArgs A) {
-    const int64_t c = blockIdx.x;
+    const int64_t c = xcd_remap(blockIdx.x, gridDim.x);   // each XCD streams one contiguous run of chunks
+    if (c >= A.total_chunks) return;
     const int i = __builtin_amdgcn_readfirstlane(find_tensor(A.prefix, A.n, c));
     const AdamWDesc D = A.descs[i];   // by value: held in registers, never re-read after a store
     const int64_t base = (c - A.prefix[i]) * ADAMW_CHUNK;
@@ -500,7 +503,8 @@ __global__ __launch_bounds__(NTHR) void k_table(const u32x4* src, u32x4* dst, in
 }
 
 __global__ __launch_bounds__(NTHR) void k_qkclip(QkArgs A) {
-    const int64_t c = blockIdx.x;
+    const int64_t c = xcd_remap(blockIdx.x, gridDim.x);
+    if (c >= A.total_chunks) return;
     const int i = __builtin_amdgcn_readfirstlane(find_tensor(A.prefix, A.n, c));
     const QkSeg S = A.segs[i];   // by value: held in registers, never re-read after a store
     const int64_t base = (c - A.prefix[i]) * QK_CHUNK;
@@ -532,9 +536,15 @@ hipError_t launch_table_copy(const void* src, void* dst, size_t bytes, hipStream
     return hipGetLastError();
 }
 
+// Grids of the streaming kernels are rounded up to a multiple of 8 (the
+// extra workgroups exit at once) so that xcd_remap gives every XCD one
+// contiguous run of tiles or chunks: prep measured 9 % faster that way than
+// with consecutive workgroups spread round-robin over the XCDs.
+inline unsigned grid8(int64_t n) { return (unsigned)((n + 7) / 8 * 8); }
+
 hipError_t launch_prep(const PrepArgs& a, hipStream_t s) {
     if (a.total_tiles <= 0) return hipSuccess;
-    dim3 grid(a.total_tiles), block(NTHR);
+    dim3 grid(grid8(a.total_tiles)), block(NTHR);
     if (a.src_dtype == DT_BF16) {
         if (a.ns_dtype == DT_BF16) hipLaunchKernelGGL((k_prep<bf16, bf16>), grid, block, 0, s, a);
         else hipLaunchKernelGGL((k_prep<bf16, float>), grid, block, 0, s, a);
@@ -553,7 +563,7 @@ hipError_t launch_norm(const NormArgs& a, hipStream_t s) {
 
 hipError_t launch_finish(const FinishArgs& a, hipStream_t s) {
     if (a.total_tiles <= 0) return hipSuccess;
-    dim3 grid(a.total_tiles), block(NTHR);
+    dim3 grid(grid8(a.total_tiles)), block(NTHR);
     if (a.src_dtype == DT_BF16) {
         if (a.ns_dtype == DT_BF16) hipLaunchKernelGGL((k_finish<bf16, bf16>), grid, block, 0, s, a);
         else hipLaunchKernelGGL((k_finish<bf16, float>), grid, block, 0, s, a);
@@ -566,13 +576,13 @@ hipError_t launch_finish(const FinishArgs& a, hipStream_t s) {
 
 hipError_t launch_adamw(const AdamWArgs& a, hipStream_t s) {
     if (a.total_chunks <= 0) return hipSuccess;
-    hipLaunchKernelGGL(k_adamw, dim3((unsigned)a.total_chunks), dim3(NTHR), 0, s, a);
+    hipLaunchKernelGGL(k_adamw, dim3(grid8(a.total_chunks)), dim3(NTHR), 0, s, a);
     return hipGetLastError();
 }
 
 hipError_t launch_qkclip(const QkArgs& a, hipStream_t s) {
     if (a.total_chunks <= 0) return hipSuccess;
-    hipLaunchKernelGGL(k_qkclip, dim3((unsigned)a.total_chunks), dim3(NTHR), 0, s, a);
+    hipLaunchKernelGGL(k_qkclip, dim3(grid8(a.total_chunks)), dim3(NTHR), 0, s, a);
     return hipGetLastError();
 }
 
