@@ -1172,12 +1172,14 @@ __global__ __launch_bounds__(NTHR) void k_ns_small(SmallArgs A) {
             __syncthreads();   // X'_j complete in sG
             {
                 // sG is X'_j K-blocked with 128 rows, which is exactly the
-                // 32 KB run of X (mp = 128) holding columns 128j .. 128j+127
+                // 32 KB run of X (mp = 128) holding columns 128j .. 128j+127;
+                // stored non-temporally (read back only by the next step):
+                // 2.5 % faster on the per-head set
                 bf16* xd = xout + (int64_t)j * OPB;
 #pragma unroll
                 for (int i = 0; i < OPB / (NTHR * 8); ++i) {
                     const int o = (i * NTHR + tid) * 8;
-                    *gp((bf16x8*)(xd + o)) = *(const bf16x8*)(sG + o);
+                    __builtin_nontemporal_store(*(const bf16x8*)(sG + o), gp((bf16x8*)(xd + o)));
                 }
             }
             block_mma(accg, sG, sG);
