@@ -299,7 +299,10 @@ __device__ __forceinline__ void epilogue_mode(const GemmArgs& A, const NsProb& P
     const float f = gram && A.first ? P.fold[0] : 1.f;   // the apply takes it through B
     const bool diag = gram && ti == tj;
     if (diag && wm0 > wn0) return;   // below the diagonal: written by the mirror of the quadrant above
-    const bool mirror = gram && (ti != tj || wm0 < wn0);
+    // a wave block on the diagonal holds only its fragments on or above the
+    // diagonal (fm <= fn); the others are written as their mirrors
+    const bool tri = diag && wm0 == wn0;
+    const bool mirror = gram && (ti != tj || wm0 < wn0 || tri);
     constexpr bool last = mode == GM_APPLY_LAST;
     // X'^T is kept only for the fp32 kernel; the bf16 apply reads X itself
     const bool trans_out = mirror || (!gram && !last && sizeof(TX) == 4) || (last && P.tall);
@@ -439,6 +442,7 @@ __device__ __forceinline__ void epilogue_mode(const GemmArgs& A, const NsProb& P
         if (trans_out) {
 #pragma unroll
             for (int fp = 0; fp < F; fp += 2) {
+                if (tri && fp + 1 <= fm) continue;   // both fragments at or below the diagonal
                 float w[8];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -453,16 +457,20 @@ __device__ __forceinline__ void epilogue_mode(const GemmArgs& A, const NsProb& P
                 const int r0 = row_base + fm * 16 + 8 * (g4 >> 1);
                 float v[8];
                 if constexpr (gram) {
-                    if constexpr (mode == GM_GRAM2) {
-                        float a8[8];   // A[r0+e][c] = A[c][r0+e]
-                        load8<TX>(tdst((TX*)P.a, mp, mp, c, r0, fm, fp), a8);
+                    // on a diagonal wave block only the fragments above the
+                    // diagonal are mirrored (this lane's fragment: fp + (g4&1))
+                    if (!tri || fp + (g4 & 1) > fm) {
+                        if constexpr (mode == GM_GRAM2) {
+                            float a8[8];   // A[r0+e][c] = A[c][r0+e]
+                            load8<TX>(tdst((TX*)P.a, mp, mp, c, r0, fm, fp), a8);
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) v[e] = ga * a8[e] + gs * w[e];
-                    } else {
+                            for (int e = 0; e < 8; ++e) v[e] = ga * a8[e] + gs * w[e];
+                        } else {
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) v[e] = gs * w[e];
+                            for (int e = 0; e < 8; ++e) v[e] = gs * w[e];
+                        }
+                        store8<TX>(tdst(gdst, mp, mp, c, r0, fm, fp), v);
                     }
-                    store8<TX>(tdst(gdst, mp, mp, c, r0, fm, fp), v);
                 } else {
 #pragma unroll
                     for (int e = 0; e < 8; ++e) v[e] = w[e];
@@ -531,6 +539,9 @@ __device__ __forceinline__ void epilogue_mode(const GemmArgs& A, const NsProb& P
             }
             const int r = row_base + fm * 16 + rr, c = col_base + c8;
             if constexpr (gram) {
+                // a diagonal wave block stores its fragments on or above the
+                // diagonal only (this lane's fragment: c8 / 16)
+                if (tri && c8 / 16 < fm) continue;
                 if constexpr (mode == GM_GRAM2) {
                     float a8[8];
                     load8<TX>(rdst((TX*)P.a, mp, mp, r, c, fm, pass), a8);
@@ -799,7 +810,13 @@ __global__ __launch_bounds__(NTHR) void k_gemm_bf16(GemmArgs A) {
     auto mma = [&](auto idx, const bf16x8 (&af)[F], const bf16x8 (&bfv)[F]) { mma_acc(idx, acc, af, bfv); };
     auto step = [&](auto domma, auto st, int kt, const bf16x8 (&ac)[F], const bf16x8 (&bc)[F], bf16x8 (&an)[F],
                     bf16x8 (&bn)[F]) {
-        constexpr bool DO = decltype(domma)::value != 0;
+        constexpr int DM = decltype(domma)::value;
+        constexpr bool DO = DM != 0;
+        // one MFMA, or none for a fragment below the diagonal (DM == 2)
+        auto mmaw = [&](auto j) {
+            constexpr int idx = decltype(j)::value;
+            if constexpr (DM != 2 || idx / F <= idx % F) mma(j, ac, bc);
+        };
         constexpr int S = decltype(st)::value;
         using SN = Stage<(S + 1) % NS>;
         if constexpr (S == 0) {
@@ -808,7 +825,7 @@ __global__ __launch_bounds__(NTHR) void k_gemm_bf16(GemmArgs A) {
             asm volatile("s_nop 1");
             __builtin_amdgcn_sched_barrier(0);
         }
-        if constexpr (DO) static_for<0, HEAD * F>([&](auto j) { mma(j, ac, bc); });
+        if constexpr (DO) static_for<0, HEAD * F>([&](auto j) { mmaw(j); });
         __builtin_amdgcn_sched_barrier(0);
         MU_WAIT_VMCNT_LGKM0((NS - 2) * NDMA);
         __builtin_amdgcn_s_barrier();
@@ -821,7 +838,7 @@ __global__ __launch_bounds__(NTHR) void k_gemm_bf16(GemmArgs A) {
             if constexpr (DO) {
                 if constexpr (g < F) bn[g] = read_b(SN{}, g);
                 else an[g - F] = read_a(SN{}, g - F);
-                static_for<HEAD * F + g * NMB / G, HEAD * F + (g + 1) * NMB / G>([&](auto j) { mma(j, ac, bc); });
+                static_for<HEAD * F + g * NMB / G, HEAD * F + (g + 1) * NMB / G>([&](auto j) { mmaw(j); });
             }
             __builtin_amdgcn_sched_barrier(0);
         });
@@ -836,11 +853,13 @@ __global__ __launch_bounds__(NTHR) void k_gemm_bf16(GemmArgs A) {
     };
     // On a diagonal Gram tile the wave below the diagonal would compute the
     // transpose of the wave above it: it only keeps the loads and barriers
-    // going, and the epilogue of the wave above writes both quadrants. Under
-    // the power limit the saved MFMA work (3 % of the 8B-shaped Gram) gave
-    // 0.7 %.
+    // going, and the epilogue of the wave above writes both quadrants. The
+    // two waves on the diagonal compute only their fragments on or above it
+    // and mirror those. Under the power limit the saved MFMA work (3 % of the
+    // 8B-shaped Gram for the skipped quadrant) gave 0.7 %.
     if constexpr (SYM) {
         if (ti == tj && wm0 > wn0) kloop(Stage<0>{});
+        else if (ti == tj && wm0 == wn0) kloop(Stage<2>{});
         else kloop(Stage<1>{});
     } else {
         kloop(Stage<1>{});
