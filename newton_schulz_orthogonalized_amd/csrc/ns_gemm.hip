@@ -609,7 +609,8 @@ __device__ __forceinline__ void epilogue(const GemmArgs& A, const NsProb& P, int
 // row r at byte 16*(16c + r)): that is exactly the lane order of a 16x16x32
 // MFMA fragment, so a fragment read is one linear ds_read_b128 of a block
 // (lane l at byte 16*l, free of bank conflicts) and one direct load fills one
-// block.
+// block. The apply's right operand, X, is the exception: its blocks hold rows
+// of k, so its fragments come from two ds_read_b64_tr_b16 each (see read_b).
 //
 // Step kt (slot kt%NS holds slice kt, whose fragments are in registers; the
 // slices up to kt+NS-1 are in flight):
