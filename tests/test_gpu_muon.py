@@ -234,6 +234,22 @@ def test_long_k_gram_windows():
         assert torch.equal(w1[i], w2) and torch.equal(o1[i], o2), sh
 
 
+@pytest.mark.parametrize("shape", [(2560, 2816), (2816, 2560)])
+def test_gram_tile_blocks_with_a_partial_block(shape):
+    """m = 2560: 10 x 10 Gram tiles of 256, enumerated as one 8 x 8 block, a
+    partial 8 x 2 block and a 2 x 2 triangle, with diagonal tiles whose lower
+    parts are mirrored; wide and tall."""
+    print(f"[gram blocks] shape={shape}", flush=True)
+    w, g, m = make_matrix_inputs(shape, 14100, torch.bfloat16, 1e-3, 0.02, 1e-3)
+    w0, g0, m0 = to_np(w), to_np(g), to_np(m)
+    o = torch.zeros(shape, dtype=torch.float32, device="cuda")
+    nso().muon_step([w], [g], [m], lr=0.02, weight_decay=0.01, precision="bf16", ortho_outs=[o])
+    torch.cuda.synchronize()
+    ref = O.muon_step_ref(w0, g0, m0, lr=0.02, weight_decay=0.01)
+    assert O.rel_fro(to_np(o), ref["o"]) <= BF16_TOL
+    assert O.rel_fro(to_np(m), ref["m"]) <= MOM_TOL
+
+
 def test_zero_gradient_and_momentum_decay_only():
     w = as_dtype(host_normal((256, 512), 13000, 0.02), torch.bfloat16).cuda()
     w0 = to_np(w)
