@@ -120,3 +120,30 @@ def test_fused_matches_tiled_path_closely():
         o2[part] = op
     torch.cuda.synchronize()
     assert O.rel_fro(to_np(o1), to_np(o2)) <= 5e-3
+
+
+def test_fused_and_tiled_problems_in_one_call():
+    """A call holding a fused group (256 short heads) next to tiled problems
+    (a 256-tile block, a ragged 128-tile block, a tall one): the fused launch,
+    the tiled steps and the shared last-apply launches must not disturb each
+    other."""
+    import newton_schulz_orthogonalized_amd as nso
+    specs = [((32768, 512), 256), ((1024, 2048), 1), ((300, 77), 1), ((1536, 640), 2)]
+    print(f"[fused + tiled] {specs}", flush=True)
+    ws, gs, ms, oo, host = [], [], [], [], []
+    for i, (shape, heads) in enumerate(specs):
+        w, g, m = make_matrix_inputs(shape, 26000 + 10 * i, torch.bfloat16, 1e-3, 0.02, 1e-3)
+        host.append((to_np(w), to_np(g), to_np(m)))
+        ws.append(w); gs.append(g); ms.append(m)
+        oo.append(torch.zeros(shape, dtype=torch.float32, device="cuda"))
+    L = _lib()
+    L.mu_profile_enable(True)
+    nso.muon_step(ws, gs, ms, lr=0.02, weight_decay=0.01, heads=[h for _, h in specs], precision="bf16",
+                  ortho_outs=oo)
+    torch.cuda.synchronize()
+    L.mu_profile_enable(False)
+    assert L.mu_profile_read(L.MU_K_FUSED)["launches"] == 1
+    for i, (shape, heads) in enumerate(specs):
+        w0, g0, m0 = host[i]
+        ref = O.muon_step_ref(w0, g0, m0, lr=0.02, weight_decay=0.01, heads=heads)
+        _check(shape, heads, w0, to_np(ws[i]), to_np(ms[i]), to_np(oo[i]), ref)
