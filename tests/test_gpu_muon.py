@@ -234,6 +234,23 @@ def test_long_k_gram_windows():
         assert torch.equal(w1[i], w2) and torch.equal(o1[i], o2), sh
 
 
+def test_long_k_quintic_steps():
+    """Quintic steps (the A^2 pass) on a call dominated by long K, so both
+    Gram passes run with windowed tile order and mirrored diagonal tiles."""
+    shapes = [(512, 12800), (12544, 768)]
+    coeffs = [(3.4445, -4.775, 2.0315)] * 5
+    print(f"[long-K quintic] shapes={shapes}", flush=True)
+    ins = [make_matrix_inputs(sh, 13700 + i, torch.bfloat16, 1e-3, 0.02, 1e-3) for i, sh in enumerate(shapes)]
+    host = [(to_np(w), to_np(g), to_np(m)) for w, g, m in ins]
+    oo = [torch.zeros(sh, dtype=torch.float32, device="cuda") for sh in shapes]
+    nso().muon_step([w for w, _, _ in ins], [g for _, g, _ in ins], [m for _, _, m in ins], lr=0.02,
+                    weight_decay=0.01, coeffs=coeffs, precision="bf16", ortho_outs=oo)
+    torch.cuda.synchronize()
+    for i, sh in enumerate(shapes):
+        ref = O.muon_step_ref(*host[i], lr=0.02, weight_decay=0.01, coeffs=coeffs)
+        assert O.rel_fro(to_np(oo[i]), ref["o"]) <= BF16_TOL, sh
+
+
 @pytest.mark.parametrize("shape", [(2560, 2816), (2816, 2560)])
 def test_gram_tile_blocks_with_a_partial_block(shape):
     """m = 2560: 10 x 10 Gram tiles of 256, enumerated as one 8 x 8 block, a
