@@ -117,24 +117,32 @@ struct Group {
     int first, count;  // range in the problem array
     bool fused;        // mp == 128 problems run by k_ns_small up to the last apply
     int gram_window;   // GemmArgs::xcd_window of the Gram launches
+    std::vector<int> gram_order;   // group-local problem index at each Gram prefix position
     std::vector<int> gram_prefix, apply_prefix;
 };
 
-// Gram tiles go to the XCDs in windows of 64 per XCD when the group's work is
-// dominated by long K: there a tile's two strips of X (tile rows x K bf16)
-// exceed an XCD's 4 MB L2 well, tiles sharing a strip drift apart, and keeping
-// all XCDs on the same few matrices measured 2 % faster (K = 14336). With
-// strips up to about the L2 size (K = 2048 .. 8192) the plain contiguous split
-// measured 3.5 % faster. Windows are used when most of the Gram flops come
-// from problems with K >= 12288 (strips of 6 MB and more).
-int gram_window_for(const std::vector<ProbPlan>& probs, int first, int count) {
+// Gram tile order and XCD windows. The Gram launches walk a group's problems
+// in order of falling K (np), then falling m (gram_order; the apply keeps the
+// table order), and hand the tile order to the XCDs in windows, so that all
+// XCDs work on problems of the same K at a time and the long ones start first.
+// Window per XCD: 64 when most of the Gram flops come from K >= 12288 (a
+// tile's two strips of X, 6 MB and more, exceed an XCD's 4 MB L2, and tiles
+// sharing a strip must stay close), 4 for launches of under four tiles per
+// CU, 8 otherwise. Same-box ms per Gram launch, table order with the plain
+// contiguous split (windows of 64 on the 8B set) against this scheme:
+// Llama-3-8B-shaped 21.56 -> 20.61, Llama-1B-shaped 2.00 -> 1.92 (windows of
+// 8; the contiguous split on the sorted order: 3.76), GPT-2-small-shaped
+// 0.101 -> 0.081 (windows of 4; of 8: 0.094).
+constexpr int GW_SMALL = 4, GW_MID = 8;
+int gram_window_for(const std::vector<ProbPlan>& probs, int first, int count, int tiles) {
     double all = 0, long_k = 0;
     for (int i = first; i < first + count; ++i) {
         const double m = probs[i].d.mp, k = probs[i].d.np;
         all += m * m * k;
         if (k >= 12288) long_k += m * m * k;
     }
-    return (all > 0 && long_k > 0.5 * all) ? 64 : 0;
+    if (all > 0 && long_k > 0.5 * all) return 64;
+    return tiles < 4 * 256 ? GW_SMALL : GW_MID;
 }
 
 // Problems with mp == 128 go through the fused kernel (one workgroup per
@@ -241,15 +249,24 @@ void build_plan(const std::vector<Item>& items, int ns_dt, const std::vector<Coe
             if (pp.tile == t && is_fused(pp) == fused) pl.probs.push_back(pp);
         g.count = (int)pl.probs.size() - g.first;
         if (g.count == 0) continue;
-        g.gram_window = gram_window_for(pl.probs, g.first, g.count);
+        g.gram_order.resize(g.count);
+        for (int i = 0; i < g.count; ++i) g.gram_order[i] = i;
+        std::stable_sort(g.gram_order.begin(), g.gram_order.end(), [&](int u, int v) {
+            const NsProb& a = pl.probs[g.first + u].d;
+            const NsProb& b = pl.probs[g.first + v].d;
+            return a.np != b.np ? a.np > b.np : a.mp > b.mp;
+        });
         g.gram_prefix.assign(1, 0);
         g.apply_prefix.assign(1, 0);
-        for (int i = g.first; i < g.first + g.count; ++i) {
-            const NsProb& d = pl.probs[i].d;
+        for (int i = 0; i < g.count; ++i) {
+            const NsProb& dg = pl.probs[g.first + g.gram_order[i]].d;
+            const int Tg = dg.mp / t;
+            g.gram_prefix.push_back(g.gram_prefix.back() + Tg * (Tg + 1) / 2);
+            const NsProb& d = pl.probs[g.first + i].d;
             const int T = d.mp / t;
-            g.gram_prefix.push_back(g.gram_prefix.back() + T * (T + 1) / 2);
             g.apply_prefix.push_back(g.apply_prefix.back() + T * (d.np / t));
         }
+        g.gram_window = gram_window_for(pl.probs, g.first, g.count, g.gram_prefix.back());
         pl.groups.push_back(std::move(g));
     }
     pl.prep_prefix.assign(1, 0);
@@ -266,7 +283,7 @@ void build_plan(const std::vector<Item>& items, int ns_dt, const std::vector<Coe
     pl.off_prep_prefix = o;
     o += sizeof(int) * (P + 1);
     pl.off_group_prefix = o;
-    for (auto& g : pl.groups) o += sizeof(int) * (g.gram_prefix.size() + g.apply_prefix.size());
+    for (auto& g : pl.groups) o += sizeof(int) * (g.gram_order.size() + g.gram_prefix.size() + g.apply_prefix.size());
     pl.table_bytes = o;
     o = align_up(o);
     pl.off_partials = o;
@@ -316,6 +333,8 @@ void carve(Plan& pl, char* ws, std::vector<char>& host_table) {
     std::memcpy(h + pl.off_prep_prefix, pl.prep_prefix.data(), sizeof(int) * pl.prep_prefix.size());
     size_t o2 = pl.off_group_prefix;
     for (auto& g : pl.groups) {
+        std::memcpy(h + o2, g.gram_order.data(), sizeof(int) * g.gram_order.size());
+        o2 += sizeof(int) * g.gram_order.size();
         std::memcpy(h + o2, g.gram_prefix.data(), sizeof(int) * g.gram_prefix.size());
         o2 += sizeof(int) * g.gram_prefix.size();
         std::memcpy(h + o2, g.apply_prefix.data(), sizeof(int) * g.apply_prefix.size());
@@ -473,10 +492,12 @@ int run_pipeline(Plan& pl, char* ws, const mu_muon_hparams* hp, int src_dt, bool
     }
 
     // group-level device pointers
-    std::vector<const int*> gram_pf, apply_pf;
+    std::vector<const int*> gram_ord, gram_pf, apply_pf;
     {
         size_t o = pl.off_group_prefix;
         for (auto& g : pl.groups) {
+            gram_ord.push_back((const int*)(ws + o));
+            o += sizeof(int) * g.gram_order.size();
             gram_pf.push_back((const int*)(ws + o));
             o += sizeof(int) * g.gram_prefix.size();
             apply_pf.push_back((const int*)(ws + o));
@@ -547,6 +568,7 @@ int run_pipeline(Plan& pl, char* ws, const mu_muon_hparams* hp, int src_dt, bool
             GemmArgs gg = ga;
             gg.mode = GM_GRAM;
             gg.prefix = gram_pf[gi];
+            gg.order = gram_ord[gi];
             gg.total_tiles = g.gram_prefix.back();
             gg.first = first ? 1 : 0;
             gg.xcd_window = g.gram_window;
@@ -556,6 +578,7 @@ int run_pipeline(Plan& pl, char* ws, const mu_muon_hparams* hp, int src_dt, bool
                 GemmArgs g2 = ga;
                 g2.mode = GM_GRAM2;
                 g2.prefix = gram_pf[gi];
+                g2.order = gram_ord[gi];
                 g2.total_tiles = g.gram_prefix.back();
                 g2.first = first ? 1 : 0;
                 g2.xcd_window = g.gram_window;

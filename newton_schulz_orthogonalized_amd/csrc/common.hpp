@@ -92,9 +92,10 @@ __device__ inline int xcd_remap(int wg, int grid) {
 // The same in windows: the grid is cut into windows of 8*W logical tiles and
 // XCD x receives the contiguous block [x*W, (x+1)*W) of each window (the last
 // window splits its remainder evenly), so the XCDs move through the logical
-// order together. For Gram launches with a long K (each tile streaming two
-// strips of X larger than an XCD's L2) this keeps the X of only a few
-// matrices in flight at a time. W <= 0 is the plain contiguous split.
+// order together. The Gram launches use it over a tile order sorted by K, so
+// that the XCDs hold the X of only a few matrices of like K at a time (with
+// a long K each tile streams two strips of X larger than an XCD's L2). W <= 0
+// is the plain contiguous split.
 __device__ inline int xcd_remap_window(int wg, int grid, int W) {
     if (W <= 0) return xcd_remap(wg, grid);
     if ((grid & 7) != 0) return wg;

@@ -659,9 +659,10 @@ __global__ __launch_bounds__(NTHR) void k_gemm_bf16(GemmArgs A) {
     const int wg = SYM ? xcd_remap_window(blockIdx.x, gridDim.x, A.xcd_window)
                        : xcd_remap_window(blockIdx.x, gridDim.x, 256);
     if (wg >= A.total_tiles) return;
-    const int p = __builtin_amdgcn_readfirstlane(find_prob(A.prefix, A.nprobs, wg));
+    const int ps = __builtin_amdgcn_readfirstlane(find_prob(A.prefix, A.nprobs, wg));
+    const int p = A.order ? __builtin_amdgcn_readfirstlane(A.order[ps]) : ps;
     const NsProb P = A.probs[p];   // by value: held in registers, never re-read after a store
-    const int local = wg - A.prefix[p];
+    const int local = wg - A.prefix[ps];
     const int mode = A.mode;
     int ti, tj;
     if (SYM) upper_tile(local, P.mp / TS, ti, tj);
@@ -894,9 +895,10 @@ __global__ __launch_bounds__(NTHR) void k_gemm_f32(GemmArgs A) {
 
     const int wg = xcd_remap(blockIdx.x, gridDim.x);
     if (wg >= A.total_tiles) return;
-    const int p = __builtin_amdgcn_readfirstlane(find_prob(A.prefix, A.nprobs, wg));
+    const int ps = __builtin_amdgcn_readfirstlane(find_prob(A.prefix, A.nprobs, wg));
+    const int p = A.order ? __builtin_amdgcn_readfirstlane(A.order[ps]) : ps;
     const NsProb P = A.probs[p];   // by value: held in registers, never re-read after a store
-    const int local = wg - A.prefix[p];
+    const int local = wg - A.prefix[ps];
     const int mode = A.mode;
     int ti, tj;
     if (SYM) upper_tile(local, P.mp / TS, ti, tj);
