@@ -47,8 +47,8 @@ enum GemmMode : int {
 struct GemmArgs {
     const NsProb* probs;
     const int* prefix;   // nprobs+1 cumulative tiles for this mode
-    const int* order;    // Gram: problem at each prefix position (the tile order
-                         // runs through the problems in this order); null: identity
+    const int* order;    // problem at each prefix position (the tile order runs
+                         // through the problems in this order); null: identity
     int nprobs;
     int total_tiles;
     int mode;
