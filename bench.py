@@ -2,7 +2,7 @@
 """Benchmark of one optimizer step (Muon over every 2-D hidden weight + AdamW
 over the rest) on a transformer-shaped parameter set, on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--config llama_8b]
+    python bench.py [--steps K] [--warmup W] [--config llama_8b] [--coeffs cubic|quintic]
 
 A step is one mu_muon_step over the whole Muon list (momentum, normalisation,
 five Newton-Schulz steps, update) plus one mu_adamw_step over the whole AdamW
@@ -29,6 +29,14 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3        # MI355X fp32 matrix
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 
+# Per-step (a, b, c) of X <- a X + b (X X^T) X + c (X X^T)^2 X. cubic: the
+# Newton-Schulz step of the Muon pages, 1.5 X - 0.5 X X^T X. quintic: the
+# second-order Newton-Schulz iteration for the polar factor (the series of
+# (X^T X)^(-1/2) about I cut after the quadratic term: 15/8, -10/8, 3/8), which
+# exercises the A A^T pass of a quintic step with coefficients of known
+# convergence; the pages name tuned quintic schedules but print no values.
+COEFF_SCHEDULES = {"cubic": (1.5, -0.5, 0.0), "quintic": (1.875, -1.25, 0.375)}
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -37,6 +45,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="llama_8b")
     ap.add_argument("--ns-steps", type=int, default=5)
+    ap.add_argument("--coeffs", default="cubic", choices=sorted(COEFF_SCHEDULES),
+                    help="Newton-Schulz polynomial of every step")
     ap.add_argument("--precision", default="bf16", choices=["bf16", "f32"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceilings", action="store_true", help="skip the copy / library-GEMM ceiling measurement")
@@ -166,7 +176,7 @@ def build_set(ps, set_index, device, torch):
     return mu, aw
 
 
-def cpu_baseline(ps, set_index, ns_steps):
+def cpu_baseline(ps, set_index, ns_steps, coeffs):
     """The CPU oracle, as it stands, on a bounded sample of the same workload,
     scaled to one whole parameter set by algorithmic work."""
     import numpy as np
@@ -189,7 +199,7 @@ def cpu_baseline(ps, set_index, ns_steps):
         g = host_normal(e.shape, 778 + k, ps.grad_std)
         m = host_normal(e.shape, 779 + k, ps.mom_std)
         t0 = time.perf_counter()
-        O.muon_step_ref(w, g, m, lr=0.02, weight_decay=0.01, heads=e.heads, coeffs=O.default_coeffs(ns_steps))
+        O.muon_step_ref(w, g, m, lr=0.02, weight_decay=0.01, heads=e.heads, coeffs=coeffs)
         t_muon += time.perf_counter() - t0
         picked.append(e)
     sample = ParamSet("sample", [MuonEntry(e.name, e.shape, e.heads) for e in picked])
@@ -201,7 +211,8 @@ def cpu_baseline(ps, set_index, ns_steps):
         t0 = time.perf_counter()
         O.adamw_ref(p, g, z, z, lr=0.02, weight_decay=0.01, beta1=0.9, beta2=0.95, eps=1e-8, step=1)
         t_aw = time.perf_counter() - t0
-    muon_scale = ps.ns_flops(ns_steps) / sample.ns_flops(ns_steps)
+    nq = sum(1 for c in coeffs if c[2] != 0.0)
+    muon_scale = ps.ns_flops(ns_steps, nq) / sample.ns_flops(ns_steps, nq)
     aw_scale = ps.adamw_elems() / n_aw if ps.adamw else 0.0
     est_ms = 1e3 * (t_muon * muon_scale + t_aw * aw_scale)
     counts = {}
@@ -238,8 +249,9 @@ def main():
     print(f"[bench] building {args.config}: {len(ps.muon)} Muon matrices ({ps.muon_elems()} elems), "
           f"{len(ps.adamw)} AdamW tensors ({ps.adamw_elems()} elems)", file=sys.stderr, flush=True)
     mu, aw = build_set(ps, set_index, device, torch)
+    coeffs = [COEFF_SCHEDULES[args.coeffs]] * args.ns_steps
     ws_bytes = nso.muon_workspace_bytes(mu["p"], mu["g"], mu["m"], heads=mu["heads"], ns_steps=args.ns_steps,
-                                        precision=precision)
+                                        coeffs=coeffs, precision=precision)
     ws = _lib.workspace(ws_bytes, device)
     aw_ws = _lib.workspace(_lib.mu_adamw_workspace_size(len(aw["p"])), device)
     torch.cuda.synchronize()
@@ -261,7 +273,7 @@ def main():
     def step():
         state["t"] += 1
         nso.muon_step(mu["p"], mu["g"], mu["m"], lr=0.02, weight_decay=0.01, heads=mu["heads"],
-                      ns_steps=args.ns_steps, precision=precision, workspace=ws)
+                      ns_steps=args.ns_steps, coeffs=coeffs, precision=precision, workspace=ws)
         if aw["p"]:
             nso.adamw_step(aw["p"], aw["g"], aw["m"], aw["v"], lr=0.02, weight_decay=0.01, beta1=0.9,
                            beta2=0.95, eps=1e-8, step=state["t"], workspace=aw_ws)
@@ -312,9 +324,11 @@ def main():
         "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": False, "scaling": "weak",
         "vs_baseline": None, "dtype": precision, "data": "synthetic",
         "config": {"workload": f"{args.config}: Muon over {len(ps.muon)} matrices ({ps.muon_elems()} elements), "
-                               f"AdamW over {len(ps.adamw)} tensors ({ps.adamw_elems()} elements)",
+                               f"AdamW over {len(ps.adamw)} tensors ({ps.adamw_elems()} elements)"
+                               + ("" if args.coeffs == "cubic" else f"; {args.coeffs} Newton-Schulz steps"),
                    "muon_matrices": len(ps.muon), "adamw_tensors": len(ps.adamw),
-                   "ns_steps": args.ns_steps, "ns_precision": precision, "parallelism": "single-gpu"},
+                   "ns_steps": args.ns_steps, "ns_coeffs": list(COEFF_SCHEDULES[args.coeffs]),
+                   "ns_precision": precision, "parallelism": "single-gpu"},
         "muon_ms_per_step": sum(prof[k]["ms"] for k in ("prep", "norm", "gram", "gram2", "apply", "finish", "ns_fused")) / K,
         "adamw_ms_per_step": prof["adamw"]["ms"] / K,
         "ns_ms_per_step": ns_ms, "ns_tflops": ns_tflops, "ns_frac_peak": ns_tflops / peak,
@@ -328,7 +342,7 @@ def main():
         out["ceilings"] = measure_ceilings(torch, device)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(ps, set_index, args.ns_steps)
+        out["cpu_baseline"] = cpu_baseline(ps, set_index, args.ns_steps, coeffs)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

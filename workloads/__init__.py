@@ -55,14 +55,16 @@ class ParamSet:
     def adamw_elems(self) -> int:
         return sum(int(np.prod(e.shape)) for e in self.adamw)
 
-    def ns_flops(self, steps: int = 5) -> float:
+    def ns_flops(self, steps: int = 5, quintic_steps: int = 0) -> float:
         """Algorithmic Newton-Schulz flops: per step m(m+1)n (Gram, symmetric half)
-        + 2 m^2 n (apply) + 3 m n (axpy), with m <= n the sides of each head block."""
+        + 2 m^2 n (apply) + 3 m n (axpy), with m <= n the sides of each head block,
+        plus m(m+1)m (A A^T, symmetric half) on each of `quintic_steps` steps."""
         tot = 0.0
         for e in self.muon:
             r, c = e.shape[0] // e.heads, e.shape[1]
             m, n = min(r, c), max(r, c)
             tot += e.heads * steps * (m * (m + 1) * n + 2.0 * m * m * n + 3.0 * m * n)
+            tot += e.heads * quintic_steps * (m * (m + 1) * m)
         return tot
 
 
