@@ -38,6 +38,8 @@
 // f = 1/||U||_F (so the normalised X0 is never materialised); the last apply
 // writes the decoupled-weight-decay update W <- W - lr*wd*W - lr*scale*O
 // straight into the parameter.
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -347,6 +349,26 @@ __device__ __forceinline__ void epilogue_mode(const GemmArgs& A, const NsProb& P
     if (mode == GM_GRAM && !A.use_b) { gs = A.cb * f * f * f; gd = A.ca * f; }
     if (mode == GM_GRAM2) { gs = A.cc * f; gd = A.ca * f; ga = A.cb * f; }
     TX* gdst = (TX*)(mode == GM_GRAM2 ? P.b : P.a);
+    // A^2 pass: B = gd I + ga A + gs A A^T takes A over the whole block. The
+    // stored A is exactly symmetric (the Gram writes both triangles from the
+    // same values), so the four accumulator rows r .. r+3 of a lane's column
+    // c are read as A[c][r .. r+3]: four consecutive k of operand row c, one
+    // 8-byte piece (16 for fp32). All of them are loaded here, before the
+    // strip loop: loaded next to their use, each waited behind the stores of
+    // the strip before it (the A^2 pass ran 12-23 % slower that way).
+    constexpr bool a2 = mode == GM_GRAM2;
+    typedef typename std::conditional<sizeof(TX) == 2, bf16x4, f32x4>::type A4;
+    A4 apre[a2 ? F : 1][a2 ? F : 1];
+    if constexpr (a2) {
+        const TX* ab = (const TX*)P.a;
+#pragma unroll
+        for (int fm = 0; fm < F; ++fm)
+#pragma unroll
+            for (int fn = 0; fn < F; ++fn) {
+                const int c = col_base + fn * 16 + l16, r = row_base + fm * 16 + 4 * g4;
+                apre[fm][fn] = *gp((const A4*)(ab + op_off<TX>(c, r, P.mp, P.mp)));
+            }
+    }
     TX* xdst = (TX*)(A.src ? P.x[0] : P.x[1]);
     TX* xtdst = (TX*)(A.src ? P.xt[0] : P.xt[1]);
     // Where this lane's run of 8 goes in a workspace operand with R rows and
@@ -384,6 +406,16 @@ __device__ __forceinline__ void epilogue_mode(const GemmArgs& A, const NsProb& P
         for (int fn = 0; fn < F; ++fn)
 #pragma unroll
             for (int e = 0; e < 4; ++e) av[fn][e] = agpr_read(acc[fm][fn][e]);
+        if constexpr (a2) {
+            // B's values, in the accumulator layout (rows 4*g4 + e, column l16)
+#pragma unroll
+            for (int fn = 0; fn < F; ++fn)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    av[fn][e] = gs * av[fn][e] + ga * (float)apre[fm][fn][e];
+                    if (diag && row_base + fm * 16 + 4 * g4 + e == col_base + fn * 16 + l16) av[fn][e] += gd;
+                }
+        }
         // the row-major copy is staged first: the swaps below then consume
         // the accumulator values in place instead of copying them
         if (row_out) {
@@ -460,15 +492,10 @@ __device__ __forceinline__ void epilogue_mode(const GemmArgs& A, const NsProb& P
                     // on a diagonal wave block only the fragments above the
                     // diagonal are mirrored (this lane's fragment: fp + (g4&1))
                     if (!tri || fp + (g4 & 1) > fm) {
-                        if constexpr (mode == GM_GRAM2) {
-                            float a8[8];   // A[r0+e][c] = A[c][r0+e]
-                            load8<TX>(tdst((TX*)P.a, mp, mp, c, r0, fm, fp), a8);
+                        // (the A^2 pass has B's values in w already; B is
+                        // symmetric, so they are the mirrored ones too)
 #pragma unroll
-                            for (int e = 0; e < 8; ++e) v[e] = ga * a8[e] + gs * w[e];
-                        } else {
-#pragma unroll
-                            for (int e = 0; e < 8; ++e) v[e] = gs * w[e];
-                        }
+                        for (int e = 0; e < 8; ++e) v[e] = a2 ? w[e] : gs * w[e];
                         store8<TX>(tdst(gdst, mp, mp, c, r0, fm, fp), v);
                     }
                 } else {
@@ -542,19 +569,14 @@ __device__ __forceinline__ void epilogue_mode(const GemmArgs& A, const NsProb& P
                 // a diagonal wave block stores its fragments on or above the
                 // diagonal only (this lane's fragment: c8 / 16)
                 if (tri && c8 / 16 < fm) continue;
-                if constexpr (mode == GM_GRAM2) {
-                    float a8[8];
-                    load8<TX>(rdst((TX*)P.a, mp, mp, r, c, fm, pass), a8);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) v[e] = ga * a8[e] + gs * v[e];
-                } else {
+                if constexpr (!a2) {   // (the A^2 pass staged B's values)
 #pragma unroll
                     for (int e = 0; e < 8; ++e) v[e] *= gs;
-                }
-                if (diag) {
+                    if (diag) {
 #pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        if (r == c + e) v[e] += gd;
+                        for (int e = 0; e < 8; ++e)
+                            if (r == c + e) v[e] += gd;
+                    }
                 }
                 store8<TX>(rdst(gdst, mp, mp, r, c, fm, pass), v);
             } else {
