@@ -200,18 +200,6 @@ __device__ __forceinline__ void update8_pre(const GemmArgs& A, const NsProb& P, 
 }
 
 template <typename TX>
-__device__ __forceinline__ void load8(const TX* p, float* v) {
-    if constexpr (sizeof(TX) == 2) {
-        bf16x8 q = *gp((const bf16x8*)p);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = (float)q[e];
-    } else {
-        f32x4 a = gp((const f32x4*)p)[0], b = gp((const f32x4*)p)[1];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) { v[e] = a[e]; v[e + 4] = b[e]; }
-    }
-}
-template <typename TX>
 __device__ __forceinline__ void store8(TX* p, const float* v) {
     if constexpr (sizeof(TX) == 2) {
         bf16x8 q;
