@@ -36,12 +36,27 @@ SAMPLES = {
 }
 
 
+# quintic steps as `bench.py --coeffs quintic` runs them: the second-order
+# Newton-Schulz polynomial for the polar factor, five times
+QUINTIC = [(1.875, -1.25, 0.375)] * 5
+
+
 @pytest.mark.parametrize("set_name", ["gpt2_small", "per_head_wq", "llama_1b", "llama_8b"])
 def test_full_set_muon_step(set_name):
+    _full_set_muon_step(set_name, None)
+
+
+@pytest.mark.parametrize("set_name", ["llama_1b", "llama_8b"])
+def test_full_set_muon_step_quintic(set_name):
+    _full_set_muon_step(set_name, QUINTIC)
+
+
+def _full_set_muon_step(set_name, coeffs):
     import newton_schulz_orthogonalized_amd as nso
     idx = list(PARAM_SETS).index(set_name)
     ps = PARAM_SETS[set_name]()
-    print(f"[fullsize muon] {set_name}: {len(ps.muon)} matrices, {ps.muon_elems()} elements", flush=True)
+    print(f"[fullsize muon] {set_name}: {len(ps.muon)} matrices, {ps.muon_elems()} elements, "
+          f"{'cubic' if coeffs is None else 'quintic'} steps", flush=True)
     dt = torch.bfloat16
     ws, gs, ms, oo, keep = [], [], [], [], {}
     for j, e in enumerate(ps.muon):
@@ -54,12 +69,13 @@ def test_full_set_muon_step(set_name):
             keep[j] = (to_np(w), to_np(g), to_np(m))
             o = torch.zeros(e.shape, dtype=torch.float32, device="cuda")
         ws.append(w); gs.append(g); ms.append(m); oo.append(o)
-    nso.muon_step(ws, gs, ms, lr=0.02, weight_decay=0.01, heads=[e.heads for e in ps.muon], ortho_outs=oo)
+    nso.muon_step(ws, gs, ms, lr=0.02, weight_decay=0.01, heads=[e.heads for e in ps.muon], ortho_outs=oo,
+                  coeffs=coeffs)
     torch.cuda.synchronize()
     for j, (w0, g0, m0) in keep.items():
         e = ps.muon[j]
         print(f"  oracle for {e.name} {e.shape} heads={e.heads}", flush=True)
-        ref = O.muon_step_ref(w0, g0, m0, lr=0.02, weight_decay=0.01, heads=e.heads)
+        ref = O.muon_step_ref(w0, g0, m0, lr=0.02, weight_decay=0.01, heads=e.heads, coeffs=coeffs)
         o = to_np(oo[j])
         assert O.rel_fro(o, ref["o"]) <= BF16_TOL, e.name
         assert O.rel_fro(to_np(ms[j]), ref["m"]) <= MOM_TOL, e.name
