@@ -139,6 +139,7 @@ struct Group {
 // 8; the contiguous split on the sorted order: 3.76), GPT-2-small-shaped
 // 0.101 -> 0.081 (windows of 4; of 8: 0.094).
 constexpr int GW_SMALL = 4, GW_MID = 8;
+constexpr int MI355X_CUS = 256;   // compute units of the one chip this library targets
 int gram_window_for(const std::vector<ProbPlan>& probs, int first, int count, int tiles) {
     double all = 0, long_k = 0;
     for (int i = first; i < first + count; ++i) {
@@ -147,7 +148,7 @@ int gram_window_for(const std::vector<ProbPlan>& probs, int first, int count, in
         if (k >= 12288) long_k += m * m * k;
     }
     if (all > 0 && long_k > 0.5 * all) return 64;
-    return tiles < 4 * 256 ? GW_SMALL : GW_MID;
+    return tiles < 4 * MI355X_CUS ? GW_SMALL : GW_MID;
 }
 
 // Problems with mp == 128 go through the fused kernel (one workgroup per
