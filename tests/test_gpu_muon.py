@@ -267,6 +267,20 @@ def test_gram_tile_blocks_with_a_partial_block(shape):
     assert O.rel_fro(to_np(m), ref["m"]) <= MOM_TOL
 
 
+@pytest.mark.parametrize("shape", [(256, 1 << 21), (1 << 21, 128)])
+def test_longest_side_at_the_limit(shape):
+    """A long side of 2^21, the largest the C ABI accepts: a wide block on the
+    256-row tiles and a tall one on the 128-row tiles, each streaming one K
+    of 2^21 through every Gram tile."""
+    print(f"[longest side] shape={shape}", flush=True)
+    w0, w1, m1, o, norms, ref = _step_case(shape, torch.bfloat16, "bf16", 9900, gstd=1e-3, wstd=0.02, mstd=1e-3)
+    assert O.rel_fro(m1, ref["m"]) <= MOM_TOL
+    assert O.rel_fro(o, ref["o"]) <= BF16_TOL
+    assert abs(norms[0] - ref["norms"][0]) <= 1e-4 * ref["norms"][0]
+    want = w0 - 0.02 * 0.01 * w0 - 0.02 * o
+    assert np.all(np.abs(w1 - want) <= bf16_ulp(want) * 0.5 + 8 * 2.0 ** -24 * (np.abs(w0) + 0.02 * np.abs(o)))
+
+
 def test_zero_gradient_and_momentum_decay_only():
     w = as_dtype(host_normal((256, 512), 13000, 0.02), torch.bfloat16).cuda()
     w0 = to_np(w)
