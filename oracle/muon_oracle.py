@@ -127,9 +127,16 @@ def momentum_ref(grad, momentum, mu: float = DEFAULT_MU, nesterov: bool = True):
 
 
 def frobenius_normalize_ref(block, eps: float = DEFAULT_NORM_EPS):
-    """X0 = B / (||B||_F + eps). Returns (X0, ||B||_F)."""
+    """X0 = B / (||B||_F + eps). Returns (X0, ||B||_F).
+
+    B = 0 gives X0 = 0 for every eps, eps = 0 included (a reading: the zero
+    input has the zero direction, so the step only decays the weight; the
+    formula alone would give 0/0 there).
+    """
     b = np.asarray(block, dtype=np.float64)
     s = math.sqrt(float(np.sum(b * b)))
+    if s == 0.0:
+        return np.zeros_like(b), s
     return b / (s + eps), s
 
 

@@ -208,29 +208,101 @@ def test_heads_must_divide_rows():
 
 
 # --------------------------------------------------------------------------
-# Brute force on a tiny input: the page's cubic step with explicit loops
+# Exact arithmetic on tiny inputs: the iteration in rational numbers
 # --------------------------------------------------------------------------
 
-def _loop_matmul(a, b):
-    n, k = len(a), len(a[0])
-    m = len(b[0])
-    return [[sum(a[i][t] * b[t][j] for t in range(k)) for j in range(m)] for i in range(n)]
+def _exact_pipeline(x, norm, steps):
+    """X / norm, then each step X <- a X + b X X^T X + c X X^T X X^T X with every
+    entry written as its scalar sum over the inner indices, in Fractions."""
+    from fractions import Fraction as Fr
+    r, c = len(x), len(x[0])
+    cur = [[Fr(v) / norm for v in row] for row in x]
+    for a, b, q in steps:
+        a, b, q = Fr(a), Fr(b), Fr(q)
+        # G[i][l] = sum_k x_ik x_lk, then (G X)_ij and (G G X)_ij
+        g = [[sum(cur[i][k] * cur[l][k] for k in range(c)) for l in range(r)] for i in range(r)]
+        gx = [[sum(g[i][l] * cur[l][j] for l in range(r)) for j in range(c)] for i in range(r)]
+        ggx = [[sum(g[i][l] * gx[l][j] for l in range(r)) for j in range(c)] for i in range(r)]
+        cur = [[a * cur[i][j] + b * gx[i][j] + q * ggx[i][j] for j in range(c)] for i in range(r)]
+    return np.array([[float(v) for v in row] for row in cur])
 
 
-def _loop_transpose(a):
-    return [list(r) for r in zip(*a)]
+@pytest.mark.parametrize("x,norm", [([[1, 2, 2], [0, 4, 0]], 5), ([[2, 0], [1, 2], [0, 4]], 5),
+                                    ([[1, 1, 1, 1]], 2)])
+def test_exact_rational_cubic_iteration(x, norm):
+    """Inputs whose Frobenius norm is an integer, with eps = 0, so X0 is
+    rational and five cubic steps can be done exactly; the float64 pipeline
+    (tall inputs included) must agree to rounding."""
+    from fractions import Fraction as Fr
+    want = _exact_pipeline(x, norm, [(Fr(3, 2), Fr(-1, 2), 0)] * 5)
+    out, norms = O.orthogonalize_ref(np.array(x, dtype=np.float64), eps=0.0)
+    assert norms[0] == float(norm)
+    assert np.max(np.abs(out - want)) < 1e-15
 
 
-def test_brute_force_cubic_iteration_3x5():
-    x = _rng(12).standard_normal((3, 5))
-    s = math.sqrt(sum(v * v for v in x.reshape(-1)))
-    xl = [[v / (s + O.DEFAULT_NORM_EPS) for v in row] for row in x.tolist()]
-    for _ in range(5):
-        xtx = _loop_matmul(_loop_transpose(xl), xl)        # X^T X as printed
-        prod = _loop_matmul(xl, xtx)                       # X (X^T X)
-        xl = [[1.5 * xl[i][j] - 0.5 * prod[i][j] for j in range(5)] for i in range(3)]
-    out, _ = O.orthogonalize_ref(x)
-    assert np.max(np.abs(out - np.array(xl))) < 1e-14
+def test_exact_rational_mixed_coefficients():
+    from fractions import Fraction as Fr
+    steps = [(Fr(15, 8), Fr(-5, 4), Fr(3, 8)), (Fr(3, 2), Fr(-1, 2), 0), (Fr(2), Fr(-3, 2), Fr(1, 2))]
+    x = [[1, 2, 2], [0, 4, 0]]
+    want = _exact_pipeline(x, 5, steps)
+    out, _ = O.orthogonalize_ref(np.array(x, dtype=np.float64), coeffs=[tuple(map(float, t)) for t in steps],
+                                 eps=0.0)
+    assert np.max(np.abs(out - want)) < 1e-15
+
+
+# --------------------------------------------------------------------------
+# Extreme magnitudes and the zero input
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("c", [1e-25, 1e-35, 1e18, 1e30])
+def test_scale_invariance_at_extreme_magnitudes(c):
+    """With eps = 0 the iteration sees only U / ||U||_F, so a positive factor
+    drops out at either end of the float32 range."""
+    x = _rng(40).standard_normal((9, 21))
+    base, nb = O.orthogonalize_ref(x, eps=0.0)
+    out, ns = O.orthogonalize_ref(c * x, eps=0.0)
+    assert O.rel_fro(out, base) < 1e-13
+    assert abs(ns[0] / (c * nb[0]) - 1.0) < 1e-14
+
+
+@pytest.mark.parametrize("coeffs", [None, [(1.875, -1.25, 0.375), (1.5, -0.5, 0.0), (2.0, -1.5, 0.5)]])
+def test_input_far_below_eps_stays_linear(coeffs):
+    """||U||_F << eps: X0 = U / (||U||_F + eps) has singular values near 1e-18,
+    where a step multiplies X by a to within |b| s^2 ~ 1e-36 relative, so the
+    output is the product of the a_k times X0."""
+    x = _rng(41).standard_normal((9, 21)) * 1e-25
+    out, norms = O.orthogonalize_ref(x, coeffs=coeffs)
+    ks = O.default_coeffs() if coeffs is None else coeffs
+    gain = float(np.prod([k[0] for k in ks]))
+    x0 = x / (norms[0] + O.DEFAULT_NORM_EPS)
+    assert O.rel_fro(out, gain * x0) < 1e-14
+
+
+def test_zero_input_with_zero_eps_gives_zero_direction():
+    out, norms = O.orthogonalize_ref(np.zeros((3, 7)), eps=0.0)
+    assert np.all(out == 0.0) and norms[0] == 0.0
+    w = _rng(42).standard_normal((3, 7))
+    r = O.muon_step_ref(w, np.zeros((3, 7)), np.zeros((3, 7)), lr=0.1, weight_decay=0.5, eps=0.0)
+    assert np.all(r["o"] == 0.0)
+    assert np.allclose(r["w"], w * (1 - 0.05), rtol=0, atol=1e-15)
+
+
+# --------------------------------------------------------------------------
+# The parity measure itself
+# --------------------------------------------------------------------------
+
+def test_rel_fro_hand_values():
+    # ||x - ref||_F / ||ref||_F: a difference of 1 against sqrt(1 + 4 + 9 + 25)
+    assert abs(O.rel_fro([[1, 2], [3, 4]], [[1, 2], [3, 5]]) - 1 / math.sqrt(39)) < 1e-16
+    # the denominator is the reference's norm, not the candidate's
+    assert O.rel_fro([6.0, 8.0], [3.0, 4.0]) == 1.0
+    assert O.rel_fro([3.0, 4.0], [6.0, 8.0]) == 0.5
+    assert O.rel_fro([0.0, 0.0], [3.0, 4.0]) == 1.0
+    # a zero reference: the absolute error
+    assert O.rel_fro([3.0, 4.0], [0.0, 0.0]) == 5.0
+    assert O.rel_fro([0.0, 0.0], [0.0, 0.0]) == 0.0
+    # every element counts, whatever the shape
+    assert O.rel_fro(np.ones((2, 3)), np.zeros((2, 3)) + 2.0) == 0.5
 
 
 # --------------------------------------------------------------------------
