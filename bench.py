@@ -329,7 +329,8 @@ def main():
                    "muon_matrices": len(ps.muon), "adamw_tensors": len(ps.adamw),
                    "ns_steps": args.ns_steps, "ns_coeffs": list(COEFF_SCHEDULES[args.coeffs]),
                    "ns_precision": precision, "parallelism": "single-gpu"},
-        "muon_ms_per_step": sum(prof[k]["ms"] for k in ("prep", "norm", "gram", "gram2", "apply", "finish", "ns_fused")) / K,
+        "muon_ms_per_step": sum(prof[k]["ms"] for k in ("prep", "norm", "rescale", "gram", "gram2", "apply", "finish",
+                                                          "ns_fused")) / K,
         "adamw_ms_per_step": prof["adamw"]["ms"] / K,
         "ns_ms_per_step": ns_ms, "ns_tflops": ns_tflops, "ns_frac_peak": ns_tflops / peak,
         "adamw_gbs": adamw_gbs, "adamw_frac_hbm": (adamw_gbs / PEAK_HBM_GBS) if adamw_gbs else None,

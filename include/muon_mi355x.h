@@ -20,6 +20,10 @@
  * A device fault inside a kernel is asynchronous and surfaces at the caller's
  * next synchronisation. Calls that share a workspace must not overlap in time.
  * Streams are passed as void* and must be hipStream_t values (0 = null stream).
+ * Calls cannot be captured into a HIP graph: on a capturing stream every
+ * entry point returns MU_ERR_INVALID_ARG without enqueuing anything (each
+ * call stages its descriptor table through pinned host memory that later
+ * calls reuse, so a replayed capture would read another call's table).
  */
 #ifndef MUON_MI355X_H
 #define MUON_MI355X_H
@@ -96,6 +100,11 @@ typedef struct mu_matrix {
  * Hyper-parameters of one Muon call (one value for every matrix in the list).
  * coeffs: host pointer to ns_steps rows of (a, b, c); NULL means the pages'
  * cubic step (1.5, -0.5, 0) every time. ns_steps = 0 applies the normalised U.
+ * norm_eps: any finite value >= 0, 0 included. ||U_h||_F is summed in float64
+ * and the normalisation holds at any magnitude of U whose nonzero elements are
+ * normal float32 numbers (values below 2^-126 keep the precision their
+ * float32 / bfloat16 storage gives them); U_h = 0 gives O_h = 0 for every
+ * norm_eps, and NaN or infinity in U_h makes O_h NaN.
  */
 typedef struct mu_muon_hparams {
     float lr;
@@ -245,7 +254,8 @@ int mu_version(void);
 #define MU_K_ADAMW 6     /* AdamW */
 #define MU_K_QKCLIP 7    /* QK-Clip rescale (bytes assume every head clipped) */
 #define MU_K_FUSED 8     /* every step but the last apply of mp == 128 problems (>= 256 in a call) */
-#define MU_K_COUNT 9
+#define MU_K_RESCALE 9   /* exact 2^e rescale of X0 where ||U||_F is outside [2^-24, 2^24] */
+#define MU_K_COUNT 10
 int mu_profile_enable(int on);
 int mu_profile_read(int kernel, double* total_ms, int64_t* launches, double* flops, double* bytes);
 const char* mu_kernel_name(int kernel);

@@ -30,8 +30,9 @@ MU_ERR_LAYOUT = 3
 MU_ERR_WORKSPACE = 4
 MU_ERR_HIP = 5
 
-MU_K_PREP, MU_K_NORM, MU_K_GRAM, MU_K_GRAM2, MU_K_APPLY, MU_K_FINISH, MU_K_ADAMW, MU_K_QKCLIP, MU_K_FUSED = range(9)
-MU_K_COUNT = 9
+(MU_K_PREP, MU_K_NORM, MU_K_GRAM, MU_K_GRAM2, MU_K_APPLY, MU_K_FINISH, MU_K_ADAMW, MU_K_QKCLIP, MU_K_FUSED,
+ MU_K_RESCALE) = range(10)
+MU_K_COUNT = 10
 
 EXPORTED = (
     "mu_muon_workspace_size", "mu_muon_step", "mu_ortho_workspace_size", "mu_muon_orthogonalize",
@@ -342,3 +343,18 @@ def workspace(nbytes: int, device) -> Optional[torch.Tensor]:
     buf = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
     off = (-buf.data_ptr()) % 256
     return buf[off:off + nbytes]
+
+
+def tie_to_stream(buf: Optional[torch.Tensor], stream, current=None) -> None:
+    """Keep a buffer allocated on the current stream alive for work queued on
+    `stream` (a torch stream or a raw hipStream_t value): the caching
+    allocator may otherwise hand its memory to the next allocation on the
+    current stream as soon as the caller drops it, while the library's kernels
+    on `stream` still read it. No-op for None or for the current stream."""
+    if buf is None or stream is None:
+        return
+    if not isinstance(stream, torch.cuda.Stream):
+        stream = torch.cuda.ExternalStream(int(stream), device=buf.device)
+    cur = torch.cuda.current_stream(buf.device) if current is None else current
+    if stream.cuda_stream != cur.cuda_stream:
+        buf.record_stream(stream)

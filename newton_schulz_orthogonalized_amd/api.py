@@ -2,7 +2,10 @@
 
 Each function marshals torch tensors into the library's descriptor lists,
 allocates the workspace the library asks for (unless one is passed in) and
-enqueues the work on the current stream. Nothing here computes.
+enqueues the work on `stream` (default: the current stream). A workspace
+allocated here on the current stream is recorded on `stream` when that is
+another stream, so the caching allocator does not reuse it while the library's
+kernels still read it. Nothing here computes.
 """
 
 from __future__ import annotations
@@ -28,6 +31,7 @@ def muon_step(params: Sequence[torch.Tensor], grads: Sequence[torch.Tensor], mom
         return
     if workspace is None:
         workspace = _lib.workspace(_lib.mu_muon_workspace_size(mats, n, hp), params[0].device)
+        _lib.tie_to_stream(workspace, stream)
     _lib.mu_muon_step(mats, n, hp, workspace, stream)
     del keep
 
@@ -53,6 +57,7 @@ def orthogonalize(inputs: Sequence[torch.Tensor], *, heads: Optional[Sequence[in
         return list(outputs)
     if workspace is None:
         workspace = _lib.workspace(_lib.mu_ortho_workspace_size(xs, n, hp), inputs[0].device)
+        _lib.tie_to_stream(workspace, stream)
     _lib.mu_muon_orthogonalize(xs, n, hp, workspace, stream)
     del keep
     return list(outputs)
@@ -70,6 +75,7 @@ def adamw_step(params, grads, exp_avgs, exp_avg_sqs, *, lr, weight_decay, beta1:
         return
     if workspace is None:
         workspace = _lib.workspace(_lib.mu_adamw_workspace_size(n), params[0].device)
+        _lib.tie_to_stream(workspace, stream)
     _lib.mu_adamw_step(ts, n, beta1, beta2, eps, step, workspace, stream)
 
 
@@ -86,4 +92,5 @@ def qk_clip(wqs, wks, max_logits, *, q_heads, k_heads, tau: float = 100.0, gamma
         return
     if workspace is None:
         workspace = _lib.workspace(_lib.mu_qk_clip_workspace_size(pairs, n), wqs[0].device)
+        _lib.tie_to_stream(workspace, stream)
     _lib.mu_qk_clip(pairs, n, tau, workspace, stream)

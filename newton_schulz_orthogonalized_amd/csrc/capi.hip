@@ -166,7 +166,7 @@ struct Plan {
     bool quintic;
     // workspace layout
     size_t off_table, off_prep_prefix, off_group_prefix, table_bytes;
-    size_t off_partials, off_fold, off_bufs, total;
+    size_t off_partials, off_fold, off_xexp, off_bufs, total;
     int64_t total_parts;
 };
 
@@ -296,9 +296,11 @@ void build_plan(const std::vector<Item>& items, int ns_dt, const std::vector<Coe
     pl.table_bytes = o;
     o = align_up(o);
     pl.off_partials = o;
-    o = align_up(o + sizeof(float) * (size_t)pl.total_parts);
+    o = align_up(o + sizeof(double) * (size_t)pl.total_parts);
     pl.off_fold = o;
     o = align_up(o + sizeof(float) * P);
+    pl.off_xexp = o;
+    o = align_up(o + sizeof(int32_t) * P);
     pl.off_bufs = o;
     for (auto& pp : pl.probs) o += (pp.d.xt_used ? 4 : 2) * pp.x_bytes + pp.a_bytes * (pl.quintic ? 2 : 1);
     pl.total = o;
@@ -306,8 +308,9 @@ void build_plan(const std::vector<Item>& items, int ns_dt, const std::vector<Coe
 
 // Fill buffer pointers for a workspace base and serialise the table.
 void carve(Plan& pl, char* ws, std::vector<char>& host_table) {
-    float* partials = (float*)(ws + pl.off_partials);
+    double* partials = (double*)(ws + pl.off_partials);
     float* fold = (float*)(ws + pl.off_fold);
+    int32_t* xexp = (int32_t*)(ws + pl.off_xexp);
     size_t o = pl.off_bufs;
     int64_t part = 0;
     for (size_t i = 0; i < pl.probs.size(); ++i) {
@@ -335,6 +338,7 @@ void carve(Plan& pl, char* ws, std::vector<char>& host_table) {
         d.partials = partials + part;
         part += d.nparts;
         d.fold = fold + i;
+        d.xexp = xexp + i;
     }
     host_table.assign(pl.table_bytes, 0);
     char* h = host_table.data();
@@ -493,8 +497,15 @@ int run_pipeline(Plan& pl, char* ws, const mu_muon_hparams* hp, int src_dt, bool
     rc = timed_launch(MU_K_PREP, 0.0, prep_bytes, s, [&] { return launch_prep(pa, s); }, "prep launch");
     if (rc) return rc;
     NormArgs na{dprobs, P, hp->norm_eps};
-    rc = timed_launch(MU_K_NORM, 0.0, 4.0 * (double)pl.total_parts, s, [&] { return launch_norm(na, s); }, "norm launch");
+    rc = timed_launch(MU_K_NORM, 0.0, 8.0 * (double)pl.total_parts, s, [&] { return launch_norm(na, s); }, "norm launch");
     if (rc) return rc;
+    {   // exact power-of-two rescale of X0 for norms outside the band (usually none)
+        int64_t max_el = 0;
+        for (auto& pp : pl.probs) max_el = std::max<int64_t>(max_el, (int64_t)pp.d.mp * pp.d.np);
+        RescaleArgs ra{dprobs, (const int32_t*)(ws + pl.off_xexp), P, ns_dt, max_el};
+        rc = timed_launch(MU_K_RESCALE, 0.0, 4.0 * P, s, [&] { return launch_rescale(ra, s); }, "rescale launch");
+        if (rc) return rc;
+    }
 
     if (hp->ns_steps == 0) {
         FinishArgs fa{dprobs, dprep, P, pl.prep_prefix.back(), ns_dt, src_dt, step_mode ? 1 : 0, hp->lr, hp->weight_decay};
@@ -614,6 +625,19 @@ int run_pipeline(Plan& pl, char* ws, const mu_muon_hparams* hp, int src_dt, bool
 }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Calls are not capturable: each call stages its descriptor table through a
+// ring of pinned host slots that later calls overwrite, so a captured graph
+// would replay a table copy from memory that no longer holds its table.
+int check_not_capturing(hipStream_t s) {
+    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+    hipError_t e = hipStreamIsCapturing(s, &st);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
+    if (st != hipStreamCaptureStatusNone)
+        return fail(MU_ERR_INVALID_ARG, "the stream is capturing a graph; calls of this library cannot be captured "
+                                        "(their descriptor tables are staged through reused host memory)");
+    return MU_OK;
+}
 
 int validate_mats(const mu_matrix* m, int32_t n, std::vector<Item>& items, int& dt) {
     if (n < 0) return fail(MU_ERR_INVALID_ARG, "n must be >= 0");
@@ -758,6 +782,8 @@ int mu_muon_step(const mu_matrix* m, int32_t n, const mu_muon_hparams* hp, void*
     build_plan(items, ns_dtype(hp), coeffs_of(hp), dt, pl);
     rc = check_ws(pl, ws, ws_bytes);
     if (rc) return rc;
+    rc = check_not_capturing((hipStream_t)stream);
+    if (rc) return rc;
     return run_pipeline(pl, (char*)ws, hp, dt, true, (hipStream_t)stream);
 }
 
@@ -789,6 +815,8 @@ int mu_muon_orthogonalize(const mu_ortho* xs, int32_t n, const mu_muon_hparams* 
     Plan pl;
     build_plan(items, ns_dtype(hp), coeffs_of(hp), dt, pl);
     rc = check_ws(pl, ws, ws_bytes);
+    if (rc) return rc;
+    rc = check_not_capturing((hipStream_t)stream);
     if (rc) return rc;
     return run_pipeline(pl, (char*)ws, hp, dt, false, (hipStream_t)stream);
 }
@@ -869,7 +897,9 @@ int mu_qk_clip(const mu_qk_pair* pairs, int32_t n, float tau, void* ws, size_t w
     std::memcpy(table.data(), segs.data(), sizeof(QkSeg) * segs.size());
     std::memcpy(table.data() + sizeof(QkSeg) * segs.size(), prefix.data(), sizeof(int64_t) * prefix.size());
     hipStream_t s = (hipStream_t)stream;
-    int rc = upload(table.data(), table.size(), ws, s);
+    int rc = check_not_capturing(s);
+    if (rc) return rc;
+    rc = upload(table.data(), table.size(), ws, s);
     if (rc) return rc;
     QkArgs a{};
     a.segs = (const QkSeg*)ws;
@@ -936,7 +966,9 @@ int mu_adamw_step(const mu_tensor* ts, int32_t n, const mu_adamw_hparams* hp, vo
     std::memcpy(table.data(), d.data(), sizeof(AdamWDesc) * n);
     std::memcpy(table.data() + sizeof(AdamWDesc) * n, prefix.data(), sizeof(int64_t) * (n + 1));
     hipStream_t s = (hipStream_t)stream;
-    int rc = upload(table.data(), table.size(), ws, s);
+    int rc = check_not_capturing(s);
+    if (rc) return rc;
+    rc = upload(table.data(), table.size(), ws, s);
     if (rc) return rc;
     AdamWArgs a{};
     a.descs = (const AdamWDesc*)ws;
@@ -1007,6 +1039,7 @@ const char* mu_kernel_name(int k) {
         case MU_K_ADAMW: return "adamw";
         case MU_K_QKCLIP: return "qk_clip";
         case MU_K_FUSED: return "ns_fused";
+        case MU_K_RESCALE: return "rescale";
         default: return "unknown";
     }
 }

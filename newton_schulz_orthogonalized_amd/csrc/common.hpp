@@ -63,8 +63,12 @@ struct NsProb {
     void* xt[2];       // their transposes, np x mp, when xt_used
     void* a;           // a I + b A (cubic steps) or A = X X^T (quintic steps), mp x mp
     void* b;           // a I + b A + c A^2 (quintic steps), mp x mp, or null
-    float* partials;   // per prep-tile sums of squares
-    float* fold;       // 1 / (||U||_F + eps), written by the norm kernel
+    double* partials;  // per prep-tile sums of squares (float64: no overflow or
+                       // underflow for any finite float32 U)
+    float* fold;       // 2^-e / (||U||_F + eps), written by the norm kernel: the
+                       // factor that turns the stored X0 into U / (||U||_F + eps)
+    int32_t* xexp;     // e: the stored X0 is U * 2^e (0 unless ||U||_F lies
+                       // outside the band where the unscaled Gram is exact)
     float* norm_out;   // optional ||U||_F
     float* oout;       // optional float32 copy of O in U-space (step only)
     int32_t nparts;    // number of prep tiles (see prep_rows / prep_cols)
@@ -133,6 +137,11 @@ template <> __device__ inline bf16 from_f32<bf16>(float v) { return (bf16)v; }
 // Wavefront sum in a fixed order (butterfly over 64 lanes): every lane ends
 // with the same value, and the order does not depend on timing.
 __device__ inline float wave_sum(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+__device__ inline double wave_sum(double v) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
     return v;

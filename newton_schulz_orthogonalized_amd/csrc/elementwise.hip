@@ -95,12 +95,13 @@ __device__ inline void load_x4(const TX* p, float v[4]) {
 }
 
 // Block-wide fixed-order sum (four waves); result valid in every thread.
-__device__ inline float block_sum(float v, float* red) {
+template <typename T>
+__device__ inline T block_sum(T v, T* red) {
     v = wave_sum(v);
     const int w = threadIdx.x >> 6;
     if ((threadIdx.x & 63) == 0) red[w] = v;
     __syncthreads();
-    float s = ((red[0] + red[1]) + red[2]) + red[3];
+    T s = ((red[0] + red[1]) + red[2]) + red[3];
     __syncthreads();
     return s;
 }
@@ -158,7 +159,7 @@ __global__ __launch_bounds__(NTHR) void k_prep(PrepArgs A) {
     constexpr int TPR = TC / 4;          // threads per tile row
     constexpr int RSTEP = NTHR / TPR;    // rows between a thread's rows
     __shared__ float tile[TR][TC + 1];
-    __shared__ float red[4];
+    __shared__ double red[4];
     const int t = xcd_remap(blockIdx.x, gridDim.x);   // each XCD streams one contiguous run of tiles
     if (t >= A.total_tiles) return;
     const int p = __builtin_amdgcn_readfirstlane(find_prob(A.prefix, A.nprobs, t));
@@ -205,7 +206,9 @@ __global__ __launch_bounds__(NTHR) void k_prep(PrepArgs A) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) load_gm<TS>(P, ti * TR + rr + RSTEP * k, tj * TC + cc, with_m, gk[k], mk[k]);
     }
-    float ss = 0.f;
+    // sum of squares in float64: squares of float32 values are exact there and
+    // neither overflow nor underflow, whatever the magnitude of U
+    double ss = 0.0;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         const int r = ti * TR + rr + RSTEP * k, c0 = tj * TC + cc;
@@ -213,7 +216,7 @@ __global__ __launch_bounds__(NTHR) void k_prep(PrepArgs A) {
         make_u(P, r, c0, with_m, nest, A.mu, gk[k], mk[k], u);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            ss += u[e] * u[e];
+            ss = fma((double)u[e], (double)u[e], ss);
             tile[rr + RSTEP * k][cc + e] = u[e];
         }
         if constexpr (sizeof(TX) == 4) {
@@ -257,20 +260,81 @@ __global__ __launch_bounds__(NTHR) void k_prep(PrepArgs A) {
             store_x4<TX>(Tt + (int64_t)(tj * TC + a) * RD + ti * TR + cc, v);
         }
     }
-    const float s = block_sum(ss, red);
+    const double s = block_sum(ss, red);
     if (tid == 0) *gp(P.partials + local) = s;
 }
 
+// ||U||_F in float64 from the tile partials (fixed order), and the factors
+// the Newton-Schulz kernels fold into their first step. X0 is stored as U;
+// when ||U||_F lies outside [2^-NORM_BAND_LOG2, 2^NORM_BAND_LOG2] the stored
+// X0 is to be multiplied by 2^e (||U||_F 2^e in [1, 2), done by k_rescale),
+// and fold = 2^-e / (||U||_F + eps) turns the stored X0 back into
+// U / (||U||_F + eps) either way. U = 0 gives fold = 0 (O = 0 for any eps,
+// eps = 0 included); a non-finite norm keeps e = 0 and lets NaN propagate.
 __global__ __launch_bounds__(NTHR) void k_norm(NormArgs A) {
-    __shared__ float red[4];
+    __shared__ double red[4];
     const NsProb& P = A.probs[blockIdx.x];
-    float s = 0.f;
+    double s = 0.0;
     for (int i = threadIdx.x; i < P.nparts; i += NTHR) s += *gp(P.partials + i);
     s = block_sum(s, red);
     if (threadIdx.x == 0) {
-        const float nrm = sqrtf(s);
-        *gp(P.fold) = 1.f / (nrm + A.eps);
-        if (P.norm_out) *gp(P.norm_out) = nrm;
+        const double nrm = sqrt(s);
+        int e = 0;
+        if (nrm > 0.0 && isfinite(nrm) &&
+            (nrm < ldexp(1.0, -NORM_BAND_LOG2) || nrm > ldexp(1.0, NORM_BAND_LOG2)))
+            e = -ilogb(nrm);
+        const double f = nrm == 0.0 ? 0.0 : ldexp(1.0, -e) / (nrm + (double)A.eps);
+        *gp(P.fold) = (float)f;
+        *gp(P.xexp) = e;
+        if (P.norm_out) *gp(P.norm_out) = (float)nrm;
+    }
+}
+
+// The stored X0 (and X0^T where the problem keeps it) times 2^e, for the
+// problems whose exponent is nonzero. Every workgroup reads the exponents 256
+// at a time and moves on when none is set, so with every norm inside the band
+// (the usual case) the launch costs a few microseconds; otherwise all
+// workgroups stride over each flagged problem's buffers, 16 bytes at a time.
+// A power-of-two scale is exact: every stored value stays representable
+// (values tiny against ||U||_F may become subnormal, at no cost to the result).
+template <typename TX>
+__device__ __forceinline__ void rescale_buf(void* buf, int64_t n16, int e) {
+    const int64_t stride = (int64_t)gridDim.x * NTHR;
+    for (int64_t i = (int64_t)blockIdx.x * NTHR + threadIdx.x; i < n16; i += stride) {
+        MU_GLOBAL u32x4* q = (MU_GLOBAL u32x4*)buf + i;
+        if constexpr (sizeof(TX) == 2) {
+            bf16x8 v = __builtin_bit_cast(bf16x8, *q);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) v[k] = (bf16)ldexpf((float)v[k], e);
+            *q = __builtin_bit_cast(u32x4, v);
+        } else {
+            f32x4 v = __builtin_bit_cast(f32x4, *q);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) v[k] = ldexpf(v[k], e);
+            *q = __builtin_bit_cast(u32x4, v);
+        }
+    }
+}
+
+template <typename TX>
+__global__ __launch_bounds__(NTHR) void k_rescale(RescaleArgs A) {
+    __shared__ int32_t se[NTHR];
+    for (int base = 0; base < A.nprobs; base += NTHR) {
+        const int p = base + (int)threadIdx.x;
+        const int32_t e = p < A.nprobs ? *gp(A.xexp + p) : 0;
+        if (!__syncthreads_or(e != 0)) continue;
+        se[threadIdx.x] = e;
+        __syncthreads();
+        const int cnt = min(NTHR, A.nprobs - base);
+        for (int q = 0; q < cnt; ++q) {
+            const int eq = se[q];
+            if (eq == 0) continue;
+            const NsProb P = A.probs[base + q];
+            const int64_t n16 = (int64_t)P.mp * P.np * (int64_t)sizeof(TX) / 16;
+            rescale_buf<TX>(P.x[0], n16, eq);
+            if (P.xt_used) rescale_buf<TX>(P.xt[0], n16, eq);
+        }
+        __syncthreads();   // `se` is rewritten by the next chunk
     }
 }
 
@@ -558,6 +622,17 @@ hipError_t launch_prep(const PrepArgs& a, hipStream_t s) {
 hipError_t launch_norm(const NormArgs& a, hipStream_t s) {
     if (a.nprobs <= 0) return hipSuccess;
     hipLaunchKernelGGL(k_norm, dim3(a.nprobs), dim3(NTHR), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_rescale(const RescaleArgs& a, hipStream_t s) {
+    if (a.nprobs <= 0) return hipSuccess;
+    // enough workgroups to stream one flagged problem at full rate, at most 8
+    // per compute unit; the exit path reads ceil(nprobs / 256) exponents each
+    const int64_t per_wg = (int64_t)NTHR * 64;   // elements of one problem per workgroup
+    const unsigned grid = (unsigned)std::min<int64_t>(2048, grid8(std::max<int64_t>(8, a.max_elems / per_wg)));
+    if (a.ns_dtype == DT_BF16) hipLaunchKernelGGL(k_rescale<bf16>, dim3(grid), dim3(NTHR), 0, s, a);
+    else hipLaunchKernelGGL(k_rescale<float>, dim3(grid), dim3(NTHR), 0, s, a);
     return hipGetLastError();
 }
 

@@ -37,6 +37,26 @@ struct NormArgs {
 };
 hipError_t launch_norm(const NormArgs& a, hipStream_t s);
 
+// Band of ||U||_F inside which the Newton-Schulz kernels take the stored X0 = U
+// as it is: within 2^-NORM_BAND_LOG2 .. 2^NORM_BAND_LOG2 no product of two
+// elements that matters underflows float32, no Gram entry overflows it, and
+// the folded factors f, f^2 and f^3 (f = 1/(||U||_F + eps)) stay normal
+// float32 numbers. Outside it the norm kernel picks e with ||U||_F * 2^e in
+// [1, 2) and the rescale kernel multiplies the stored X0 (and its transposed
+// copy) by 2^e, which is exact.
+constexpr int NORM_BAND_LOG2 = 24;
+
+// X0 <- X0 * 2^xexp[p] for the problems whose exponent is nonzero; a fixed
+// grid that walks the exponents and exits when none is set.
+struct RescaleArgs {
+    const NsProb* probs;
+    const int32_t* xexp;   // nprobs exponents (the norm kernel's output)
+    int nprobs;
+    int ns_dtype;
+    int64_t max_elems;     // largest mp * np of the call (sizes the grid)
+};
+hipError_t launch_rescale(const RescaleArgs& a, hipStream_t s);
+
 enum GemmMode : int {
     GM_GRAM = 0,        // B = f (a I + b f^2 X X^T), or A = f^2 X X^T when a quintic step follows  (upper, mirrored)
     GM_GRAM2 = 1,       // B = f (a I + b A + c A A^T)                                               (upper, mirrored)

@@ -186,3 +186,39 @@ def test_qk_clip_overlapping_pairs_rejected(lib):
     a = _qk(lib)
     b = _qk(lib, wq=A + (1 << 24) + 64, wk=A + (4 << 24), max_logit=A + (6 << 24))   # b.wq inside a.wk
     assert _clip(lib, [a, b]) == lib.MU_ERR_LAYOUT
+
+
+def test_tie_to_stream_records_only_other_streams(lib):
+    """A workspace allocated on the current stream is recorded on the launch
+    stream when that is another stream, so the caching allocator keeps it
+    until the library's kernels there are done."""
+    class FakeStream:
+        def __init__(self, h):
+            self.cuda_stream = h
+
+    class FakeBuf:
+        def __init__(self):
+            self.recorded = []
+            self.device = "cuda:0"
+
+        def record_stream(self, s):
+            self.recorded.append(s.cuda_stream)
+
+    import torch
+    orig = torch.cuda.Stream
+    try:
+        torch.cuda.Stream = FakeStream   # the helper takes any torch stream object as it is
+        cur = FakeStream(11)
+        b = FakeBuf()
+        lib.tie_to_stream(b, FakeStream(22), current=cur)
+        assert b.recorded == [22]
+        b = FakeBuf()
+        lib.tie_to_stream(b, FakeStream(11), current=cur)
+        assert b.recorded == []
+        b = FakeBuf()
+        lib.tie_to_stream(b, None, current=cur)
+        assert b.recorded == []
+        lib.tie_to_stream(None, FakeStream(22), current=cur)
+    finally:
+        torch.cuda.Stream = orig
+
