@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_util import bf16_ulp, need_gpu, to_np
+from gpu_util import bf16_ulp, check_w_against_oracle, need_gpu, tile_rel_fro, to_np
 from oracle import muon_oracle as O
 from workloads import PARAM_SETS, device_normal, seed_for
 
@@ -32,7 +32,7 @@ SAMPLES = {
     "gpt2_small": ["h0.attn.c_attn", "h0.attn.c_proj", "h5.mlp.c_fc", "h11.mlp.c_proj"],
     "per_head_wq": ["l0.wq", "l23.wq"],
     "llama_1b": ["l0.wk", "l23.up", "l11.down"],
-    "llama_8b": ["l0.wk", "l0.wq", "l31.gate"],
+    "llama_8b": ["l0.wk", "l0.wq", "l31.gate", "l0.down"],
 }
 
 
@@ -77,12 +77,20 @@ def _full_set_muon_step(set_name, coeffs):
         print(f"  oracle for {e.name} {e.shape} heads={e.heads}", flush=True)
         ref = O.muon_step_ref(w0, g0, m0, lr=0.02, weight_decay=0.01, heads=e.heads, coeffs=coeffs)
         o = to_np(oo[j])
-        assert O.rel_fro(o, ref["o"]) <= BF16_TOL, e.name
+        err = O.rel_fro(o, ref["o"])
+        terr = tile_rel_fro(o, ref["o"])
+        print(f"    O relF {err:.3e}, worst 256x256 tile {terr:.3e}", flush=True)
+        assert err <= BF16_TOL, e.name
+        assert terr <= BF16_TOL, e.name
         assert O.rel_fro(to_np(ms[j]), ref["m"]) <= MOM_TOL, e.name
-        # the update: W1 is the bf16 rounding of W0 - lr wd W0 - lr O, with the GPU's O
+        w1 = to_np(ws[j])
+        # the update arithmetic: W1 is the bf16 rounding of W0 - lr wd W0 - lr O, with the GPU's O
         want = w0 - 0.02 * 0.01 * w0 - 0.02 * o
         tol = bf16_ulp(want) * 0.5 + 8 * 2.0 ** -24 * (np.abs(w0) + 0.02 * np.abs(o))
-        assert np.all(np.abs(to_np(ws[j]) - want) <= tol), e.name
+        assert np.all(np.abs(w1 - want) <= tol), e.name
+        # and W1 against the oracle's W
+        frac = check_w_against_oracle(w1, w0, o, ref["w"], ref["o"], 0.02)
+        print(f"    W within 1 bf16 ulp of RNE(oracle W): {100 * frac:.2f} %", flush=True)
     # every matrix moved and stayed finite
     for j, w in enumerate(ws):
         assert torch.isfinite(w).all(), ps.muon[j].name
