@@ -212,6 +212,22 @@ int mu_muon_workspace_size(const mu_matrix* mats, int32_t n, const mu_muon_hpara
 int mu_muon_step(const mu_matrix* mats, int32_t n, const mu_muon_hparams* hp,
                  void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * For callers that cannot allocate device memory (serving loops, harnesses
+ * that forbid hipMalloc): mu_muon_step with its workspace taken from a static
+ * device array of MU_NOALLOC_SCRATCH_BYTES that the library holds on each GPU
+ * it runs on until the process ends. The call allocates no device or pinned
+ * memory. A list whose mu_muon_workspace_size exceeds the array is rejected
+ * with MU_ERR_WORKSPACE before anything is enqueued. Every call on one GPU
+ * shares that GPU's array: calls that overlap in time on one GPU (on
+ * different streams, or from different threads without ordering) race, so
+ * serialise them, e.g. on one stream. Nothing in the array needs clearing
+ * between calls: every buffer a call reads is written earlier in that call.
+ * Otherwise exactly mu_muon_step (same kernels, same results).
+ */
+#define MU_NOALLOC_SCRATCH_BYTES (64u << 20)
+int mu_muon_step_noalloc(const mu_matrix* mats, int32_t n, const mu_muon_hparams* hp, void* stream);
+
 /* Workspace bytes mu_muon_orthogonalize needs for this list. */
 int mu_ortho_workspace_size(const mu_ortho* xs, int32_t n, const mu_muon_hparams* hp, size_t* bytes);
 

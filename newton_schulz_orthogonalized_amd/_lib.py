@@ -35,7 +35,8 @@ MU_ERR_HIP = 5
 MU_K_COUNT = 10
 
 EXPORTED = (
-    "mu_muon_workspace_size", "mu_muon_step", "mu_ortho_workspace_size", "mu_muon_orthogonalize",
+    "mu_muon_workspace_size", "mu_muon_step", "mu_muon_step_noalloc", "mu_ortho_workspace_size",
+    "mu_muon_orthogonalize",
     "mu_adamw_workspace_size", "mu_adamw_step", "mu_qk_clip_workspace_size", "mu_qk_clip",
     "mu_status_string", "mu_last_error", "mu_version", "mu_profile_enable", "mu_profile_read", "mu_kernel_name",
 )
@@ -104,6 +105,7 @@ def _load() -> ctypes.CDLL:
     sz = ctypes.c_size_t
     lib.mu_muon_workspace_size.argtypes = [P(MuMatrix), ctypes.c_int32, P(MuMuonHparams), P(sz)]
     lib.mu_muon_step.argtypes = [P(MuMatrix), ctypes.c_int32, P(MuMuonHparams), ctypes.c_void_p, sz, ctypes.c_void_p]
+    lib.mu_muon_step_noalloc.argtypes = [P(MuMatrix), ctypes.c_int32, P(MuMuonHparams), ctypes.c_void_p]
     lib.mu_ortho_workspace_size.argtypes = [P(MuOrtho), ctypes.c_int32, P(MuMuonHparams), P(sz)]
     lib.mu_muon_orthogonalize.argtypes = [P(MuOrtho), ctypes.c_int32, P(MuMuonHparams), ctypes.c_void_p, sz,
                                           ctypes.c_void_p]
@@ -122,7 +124,8 @@ def _load() -> ctypes.CDLL:
                                     P(ctypes.c_double)]
     lib.mu_kernel_name.argtypes = [ctypes.c_int]
     lib.mu_kernel_name.restype = ctypes.c_char_p
-    for name in ("mu_muon_workspace_size", "mu_muon_step", "mu_ortho_workspace_size", "mu_muon_orthogonalize",
+    for name in ("mu_muon_workspace_size", "mu_muon_step", "mu_muon_step_noalloc", "mu_ortho_workspace_size",
+                 "mu_muon_orthogonalize",
                  "mu_adamw_workspace_size", "mu_adamw_step", "mu_profile_enable", "mu_profile_read"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
@@ -216,6 +219,14 @@ def mu_muon_step(mats, n, hp, workspace: Optional[torch.Tensor], stream=None) ->
     ws = 0 if workspace is None else workspace.data_ptr()
     nb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(LIB.mu_muon_step(mats, n, ctypes.byref(hp), ws, nb, _stream(stream)))
+
+
+MU_NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def mu_muon_step_noalloc(mats, n, hp, stream=None) -> None:
+    """mu_muon_step with the library's static per-GPU scratch as workspace."""
+    _check(LIB.mu_muon_step_noalloc(mats, n, ctypes.byref(hp), _stream(stream)))
 
 
 def orthos(inputs, outputs, heads=None, norm_outs=None):

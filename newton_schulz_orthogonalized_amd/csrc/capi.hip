@@ -426,6 +426,77 @@ int upload(const void* src, size_t bytes, void* dst, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------
+// Scratch of mu_muon_step_noalloc: a static device array, one copy per GPU the
+// library runs on, held until the process ends. Host code never uses its name
+// as an address: hipGetSymbolAddress gives each device's copy, once per device
+// with that device current, and only that pointer reaches kernels and copies.
+// Its descriptor tables go through host staging of its own (plain host memory,
+// two slots per device, copied with hipMemcpyAsync; a slot is rewritten only
+// after the copy that read it has completed), so that no call of the entry
+// point allocates device or pinned memory: the two events are created at the
+// same set-up as the address.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[MU_NOALLOC_SCRATCH_BYTES];
+
+struct NoallocDev {
+    bool ready = false;
+    void* ptr = nullptr;                 // this device's copy of `scratch`
+    std::vector<char> host[2];           // table staging
+    hipEvent_t ev[2] = {nullptr, nullptr};
+    bool pending[2] = {false, false};
+    int next = 0;
+};
+constexpr int NOALLOC_MAX_DEVICES = 64;
+std::mutex g_noalloc_mu;
+NoallocDev g_noalloc[NOALLOC_MAX_DEVICES];
+
+// This device's scratch state, set up on its first use (caller holds the lock).
+int noalloc_device(NoallocDev** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= NOALLOC_MAX_DEVICES)
+        return fail(MU_ERR_INVALID_ARG, "device %d is beyond the %d devices the scratch table covers", dev,
+                    NOALLOC_MAX_DEVICES);
+    NoallocDev& d = g_noalloc[dev];
+    if (!d.ready) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        for (int i = 0; i < 2; ++i) {
+            if (!d.ev[i]) {
+                e = hipEventCreateWithFlags(&d.ev[i], hipEventDisableTiming);
+                if (e != hipSuccess) return hip_fail(e, "hipEventCreate(scratch staging)");
+            }
+        }
+        d.ptr = p;
+        d.ready = true;
+    }
+    *out = &d;
+    return MU_OK;
+}
+
+// Table copy of the no-allocation path: host staging slot -> scratch.
+int upload_noalloc(NoallocDev& d, const std::vector<char>& table, void* dst, hipStream_t s) {
+    if (table.empty()) return MU_OK;
+    const int k = d.next;
+    d.next ^= 1;
+    hipError_t e;
+    if (d.pending[k]) {
+        e = hipEventSynchronize(d.ev[k]);
+        if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize(scratch staging)");
+        d.pending[k] = false;
+    }
+    d.host[k].assign(table.begin(), table.end());
+    e = hipMemcpyAsync(dst, d.host[k].data(), table.size(), hipMemcpyHostToDevice, s);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(scratch table)");
+    e = hipEventRecord(d.ev[k], s);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord(scratch staging)");
+    d.pending[k] = true;
+    return MU_OK;
+}
+
+// ---------------------------------------------------------------------------
 // Profiling: events around each launch.
 // ---------------------------------------------------------------------------
 struct ProfRec {
@@ -477,10 +548,11 @@ int timed_launch(int kernel, double flops, double bytes, hipStream_t s, F&& fn, 
 // ---------------------------------------------------------------------------
 // The NS pipeline shared by mu_muon_step and mu_muon_orthogonalize.
 // ---------------------------------------------------------------------------
-int run_pipeline(Plan& pl, char* ws, const mu_muon_hparams* hp, int src_dt, bool step_mode, hipStream_t s) {
+int run_pipeline(Plan& pl, char* ws, const mu_muon_hparams* hp, int src_dt, bool step_mode, hipStream_t s,
+                 NoallocDev* na_dev = nullptr) {
     std::vector<char> table;
     carve(pl, ws, table);
-    int rc = upload(table.data(), table.size(), ws, s);
+    int rc = na_dev ? upload_noalloc(*na_dev, table, ws, s) : upload(table.data(), table.size(), ws, s);
     if (rc) return rc;
     const NsProb* dprobs = (const NsProb*)(ws + pl.off_table);
     const int* dprep = (const int*)(ws + pl.off_prep_prefix);
@@ -785,6 +857,29 @@ int mu_muon_step(const mu_matrix* m, int32_t n, const mu_muon_hparams* hp, void*
     rc = check_not_capturing((hipStream_t)stream);
     if (rc) return rc;
     return run_pipeline(pl, (char*)ws, hp, dt, true, (hipStream_t)stream);
+}
+
+int mu_muon_step_noalloc(const mu_matrix* m, int32_t n, const mu_muon_hparams* hp, void* stream) {
+    g_err.clear();
+    int rc = check_hparams(hp, true);
+    if (rc) return rc;
+    std::vector<Item> items;
+    int dt;
+    rc = validate_mats(m, n, items, dt);
+    if (rc) return rc;
+    if (n == 0) return MU_OK;
+    Plan pl;
+    build_plan(items, ns_dtype(hp), coeffs_of(hp), dt, pl);
+    if (pl.total > (size_t)MU_NOALLOC_SCRATCH_BYTES)
+        return fail(MU_ERR_WORKSPACE, "the list needs %zu bytes of scratch, above the %zu the no-allocation call holds",
+                    pl.total, (size_t)MU_NOALLOC_SCRATCH_BYTES);
+    rc = check_not_capturing((hipStream_t)stream);
+    if (rc) return rc;
+    std::lock_guard<std::mutex> lk(g_noalloc_mu);
+    NoallocDev* d = nullptr;
+    rc = noalloc_device(&d);
+    if (rc) return rc;
+    return run_pipeline(pl, (char*)d->ptr, hp, dt, true, (hipStream_t)stream, d);
 }
 
 int mu_ortho_workspace_size(const mu_ortho* xs, int32_t n, const mu_muon_hparams* hp, size_t* bytes) {

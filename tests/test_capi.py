@@ -188,6 +188,26 @@ def test_qk_clip_overlapping_pairs_rejected(lib):
     assert _clip(lib, [a, b]) == lib.MU_ERR_LAYOUT
 
 
+def test_noalloc_scratch_limit_and_empty_list(lib):
+    """mu_muon_step_noalloc: the header's scratch size is the binding's, a list
+    beyond it is rejected before any HIP call, an empty list is a no-op, and
+    validation runs as for mu_muon_step."""
+    text = open(HEADER).read()
+    m = re.search(r"#define\s+MU_NOALLOC_SCRATCH_BYTES\s+\((\d+)u\s*<<\s*(\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == lib.MU_NOALLOC_SCRATCH_BYTES
+    big = _mat(lib, rows=8192, cols=8192, dtype=lib.MU_BF16, grad=A + (1 << 30), momentum=A + (2 << 30))
+    arr = (lib.MuMatrix * 1)(big)
+    need = ctypes.c_size_t(0)
+    assert lib.LIB.mu_muon_workspace_size(arr, 1, ctypes.byref(_hp(lib)), ctypes.byref(need)) == 0
+    assert need.value > lib.MU_NOALLOC_SCRATCH_BYTES
+    assert lib.LIB.mu_muon_step_noalloc(arr, 1, ctypes.byref(_hp(lib)), None) == lib.MU_ERR_WORKSPACE
+    assert "scratch" in lib.mu_last_error()
+    assert lib.LIB.mu_muon_step_noalloc(arr, 0, ctypes.byref(_hp(lib)), None) == 0
+    bad = (lib.MuMatrix * 1)(_mat(lib, num_heads=3))
+    assert lib.LIB.mu_muon_step_noalloc(bad, 1, ctypes.byref(_hp(lib)), None) == lib.MU_ERR_INVALID_ARG
+    assert lib.LIB.mu_muon_step_noalloc(arr, 1, ctypes.byref(_hp(lib, ns_steps=-2)), None) == lib.MU_ERR_INVALID_ARG
+
+
 def test_tie_to_stream_records_only_other_streams(lib):
     """A workspace allocated on the current stream is recorded on the launch
     stream when that is another stream, so the caching allocator keeps it

@@ -411,6 +411,7 @@ def test_stream_capture_is_rejected():
     torch.cuda.synchronize()
     s = torch.cuda.Stream()
     for call in (lambda: nso().muon_step([w], [g], [m], lr=0.02, weight_decay=0.01, workspace=ws),
+                 lambda: nso().muon_step([w], [g], [m], lr=0.02, weight_decay=0.01, noalloc=True),
                  lambda: nso().adamw_step([p], [pg], [ea], [eq], lr=0.1, weight_decay=0.0, workspace=aws)):
         graph = torch.cuda.CUDAGraph()
         with pytest.raises(_lib.MuonError) as e:
