@@ -7,9 +7,11 @@ over the rest) on a transformer-shaped parameter set, on one MI355X.
 A step is one mu_muon_step over the whole Muon list (momentum, normalisation,
 five Newton-Schulz steps, update) plus one mu_adamw_step over the whole AdamW
 list, with every input resident in HBM. W untimed steps, then K timed steps
-between two device synchronisations. Per-kernel durations come from HIP events
-the library records around each launch on its launch stream during the timed
-steps. Prints one JSON line.
+between two device synchronisations (`value`, ms per step; repeated calls
+replay their launch sequence from a HIP graph, as in a training loop), then K
+more timed steps with the library's profiler on, whose HIP events around each
+launch on its launch stream give the per-kernel durations and the roofline.
+Prints one JSON line.
 """
 
 from __future__ import annotations
@@ -117,7 +119,29 @@ def measure_ceilings(torch, device):
                                   "apply_4096x4096x14336": 2.0 * m * m * n / (ms_a * 1e-3) / 1e12}
     del x, xt, bm
     torch.cuda.empty_cache()
+    out["mfma_bf16_loop"] = mfma_loop_ceiling()
     return out
+
+
+def mfma_loop_ceiling(target_ms: float = 200.0):
+    """The dense bf16 MFMA rate this GPU sustains with no memory traffic at all
+    (every compute unit, one wave per SIMD, 16 independent 16x16x32 MFMA
+    chains), and the shader clock during that loop (s_memtime cycles over the
+    100 MHz s_memrealtime ticks, mean over waves). None if the probe library
+    is not built."""
+    import ctypes
+    path = os.path.join(ROOT, "newton_schulz_orthogonalized_amd", "libmuon_probe.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.probe_mfma_bf16.argtypes = [ctypes.c_double] + [ctypes.POINTER(ctypes.c_double)] * 3
+    lib.probe_mfma_bf16.restype = ctypes.c_int
+    tf, ms, ghz = ctypes.c_double(0), ctypes.c_double(0), ctypes.c_double(0)
+    rc = lib.probe_mfma_bf16(target_ms, ctypes.byref(tf), ctypes.byref(ms), ctypes.byref(ghz))
+    if rc != 0:
+        return {"error": f"hip error {rc}"}
+    return {"tflops": tf.value, "frac_of_spec": tf.value / PEAK_BF16_TFLOPS, "ms": ms.value,
+            "shader_clock_ghz": ghz.value}
 
 
 def time_qk_clip(ps, mu, args, torch, head_dim: int = 128):
@@ -283,16 +307,38 @@ def main():
         torch.cuda.synchronize()
         print(f"[bench] warmup step {i + 1}/{args.warmup} done", file=sys.stderr, flush=True)
 
-    _lib.mu_profile_enable(True)
+    # Timed region 1: the steps as a training loop runs them (a repeated call
+    # replays its launch sequence from a HIP graph). `value` comes from here.
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    print(f"[bench] {args.steps} timed steps in {elapsed:.3f} s", file=sys.stderr, flush=True)
+    # Timed region 2: the same number of steps with the library's profiler on,
+    # which records HIP events around every kernel on its launch stream (and
+    # launches each kernel itself instead of replaying a graph); the
+    # per-kernel durations and the roofline come from here.
+    _lib.mu_profile_enable(True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for i in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed_prof = time.perf_counter() - t1
     _lib.mu_profile_enable(False)
     prof = {_lib.mu_kernel_name(k): _lib.mu_profile_read(k) for k in range(_lib.MU_K_COUNT)}
-    print(f"[bench] {args.steps} timed steps in {elapsed:.3f} s", file=sys.stderr, flush=True)
+    # host time to issue one step with the GPU idle (no wait on earlier work)
+    issue = []
+    for _ in range(5):
+        torch.cuda.synchronize()
+        ti = time.perf_counter()
+        step()
+        issue.append(time.perf_counter() - ti)
+    torch.cuda.synchronize()
+    host_ms = 1e3 * sorted(issue)[len(issue) // 2]
+    print(f"[bench] {args.steps} profiled steps in {elapsed_prof:.3f} s", file=sys.stderr, flush=True)
 
     ms_step = 1e3 * elapsed / max(1, args.steps)
     K = max(1, args.steps)
@@ -329,6 +375,13 @@ def main():
                    "muon_matrices": len(ps.muon), "adamw_tensors": len(ps.adamw),
                    "ns_steps": args.ns_steps, "ns_coeffs": list(COEFF_SCHEDULES[args.coeffs]),
                    "ns_precision": precision, "parallelism": "single-gpu"},
+        "ms_per_step_profiled": 1e3 * elapsed_prof / max(1, args.steps),
+        # host time to issue one step (Python binding + C ABI + launches, median
+        # of five issued onto an idle GPU) and the summed kernel time of one
+        # step: host_ms_per_step below kernel_ms_per_step means the timed
+        # steps were bound by the GPU, not by issuing them
+        "host_ms_per_step": host_ms,
+        "kernel_ms_per_step": sum(v["ms"] for v in prof.values()) / K,
         "muon_ms_per_step": sum(prof[k]["ms"] for k in ("prep", "norm", "rescale", "gram", "gram2", "apply", "finish",
                                                           "ns_fused")) / K,
         "adamw_ms_per_step": prof["adamw"]["ms"] / K,
@@ -339,8 +392,13 @@ def main():
     }
     out["qk_clip"] = time_qk_clip(ps, mu, args, torch)
     if not args.no_ceilings:
-        print("[bench] measuring copy and library-GEMM ceilings", file=sys.stderr, flush=True)
+        print("[bench] measuring copy, library-GEMM and MFMA-loop ceilings", file=sys.stderr, flush=True)
         out["ceilings"] = measure_ceilings(torch, device)
+        loop = out["ceilings"].get("mfma_bf16_loop") or {}
+        if roof["bound"] == "mfma" and precision == "bf16" and loop.get("tflops"):
+            # the same kernel against the rate a pure MFMA loop reaches on this GPU
+            roof["frac_of_measured_ceiling"] = roof["achieved"] / loop["tflops"]
+            out["ns_frac_of_measured_ceiling"] = ns_tflops / loop["tflops"]
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(ps, set_index, args.ns_steps, coeffs)

@@ -4,9 +4,22 @@
  * The library updates optimizer state and parameters that the caller owns, on
  * the caller's HIP stream, with hand-written CDNA4 kernels. It never allocates
  * or frees device memory inside a step; scratch memory is a caller-provided
- * workspace whose size the *_workspace_size queries return. The only memory it
- * owns is a small pinned host staging area for the per-call descriptor tables
- * (allocated on first use) and, while profiling is on, a pool of HIP events.
+ * workspace whose size the *_workspace_size queries return. The memory it owns
+ * is a small pinned host staging area for the per-call descriptor tables
+ * (allocated on first use), while profiling is on a pool of HIP events, and
+ * for repeated Muon calls (below) the plans and HIP graphs of the last 16 call
+ * structures plus one private capture stream per device.
+ *
+ * Repeated calls: mu_muon_step and mu_muon_orthogonalize key each call on its
+ * structure (device, workspace and its size, every buffer pointer, shape,
+ * dtype, head count, the step count and coefficients); lr, weight_decay, mu,
+ * nesterov, norm_eps and the per-matrix scales are not part of it. A repeated
+ * structure skips planning, and from its second call on its kernels are
+ * replayed from a HIP graph captured once (the call's descriptor table, which
+ * carries those scalars, is still uploaded each call). Results are bit for bit
+ * those of launching the kernels one by one, which the library does while
+ * profiling is on, for the no-allocation call, and when the environment
+ * variable MU_GRAPHS is 0.
  *
  * Layout rules common to every entry point:
  *   - every tensor is dense, row-major, with no padding between rows;

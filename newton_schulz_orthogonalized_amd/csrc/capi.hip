@@ -18,7 +18,9 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
+#include <memory>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -108,6 +110,7 @@ int check_hparams(const mu_muon_hparams* hp, bool need_update_terms) {
 // ---------------------------------------------------------------------------
 struct ProbPlan {
     NsProb d;          // device descriptor (buffer pointers filled at carve time)
+    int item;          // the list entry it comes from
     int tile;          // GEMM tile edge
     size_t x_bytes, a_bytes;
 };
@@ -164,8 +167,8 @@ struct Plan {
     std::vector<Group> groups;
     int ns_dt;
     bool quintic;
-    // workspace layout
-    size_t off_table, off_prep_prefix, off_group_prefix, table_bytes;
+    // workspace layout (the uploaded table: call scalars, descriptors, prefixes)
+    size_t off_scalars, off_table, off_prep_prefix, off_group_prefix, table_bytes;
     size_t off_partials, off_fold, off_xexp, off_bufs, total;
     int64_t total_parts;
 };
@@ -198,11 +201,13 @@ void build_plan(const std::vector<Item>& items, int ns_dt, const std::vector<Coe
     for (const Coeff& c : co)
         if (c.c != 0.f) pl.quintic = true;
     std::vector<ProbPlan> all;
-    for (const Item& it : items) {
+    for (size_t ii = 0; ii < items.size(); ++ii) {
+        const Item& it = items[ii];
         const int64_t hr = it.rows / it.heads, hc = it.cols;
         for (int h = 0; h < it.heads; ++h) {
             ProbPlan pp;
             std::memset(&pp.d, 0, sizeof(pp.d));
+            pp.item = (int)ii;
             const int64_t off = (int64_t)h * hr * it.cols;
             const size_t es = dtype_size(src_dt);
             pp.d.src = (const char*)it.src + off * es;
@@ -287,6 +292,8 @@ void build_plan(const std::vector<Item>& items, int ns_dt, const std::vector<Coe
     // layout
     const size_t P = pl.probs.size();
     size_t o = 0;
+    pl.off_scalars = o;
+    o += sizeof(CallScalars);
     pl.off_table = o;
     o += sizeof(NsProb) * P;
     pl.off_prep_prefix = o;
@@ -306,7 +313,19 @@ void build_plan(const std::vector<Item>& items, int ns_dt, const std::vector<Coe
     pl.total = o;
 }
 
-// Fill buffer pointers for a workspace base and serialise the table.
+// The per-call scalars, at the head of the table (kernels read them there).
+CallScalars call_scalars(const mu_muon_hparams* hp) {
+    CallScalars c{};
+    c.lr = hp->lr;
+    c.wd = hp->weight_decay;
+    c.mu = hp->mu;
+    c.nesterov = hp->nesterov ? 1 : 0;
+    c.eps = hp->norm_eps;
+    return c;
+}
+
+// Fill buffer pointers for a workspace base and serialise the table (the
+// scalar header is left zero; the caller writes it for each call).
 void carve(Plan& pl, char* ws, std::vector<char>& host_table) {
     double* partials = (double*)(ws + pl.off_partials);
     float* fold = (float*)(ws + pl.off_fold);
@@ -548,14 +567,16 @@ int timed_launch(int kernel, double flops, double bytes, hipStream_t s, F&& fn, 
 // ---------------------------------------------------------------------------
 // The NS pipeline shared by mu_muon_step and mu_muon_orthogonalize.
 // ---------------------------------------------------------------------------
-int run_pipeline(Plan& pl, char* ws, const mu_muon_hparams* hp, int src_dt, bool step_mode, hipStream_t s,
-                 NoallocDev* na_dev = nullptr) {
-    std::vector<char> table;
-    carve(pl, ws, table);
-    int rc = na_dev ? upload_noalloc(*na_dev, table, ws, s) : upload(table.data(), table.size(), ws, s);
-    if (rc) return rc;
+// Every kernel launch of one call, in order, after its table is in the
+// workspace. The launch arguments depend only on the call's structure (the
+// plan, the workspace, the step count and coefficients); the per-call scalars
+// are read from the table, so a capture of this sequence can be replayed for
+// any later call of the same structure.
+int launch_sequence(const Plan& pl, char* ws, const mu_muon_hparams* hp, int src_dt, bool step_mode, hipStream_t s) {
+    int rc;
     const NsProb* dprobs = (const NsProb*)(ws + pl.off_table);
     const int* dprep = (const int*)(ws + pl.off_prep_prefix);
+    const CallScalars* dcs = (const CallScalars*)(ws + pl.off_scalars);
     const int P = (int)pl.probs.size();
     const int ns_dt = pl.ns_dt;
     const std::vector<Coeff> co = coeffs_of(hp);
@@ -564,11 +585,11 @@ int run_pipeline(Plan& pl, char* ws, const mu_muon_hparams* hp, int src_dt, bool
     for (auto& pp : pl.probs) elems += (double)pp.d.m * pp.d.n;
     const double src_es = (double)dtype_size(src_dt), ns_es = ns_dt == DT_BF16 ? 2.0 : 4.0;
 
-    PrepArgs pa{dprobs, dprep, P, pl.prep_prefix.back(), src_dt, ns_dt, step_mode ? 1 : 0, hp->nesterov ? 1 : 0, hp->mu};
+    PrepArgs pa{dprobs, dprep, dcs, P, pl.prep_prefix.back(), src_dt, ns_dt, step_mode ? 1 : 0};
     const double prep_bytes = elems * (src_es + (step_mode ? 8.0 : 0.0) + ns_es);
     rc = timed_launch(MU_K_PREP, 0.0, prep_bytes, s, [&] { return launch_prep(pa, s); }, "prep launch");
     if (rc) return rc;
-    NormArgs na{dprobs, P, hp->norm_eps};
+    NormArgs na{dprobs, dcs, P};
     rc = timed_launch(MU_K_NORM, 0.0, 8.0 * (double)pl.total_parts, s, [&] { return launch_norm(na, s); }, "norm launch");
     if (rc) return rc;
     {   // exact power-of-two rescale of X0 for norms outside the band (usually none)
@@ -580,7 +601,7 @@ int run_pipeline(Plan& pl, char* ws, const mu_muon_hparams* hp, int src_dt, bool
     }
 
     if (hp->ns_steps == 0) {
-        FinishArgs fa{dprobs, dprep, P, pl.prep_prefix.back(), ns_dt, src_dt, step_mode ? 1 : 0, hp->lr, hp->weight_decay};
+        FinishArgs fa{dprobs, dprep, dcs, P, pl.prep_prefix.back(), ns_dt, src_dt, step_mode ? 1 : 0};
         const double fb = elems * (ns_es + (step_mode ? 2.0 * src_es : src_es));
         return timed_launch(MU_K_FINISH, 0.0, fb, s, [&] { return launch_finish(fa, s); }, "finish launch");
     }
@@ -645,8 +666,7 @@ int run_pipeline(Plan& pl, char* ws, const mu_muon_hparams* hp, int src_dt, bool
             ga.cb = co[k].b;
             ga.cc = co[k].c;
             ga.use_b = quint ? 1 : 0;   // the Gram writes B itself on cubic steps
-            ga.lr = hp->lr;
-            ga.wd = hp->weight_decay;
+            ga.cs = dcs;
             ga.with_update = step_mode ? 1 : 0;
             auto launch = [&](const GemmArgs& a) {
                 return ns_dt == DT_BF16 ? launch_gemm_bf16(a, g.tile, s) : launch_gemm_f32(a, s);
@@ -693,6 +713,128 @@ int run_pipeline(Plan& pl, char* ws, const mu_muon_hparams* hp, int src_dt, bool
         }
         src ^= 1;
     }
+    return MU_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Repeated calls. A training loop calls the step with the same list every
+// step; only the scalars (lr, weight decay, mu, Nesterov, eps) and the
+// per-matrix scales may change. A call's structure (device, workspace, every
+// buffer pointer and shape, dtypes, head counts, step count, coefficients) is
+// its key; the plan and serialised table of the last CALL_CACHE keys are kept,
+// so a repeated call skips planning. From the second call of a key on, its
+// launch sequence is replayed from a HIP graph captured once on a private
+// stream: the call uploads its table (with this call's scalars and scales)
+// with one kernel and launches the graph, two launches in place of one per
+// kernel. While profiling is on, calls launch eagerly (each launch is timed);
+// the environment variable MU_GRAPHS=0 turns replay off.
+// ---------------------------------------------------------------------------
+constexpr size_t CALL_CACHE = 16;
+
+struct CachedCall {
+    std::vector<unsigned char> key;
+    int dev = -1;
+    Plan plan;                   // carved for the key's workspace
+    std::vector<char> table;     // its serialised table, scalar header zero
+    hipGraphExec_t exec = nullptr;
+    hipEvent_t done = nullptr;   // recorded after every replay; waited on before the exec is destroyed
+    int uses = 0;
+};
+std::mutex g_call_mu;
+std::vector<CachedCall*> g_calls;   // most recently used first
+std::vector<std::pair<int, hipStream_t>> g_capture_streams;
+
+bool graphs_enabled() {
+    static const bool on = [] {
+        const char* e = std::getenv("MU_GRAPHS");
+        return !(e && e[0] == '0');
+    }();
+    return on;
+}
+
+bool profiling_on() {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    return g_prof_on;
+}
+
+template <typename T>
+void put(std::vector<unsigned char>& k, const T& v) {
+    const unsigned char* b = (const unsigned char*)&v;
+    k.insert(k.end(), b, b + sizeof(T));
+}
+
+std::vector<unsigned char> call_key(const std::vector<Item>& items, const mu_muon_hparams* hp, int src_dt,
+                                    bool step_mode, const void* ws, size_t ws_bytes) {
+    std::vector<unsigned char> k;
+    k.reserve(64 + items.size() * 88 + 12 * (size_t)hp->ns_steps);
+    put(k, (int)step_mode);
+    put(k, src_dt);
+    put(k, hp->ns_precision);
+    put(k, hp->ns_steps);
+    for (const Coeff& c : coeffs_of(hp)) put(k, c);
+    put(k, ws);
+    put(k, ws_bytes);
+    for (const Item& it : items) {   // everything but the scale, which is patched per call
+        put(k, it.src); put(k, it.mom); put(k, it.param); put(k, it.out);
+        put(k, it.rows); put(k, it.cols); put(k, it.heads);
+        put(k, it.norm_out); put(k, it.oout); put(k, it.vec);
+    }
+    return k;
+}
+
+void drop_call(CachedCall* c) {
+    if (c->exec) {
+        if (c->done) (void)hipEventSynchronize(c->done);
+        (void)hipGraphExecDestroy(c->exec);
+    }
+    if (c->done) (void)hipEventDestroy(c->done);
+    delete c;
+}
+
+int capture_stream(hipStream_t* out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    for (auto& p : g_capture_streams)
+        if (p.first == dev) {
+            *out = p.second;
+            return MU_OK;
+        }
+    hipStream_t st = nullptr;
+    e = hipStreamCreateWithFlags(&st, hipStreamNonBlocking);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamCreate(capture)");
+    g_capture_streams.push_back({dev, st});
+    *out = st;
+    return MU_OK;
+}
+
+// Record the call's launch sequence in a graph (nothing runs).
+int capture_call(CachedCall& c, char* ws, const mu_muon_hparams* hp, int src_dt, bool step_mode) {
+    hipStream_t cap = nullptr;
+    int rc = capture_stream(&cap);
+    if (rc) return rc;
+    hipError_t e = hipStreamBeginCapture(cap, hipStreamCaptureModeThreadLocal);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamBeginCapture");
+    rc = launch_sequence(c.plan, ws, hp, src_dt, step_mode, cap);
+    hipGraph_t g = nullptr;
+    e = hipStreamEndCapture(cap, &g);
+    if (rc) {
+        if (g) (void)hipGraphDestroy(g);
+        return rc;
+    }
+    if (e != hipSuccess) return hip_fail(e, "hipStreamEndCapture");
+    hipGraphExec_t ex = nullptr;
+    e = hipGraphInstantiate(&ex, g, nullptr, nullptr, 0);
+    (void)hipGraphDestroy(g);
+    if (e != hipSuccess) return hip_fail(e, "hipGraphInstantiate");
+    hipEvent_t done = nullptr;
+    e = hipEventCreateWithFlags(&done, hipEventDisableTiming);
+    if (e != hipSuccess) {
+        (void)hipGraphExecDestroy(ex);
+        return hip_fail(e, "hipEventCreate(graph)");
+    }
+    c.exec = ex;
+    c.done = done;
     return MU_OK;
 }
 
@@ -806,6 +948,95 @@ int check_ws(const Plan& pl, void* ws, size_t ws_bytes) {
     return MU_OK;
 }
 
+// The table of one call: the carved table with this call's scalars in its
+// header and each problem's scale from its list entry.
+void table_for_call(const Plan& pl, const std::vector<char>& carved, const std::vector<Item>& items,
+                    const mu_muon_hparams* hp, std::vector<char>& out) {
+    out = carved;
+    const CallScalars cs = call_scalars(hp);
+    std::memcpy(out.data() + pl.off_scalars, &cs, sizeof(cs));
+    for (size_t i = 0; i < pl.probs.size(); ++i) {
+        NsProb* d = (NsProb*)(out.data() + pl.off_table + i * sizeof(NsProb));
+        d->scale = items[(size_t)pl.probs[i].item].scale;
+    }
+}
+
+// A call without the cache: plan (already built), carve, upload, launch.
+int run_eager(Plan& pl, const std::vector<Item>& items, char* ws, const mu_muon_hparams* hp, int src_dt,
+              bool step_mode, hipStream_t s, NoallocDev* na_dev) {
+    std::vector<char> carved, table;
+    carve(pl, ws, carved);
+    table_for_call(pl, carved, items, hp, table);
+    int rc = na_dev ? upload_noalloc(*na_dev, table, ws, s) : upload(table.data(), table.size(), ws, s);
+    if (rc) return rc;
+    return launch_sequence(pl, ws, hp, src_dt, step_mode, s);
+}
+
+// A call through the cache of repeated calls (see CachedCall).
+int run_call(const std::vector<Item>& items, const mu_muon_hparams* hp, int src_dt, bool step_mode, void* ws,
+             size_t ws_bytes, hipStream_t s) {
+    std::lock_guard<std::mutex> lk(g_call_mu);
+    std::vector<unsigned char> key = call_key(items, hp, src_dt, step_mode, ws, ws_bytes);
+    // A key seen before (on any device) has passed the workspace check; a new
+    // one is planned and checked here, before the first HIP call.
+    bool seen = false;
+    for (CachedCall* q : g_calls) seen = seen || q->key == key;
+    std::unique_ptr<CachedCall> fresh;
+    if (!seen) {
+        fresh.reset(new CachedCall());
+        build_plan(items, ns_dtype(hp), coeffs_of(hp), src_dt, fresh->plan);
+        int rc = check_ws(fresh->plan, ws, ws_bytes);
+        if (rc) return rc;
+    }
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    CachedCall* c = nullptr;
+    for (size_t i = 0; i < g_calls.size(); ++i)
+        if (g_calls[i]->dev == dev && g_calls[i]->key == key) {
+            c = g_calls[i];
+            g_calls.erase(g_calls.begin() + (long)i);
+            break;
+        }
+    if (!c) {
+        if (!fresh) {   // seen on another device: the same plan
+            fresh.reset(new CachedCall());
+            build_plan(items, ns_dtype(hp), coeffs_of(hp), src_dt, fresh->plan);
+        }
+        carve(fresh->plan, (char*)ws, fresh->table);
+        fresh->key = std::move(key);
+        fresh->dev = dev;
+        c = fresh.release();
+    }
+    g_calls.insert(g_calls.begin(), c);
+    while (g_calls.size() > CALL_CACHE) {
+        drop_call(g_calls.back());
+        g_calls.pop_back();
+    }
+    int rc = check_not_capturing(s);
+    if (rc) return rc;
+    std::vector<char> table;
+    table_for_call(c->plan, c->table, items, hp, table);
+    rc = upload(table.data(), table.size(), ws, s);
+    if (rc) return rc;
+    if (graphs_enabled() && !profiling_on()) {
+        if (!c->exec && c->uses >= 1) {
+            rc = capture_call(*c, (char*)ws, hp, src_dt, step_mode);
+            if (rc) return rc;
+        }
+        if (c->exec) {
+            e = hipGraphLaunch(c->exec, s);
+            if (e != hipSuccess) return hip_fail(e, "hipGraphLaunch");
+            e = hipEventRecord(c->done, s);
+            if (e != hipSuccess) return hip_fail(e, "hipEventRecord(graph)");
+            ++c->uses;
+            return MU_OK;
+        }
+    }
+    ++c->uses;
+    return launch_sequence(c->plan, (char*)ws, hp, src_dt, step_mode, s);
+}
+
 }  // namespace
 
 extern "C" {
@@ -850,13 +1081,7 @@ int mu_muon_step(const mu_matrix* m, int32_t n, const mu_muon_hparams* hp, void*
     rc = validate_mats(m, n, items, dt);
     if (rc) return rc;
     if (n == 0) return MU_OK;
-    Plan pl;
-    build_plan(items, ns_dtype(hp), coeffs_of(hp), dt, pl);
-    rc = check_ws(pl, ws, ws_bytes);
-    if (rc) return rc;
-    rc = check_not_capturing((hipStream_t)stream);
-    if (rc) return rc;
-    return run_pipeline(pl, (char*)ws, hp, dt, true, (hipStream_t)stream);
+    return run_call(items, hp, dt, true, ws, ws_bytes, (hipStream_t)stream);
 }
 
 int mu_muon_step_noalloc(const mu_matrix* m, int32_t n, const mu_muon_hparams* hp, void* stream) {
@@ -879,7 +1104,7 @@ int mu_muon_step_noalloc(const mu_matrix* m, int32_t n, const mu_muon_hparams* h
     NoallocDev* d = nullptr;
     rc = noalloc_device(&d);
     if (rc) return rc;
-    return run_pipeline(pl, (char*)d->ptr, hp, dt, true, (hipStream_t)stream, d);
+    return run_eager(pl, items, (char*)d->ptr, hp, dt, true, (hipStream_t)stream, d);
 }
 
 int mu_ortho_workspace_size(const mu_ortho* xs, int32_t n, const mu_muon_hparams* hp, size_t* bytes) {
@@ -907,13 +1132,7 @@ int mu_muon_orthogonalize(const mu_ortho* xs, int32_t n, const mu_muon_hparams* 
     rc = validate_ortho(xs, n, items, dt);
     if (rc) return rc;
     if (n == 0) return MU_OK;
-    Plan pl;
-    build_plan(items, ns_dtype(hp), coeffs_of(hp), dt, pl);
-    rc = check_ws(pl, ws, ws_bytes);
-    if (rc) return rc;
-    rc = check_not_capturing((hipStream_t)stream);
-    if (rc) return rc;
-    return run_pipeline(pl, (char*)ws, hp, dt, false, (hipStream_t)stream);
+    return run_call(items, hp, dt, false, ws, ws_bytes, (hipStream_t)stream);
 }
 
 // ---------------------------------------------------------------------------

@@ -175,7 +175,9 @@ __global__ __launch_bounds__(NTHR) void k_prep(PrepArgs A) {
     const int ti = local / tiles_n, tj = local - ti * tiles_n;
     const int tid = threadIdx.x;
     const int rr = tid / TPR, cc = (tid % TPR) * 4;
-    const bool with_m = A.with_momentum != 0, nest = A.nesterov != 0;
+    const bool with_m = A.with_momentum != 0;
+    const bool nest = gp(A.cs)->nesterov != 0;
+    const float mu = gp(A.cs)->mu;
     float gk[4][4], mk[4][4];
     // a tile wholly inside the head block, on vector-capable buffers, loads
     // without per-lane range checks (no divergent branches between the loads)
@@ -213,7 +215,7 @@ __global__ __launch_bounds__(NTHR) void k_prep(PrepArgs A) {
     for (int k = 0; k < 4; ++k) {
         const int r = ti * TR + rr + RSTEP * k, c0 = tj * TC + cc;
         float u[4];
-        make_u(P, r, c0, with_m, nest, A.mu, gk[k], mk[k], u);
+        make_u(P, r, c0, with_m, nest, mu, gk[k], mk[k], u);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             ss = fma((double)u[e], (double)u[e], ss);
@@ -283,7 +285,7 @@ __global__ __launch_bounds__(NTHR) void k_norm(NormArgs A) {
         if (nrm > 0.0 && isfinite(nrm) &&
             (nrm < ldexp(1.0, -NORM_BAND_LOG2) || nrm > ldexp(1.0, NORM_BAND_LOG2)))
             e = -ilogb(nrm);
-        const double f = nrm == 0.0 ? 0.0 : ldexp(1.0, -e) / (nrm + (double)A.eps);
+        const double f = nrm == 0.0 ? 0.0 : ldexp(1.0, -e) / (nrm + (double)gp(A.cs)->eps);
         *gp(P.fold) = (float)f;
         *gp(P.xexp) = e;
         if (P.norm_out) *gp(P.norm_out) = (float)nrm;
@@ -359,6 +361,7 @@ __global__ __launch_bounds__(NTHR) void k_finish(FinishArgs A) {
     const int rr = tid / TPR, cc = (tid % TPR) * 4;
     const float f = *gp(P.fold);
     const bool vec = P.vec != 0;
+    const float lr = gp(A.cs)->lr, wd = gp(A.cs)->wd;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         const int r = ti * TR + rr + RSTEP * k, c0 = tj * TC + cc;
@@ -377,7 +380,7 @@ __global__ __launch_bounds__(NTHR) void k_finish(FinishArgs A) {
         if (A.with_update) {
             float w[4];
             load4<TS>(P.param, off, valid, vec, w);
-            const float decay = A.lr * A.wd, step = A.lr * P.scale;
+            const float decay = lr * wd, step = lr * P.scale;
 #pragma unroll
             for (int e = 0; e < 4; ++e) w[e] = (w[e] - decay * w[e]) - step * o[e];
             store4<TS>(P.param, off, valid, vec, w);

@@ -17,23 +17,33 @@ template <typename TX> constexpr int prep_cols() { return sizeof(TX) == 2 ? 128 
 inline int prep_rows_dt(int ns_dtype) { return ns_dtype == DT_BF16 ? 32 : 64; }
 inline int prep_cols_dt(int ns_dtype) { return ns_dtype == DT_BF16 ? 128 : 64; }
 
+// The per-call scalars of a Muon step, at the head of the call's descriptor
+// table in the workspace. Kernels read them from there rather than from their
+// arguments, so that a launch sequence captured once in a HIP graph stays
+// valid when they change from call to call (a learning-rate schedule).
+struct CallScalars {
+    float lr, wd, mu;
+    int32_t nesterov;
+    float eps;
+    int32_t pad[3];
+};
+
 struct PrepArgs {
     const NsProb* probs;
     const int* prefix;   // nprobs+1 cumulative prep tiles
+    const CallScalars* cs;
     int nprobs;
     int total_tiles;
     int src_dtype;       // element type of src/param/out
     int ns_dtype;        // element type of the X buffers
     int with_momentum;   // 1: Muon step, 0: orthogonalise-only (U = src)
-    int nesterov;
-    float mu;
 };
 hipError_t launch_prep(const PrepArgs& a, hipStream_t s);
 
 struct NormArgs {
     const NsProb* probs;
+    const CallScalars* cs;   // eps
     int nprobs;
-    float eps;
 };
 hipError_t launch_norm(const NormArgs& a, hipStream_t s);
 
@@ -79,7 +89,7 @@ struct GemmArgs {
     int src_dtype;       // element type of param/out
     int xcd_window;      // Gram tiles per XCD per window of the tile order (0: contiguous split)
     float ca, cb, cc;    // step coefficients
-    float lr, wd;
+    const CallScalars* cs;   // lr and wd of the last apply's update
 };
 // tile: 256 or 128 (square tiles, bf16) ; float32 uses 64.
 hipError_t launch_gemm_bf16(const GemmArgs& a, int tile, hipStream_t s);
@@ -102,12 +112,12 @@ hipError_t launch_ns_small(const SmallArgs& a, hipStream_t s);
 struct FinishArgs {      // ns_steps == 0: O = fold * X0
     const NsProb* probs;
     const int* prefix;   // prep-tile prefix
+    const CallScalars* cs;   // lr, wd
     int nprobs;
     int total_tiles;
     int ns_dtype;
     int src_dtype;
     int with_update;
-    float lr, wd;
 };
 hipError_t launch_finish(const FinishArgs& a, hipStream_t s);
 

@@ -119,11 +119,14 @@ __device__ __forceinline__ void apply_tile(int local, int TM, int TN, int& ti, i
 // run cut by the block edge goes element by element in a loop that is kept
 // rolled, so the many inlined copies of this stay small.
 // ---------------------------------------------------------------------------
+// lr and wd come from the call's scalars (CallScalars), read once per wave by
+// the last-apply epilogue.
 template <typename TS>
-__device__ __forceinline__ void emit_u8(const GemmArgs& A, const NsProb& P, int ur, int uc0, const float* v) {
+__device__ __forceinline__ void emit_u8(const GemmArgs& A, const NsProb& P, float lr, float wd, int ur, int uc0,
+                                        const float* v) {
     if (ur >= P.hr || uc0 >= P.hc) return;
     const int64_t off = (int64_t)ur * P.ld + uc0;
-    const float decay = A.lr * A.wd, step = A.lr * P.scale;
+    const float decay = lr * wd, step = lr * P.scale;
     if (P.vec && uc0 + 8 <= P.hc) {
         if (P.oout) {
 #pragma unroll
@@ -178,10 +181,10 @@ __device__ __forceinline__ void emit_u8(const GemmArgs& A, const NsProb& P, int 
 
 // The update of emit_u8's vector path with the 8 parameter values already in
 // registers (loaded ahead, see the last-apply epilogue); same arithmetic.
-__device__ __forceinline__ void update8_pre(const GemmArgs& A, const NsProb& P, int ur, int uc0, const float* v,
+__device__ __forceinline__ void update8_pre(const NsProb& P, float lr, float wd, int ur, int uc0, const float* v,
                                             const bf16x4 (&q)[2]) {
     const int64_t off = (int64_t)ur * P.ld + uc0;
-    const float decay = A.lr * A.wd, step = A.lr * P.scale;
+    const float decay = lr * wd, step = lr * P.scale;
     if (P.oout) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) P.oout[off + e] = v[e];
@@ -285,6 +288,11 @@ __device__ __forceinline__ void epilogue_mode(const GemmArgs& A, const NsProb& P
     const int lane = threadIdx.x & 63;
     const int g4 = lane >> 4, l16 = lane & 15;
     constexpr int mode = MODE;
+    float lr = 0.f, wd = 0.f;   // the update's scalars (last apply only)
+    if constexpr (MODE == GM_APPLY_LAST) {
+        lr = gp(A.cs)->lr;
+        wd = gp(A.cs)->wd;
+    }
     constexpr bool gram = mode == GM_GRAM || mode == GM_GRAM2;
     const float f = gram && A.first ? P.fold[0] : 1.f;   // the apply takes it through B
     const bool diag = gram && ti == tj;
@@ -444,7 +452,7 @@ __device__ __forceinline__ void epilogue_mode(const GemmArgs& A, const NsProb& P
                             for (int pass = 0; pass < LPR; ++pass) {
                                 float v[8];
                                 half_row(pass, v);
-                                update8_pre(A, P, ur0 + pass * RPP + lane / LPR, uc0, v, pre[(fm >> 2) * LPR + pass]);
+                                update8_pre(P, lr, wd, ur0 + pass * RPP + lane / LPR, uc0, v, pre[(fm >> 2) * LPR + pass]);
                             }
                         }
                     } else {
@@ -452,7 +460,7 @@ __device__ __forceinline__ void epilogue_mode(const GemmArgs& A, const NsProb& P
                         for (int pass = 0; pass < LPR; ++pass) {
                             float v[8];
                             half_row(pass, v);
-                            emit_u8<TS>(A, P, ur0 + pass * RPP + lane / LPR, uc0, v);
+                            emit_u8<TS>(A, P, lr, wd, ur0 + pass * RPP + lane / LPR, uc0, v);
                         }
                     }
                     wave_lds_sync();
@@ -499,7 +507,7 @@ __device__ __forceinline__ void epilogue_mode(const GemmArgs& A, const NsProb& P
                         *(f32x4*)(row + ((q ^ l16) << 2)) = f32x4{v[0], v[1], v[2], v[3]};
                         *(f32x4*)(row + (((q + 1) ^ l16) << 2)) = f32x4{v[4], v[5], v[6], v[7]};
                     } else {
-                        emit_u8<TS>(A, P, c, r0, v);
+                        emit_u8<TS>(A, P, lr, wd, c, r0, v);
                     }
                 }
             }
@@ -523,7 +531,7 @@ __device__ __forceinline__ void epilogue_mode(const GemmArgs& A, const NsProb& P
                             for (int it = 0; it < WT / 8; ++it) {
                                 float v[8];
                                 block_row(it, v);
-                                update8_pre(A, P, col_base + it * 8 + (lane >> 3), uc0, v,
+                                update8_pre(P, lr, wd, col_base + it * 8 + (lane >> 3), uc0, v,
                                             pre[(fm >> 2) * (WT / 8) + it]);
                             }
                         }
@@ -532,7 +540,7 @@ __device__ __forceinline__ void epilogue_mode(const GemmArgs& A, const NsProb& P
                         for (int it = 0; it < WT / 8; ++it) {
                             float v[8];
                             block_row(it, v);
-                            emit_u8<TS>(A, P, col_base + it * 8 + (lane >> 3), uc0, v);
+                            emit_u8<TS>(A, P, lr, wd, col_base + it * 8 + (lane >> 3), uc0, v);
                         }
                     }
                     wave_lds_sync();
@@ -582,10 +590,10 @@ __device__ __forceinline__ void epilogue_mode(const GemmArgs& A, const NsProb& P
                     }
                 } else {
                     if constexpr (pre_ok) {
-                        if (fast) update8_pre(A, P, r, c, v, pre[fm * PASSES + pass]);
-                        else emit_u8<TS>(A, P, r, c, v);
+                        if (fast) update8_pre(P, lr, wd, r, c, v, pre[fm * PASSES + pass]);
+                        else emit_u8<TS>(A, P, lr, wd, r, c, v);
                     } else {
-                        emit_u8<TS>(A, P, r, c, v);
+                        emit_u8<TS>(A, P, lr, wd, r, c, v);
                     }
                 }
             }
