@@ -200,16 +200,27 @@ def orthogonalize_ref(u, heads: int = 1, coeffs=None, eps: float = DEFAULT_NORM_
     return out, norms
 
 
-def muon_update_ref(weight, ortho, lr: float, weight_decay: float, scale: float = 1.0):
-    """Decoupled-weight-decay update: W <- W - lr*wd*W - lr*scale*O (both from W_old)."""
+def muon_update_ref(weight, ortho, lr: float, weight_decay: float, scale: float = 1.0, cautious: bool = False):
+    """Decoupled-weight-decay update: W <- W - lr*wd*W - lr*scale*O (both from W_old).
+
+    cautious=True: cautious weight decay, which the nanochat optimizer page
+    ("Muon Step Implementation") names without a formula. Reading: the decay
+    acts only on the coordinates where it moves the weight the same way as the
+    update, i.e. where u = lr*scale*O has the sign of W or is zero:
+    W <- W - lr*wd*W*[W*u >= 0] - u. With O = 0 this is the plain decay; where
+    every W*u < 0 it is the update without decay.
+    """
     w = np.asarray(weight, dtype=np.float64)
     o = np.asarray(ortho, dtype=np.float64)
+    if cautious:
+        u = lr * scale * o
+        return w - lr * weight_decay * w * (w * u >= 0.0) - u
     return w - lr * weight_decay * w - lr * scale * o
 
 
 def muon_step_ref(weight, grad, momentum, *, lr: float, weight_decay: float,
                   mu: float = DEFAULT_MU, nesterov: bool = True, heads: int = 1,
-                  coeffs=None, eps: float = DEFAULT_NORM_EPS, scale: float = 1.0):
+                  coeffs=None, eps: float = DEFAULT_NORM_EPS, scale: float = 1.0, cautious: bool = False):
     """One Muon step for one 2-D weight, all four stages in order.
 
     Returns a dict with the new weight ``w`` (float64, before any bf16 cast),
@@ -221,7 +232,7 @@ def muon_step_ref(weight, grad, momentum, *, lr: float, weight_decay: float,
     x0 = np.empty_like(u)
     for sl in head_blocks(u.shape[0], heads):
         x0[sl], _ = frobenius_normalize_ref(u[sl], eps)
-    w_new = muon_update_ref(weight, o, lr, weight_decay, scale)
+    w_new = muon_update_ref(weight, o, lr, weight_decay, scale, cautious)
     return {"w": w_new, "m": m_new, "o": o, "norms": norms, "x0": x0, "u": u}
 
 

@@ -208,6 +208,47 @@ def test_heads_must_divide_rows():
 
 
 # --------------------------------------------------------------------------
+# Cautious weight decay (a reading: decay only where it agrees with the update)
+# --------------------------------------------------------------------------
+
+def test_cautious_decay_hand_values():
+    # lr 0.1, wd 0.5 (decay factor 0.05), scale 2: u = 0.2 * O
+    w = np.array([1.0, 1.0, -2.0, -2.0, 0.0, 3.0])
+    o = np.array([0.5, -0.5, -1.0, 1.0, 4.0, 0.0])
+    got = O.muon_update_ref(w, o, lr=0.1, weight_decay=0.5, scale=2.0, cautious=True)
+    # same sign: decayed (1 - 0.05 - 0.1 = 0.85; -2 + 0.1 + 0.2 = -1.7); opposite sign: not
+    # (1 + 0.1 = 1.1; -2 - 0.2 = -2.2); W = 0: only the update (-0.8); O = 0: plain decay (2.85)
+    want = np.array([0.85, 1.1, -1.7, -2.2, -0.8, 2.85])
+    assert np.allclose(got, want, rtol=0, atol=1e-15)
+
+
+def test_cautious_decay_reduces_to_the_two_plain_updates():
+    rng = _rng(50)
+    w = np.abs(rng.standard_normal((5, 9))) + 0.1
+    o = np.abs(rng.standard_normal((5, 9))) + 0.1
+    # every W u > 0: the plain decoupled update
+    assert np.array_equal(O.muon_update_ref(w, o, 0.02, 0.1, 1.5, cautious=True),
+                          O.muon_update_ref(w, o, 0.02, 0.1, 1.5))
+    # every W u < 0: the update without decay
+    assert np.array_equal(O.muon_update_ref(w, -o, 0.02, 0.1, 1.5, cautious=True),
+                          O.muon_update_ref(w, -o, 0.02, 0.0, 1.5))
+    # a negative scale flips which coordinates decay
+    assert np.array_equal(O.muon_update_ref(w, o, 0.02, 0.1, -1.5, cautious=True),
+                          O.muon_update_ref(w, o, 0.02, 0.0, -1.5))
+
+
+def test_cautious_step_changes_only_the_update():
+    rng = _rng(51)
+    w, g, m = (rng.standard_normal((6, 10)) for _ in range(3))
+    a = O.muon_step_ref(w, g, m, lr=0.05, weight_decay=0.2)
+    b = O.muon_step_ref(w, g, m, lr=0.05, weight_decay=0.2, cautious=True)
+    assert np.array_equal(a["o"], b["o"]) and np.array_equal(a["m"], b["m"])
+    keep = w * (0.05 * b["o"]) >= 0
+    assert np.array_equal(a["w"][keep], b["w"][keep])
+    assert np.allclose(b["w"][~keep], (w - 0.05 * b["o"])[~keep], rtol=0, atol=1e-15)
+
+
+# --------------------------------------------------------------------------
 # Exact arithmetic on tiny inputs: the iteration in rational numbers
 # --------------------------------------------------------------------------
 
