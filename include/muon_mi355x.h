@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define MU_API_VERSION 1
+#define MU_API_VERSION 2
 
 /* element types */
 #define MU_F32 0
@@ -83,6 +83,7 @@ extern "C" {
  *       X = U_h / (||U_h||_F + norm_eps), transposed when the block is taller
  *       than wide; ns_steps times: X <- a_k X + b_k (X X^T) X + c_k (X X^T)^2 X
  *   W <- W - lr*weight_decay*W - lr*scale*O       (O = X, untransposed)
+ *   (with cautious_wd: W <- W - lr*weight_decay*W*[W*u >= 0] - u, u = lr*scale*O)
  *
  * param    [rows, cols] dtype, updated in place (float32 math, bf16 stores
  *          round to nearest even)
@@ -118,6 +119,11 @@ typedef struct mu_matrix {
  * normal float32 numbers (values below 2^-126 keep the precision their
  * float32 / bfloat16 storage gives them); U_h = 0 gives O_h = 0 for every
  * norm_eps, and NaN or infinity in U_h makes O_h NaN.
+ * cautious_wd: 0 or 1. Cautious weight decay, which the nanochat optimizer
+ * page ("Muon Step Implementation") names without a formula; the reading used
+ * applies the decay only to elements where it moves the weight the same way
+ * as the update u = lr*scale*O (W*u >= 0, decided in float32), so O = 0 keeps
+ * the plain decay.
  */
 typedef struct mu_muon_hparams {
     float lr;
@@ -128,6 +134,7 @@ typedef struct mu_muon_hparams {
     int32_t ns_steps;
     const float* coeffs;
     int32_t ns_precision;
+    int32_t cautious_wd;
 } mu_muon_hparams;
 
 /*

@@ -56,6 +56,7 @@ class MuMuonHparams(ctypes.Structure):
         ("lr", ctypes.c_float), ("weight_decay", ctypes.c_float), ("mu", ctypes.c_float),
         ("nesterov", ctypes.c_int32), ("norm_eps", ctypes.c_float), ("ns_steps", ctypes.c_int32),
         ("coeffs", ctypes.POINTER(ctypes.c_float)), ("ns_precision", ctypes.c_int32),
+        ("cautious_wd", ctypes.c_int32),
     ]
 
 
@@ -168,7 +169,7 @@ def _require(t: torch.Tensor, what: str) -> None:
 
 def muon_hparams(lr: float, weight_decay: float, mu: float = 0.95, nesterov: bool = True, norm_eps: float = 1e-7,
                  ns_steps: int = 5, coeffs: Optional[Sequence[Sequence[float]]] = None,
-                 precision: str = "bf16"):
+                 precision: str = "bf16", cautious_wd: bool = False):
     """Build mu_muon_hparams. Returns (struct, keepalive) - keep both alive for the call."""
     buf = None
     if coeffs is not None:
@@ -183,7 +184,7 @@ def muon_hparams(lr: float, weight_decay: float, mu: float = 0.95, nesterov: boo
         buf = (ctypes.c_float * len(flat))(*flat)
     hp = MuMuonHparams(lr, weight_decay, mu, 1 if nesterov else 0, norm_eps, ns_steps,
                        ctypes.cast(buf, ctypes.POINTER(ctypes.c_float)) if buf is not None else None,
-                       MU_NS_BF16 if precision == "bf16" else MU_NS_F32)
+                       MU_NS_BF16 if precision == "bf16" else MU_NS_F32, 1 if cautious_wd else 0)
     return hp, buf
 
 

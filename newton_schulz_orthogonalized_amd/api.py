@@ -23,14 +23,16 @@ def muon_step(params: Sequence[torch.Tensor], grads: Sequence[torch.Tensor], mom
               ns_steps: int = 5, coeffs=None, precision: str = "bf16", norm_eps: float = 1e-7,
               norm_outs: Optional[Sequence[torch.Tensor]] = None,
               ortho_outs: Optional[Sequence[Optional[torch.Tensor]]] = None,
-              workspace: Optional[torch.Tensor] = None, stream=None, noalloc: bool = False) -> None:
+              workspace: Optional[torch.Tensor] = None, stream=None, noalloc: bool = False,
+              cautious_wd: bool = False) -> None:
     """In-place Muon step over 2-D params (momentum fp32, grads in the param dtype).
 
     noalloc=True runs mu_muon_step_noalloc: no workspace is allocated, the
     library's static per-GPU scratch (MU_NOALLOC_SCRATCH_BYTES) is used, and
-    calls on one GPU must not overlap in time."""
+    calls on one GPU must not overlap in time. cautious_wd=True applies the
+    decay only where it agrees in sign with the update (see the header)."""
     mats, n = _lib.matrices(params, grads, moms, heads, scales, norm_outs, ortho_outs)
-    hp, keep = _lib.muon_hparams(lr, weight_decay, mu, nesterov, norm_eps, ns_steps, coeffs, precision)
+    hp, keep = _lib.muon_hparams(lr, weight_decay, mu, nesterov, norm_eps, ns_steps, coeffs, precision, cautious_wd)
     if n == 0:
         return
     if noalloc:

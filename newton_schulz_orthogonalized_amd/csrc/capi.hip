@@ -92,6 +92,8 @@ int check_hparams(const mu_muon_hparams* hp, bool need_update_terms) {
     if (hp->ns_steps > 1000) return fail(MU_ERR_INVALID_ARG, "ns_steps too large (%d)", hp->ns_steps);
     if (hp->ns_precision != MU_NS_F32 && hp->ns_precision != MU_NS_BF16)
         return fail(MU_ERR_DTYPE, "unknown ns_precision %d", hp->ns_precision);
+    if (hp->cautious_wd != 0 && hp->cautious_wd != 1)
+        return fail(MU_ERR_INVALID_ARG, "cautious_wd must be 0 or 1 (got %d)", hp->cautious_wd);
     if (!(hp->norm_eps >= 0.f) || !std::isfinite(hp->norm_eps)) return fail(MU_ERR_INVALID_ARG, "norm_eps must be finite and >= 0");
     if (need_update_terms) {
         if (!std::isfinite(hp->lr) || !std::isfinite(hp->weight_decay) || !std::isfinite(hp->mu))
@@ -321,6 +323,7 @@ CallScalars call_scalars(const mu_muon_hparams* hp) {
     c.mu = hp->mu;
     c.nesterov = hp->nesterov ? 1 : 0;
     c.eps = hp->norm_eps;
+    c.cautious = hp->cautious_wd ? 1 : 0;
     return c;
 }
 

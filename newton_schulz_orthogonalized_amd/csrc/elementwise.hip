@@ -362,6 +362,7 @@ __global__ __launch_bounds__(NTHR) void k_finish(FinishArgs A) {
     const float f = *gp(P.fold);
     const bool vec = P.vec != 0;
     const float lr = gp(A.cs)->lr, wd = gp(A.cs)->wd;
+    const bool cautious = gp(A.cs)->cautious != 0;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         const int r = ti * TR + rr + RSTEP * k, c0 = tj * TC + cc;
@@ -382,7 +383,11 @@ __global__ __launch_bounds__(NTHR) void k_finish(FinishArgs A) {
             load4<TS>(P.param, off, valid, vec, w);
             const float decay = lr * wd, step = lr * P.scale;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) w[e] = (w[e] - decay * w[e]) - step * o[e];
+            for (int e = 0; e < 4; ++e) {
+                // cautious weight decay: no decay where the update opposes the weight's sign
+                const float d = (cautious && w[e] * (step * o[e]) < 0.f) ? 0.f : decay;
+                w[e] = (w[e] - d * w[e]) - step * o[e];
+            }
             store4<TS>(P.param, off, valid, vec, w);
         } else {
             store4<TS>(P.out, off, valid, vec, o);

@@ -25,7 +25,8 @@ struct CallScalars {
     float lr, wd, mu;
     int32_t nesterov;
     float eps;
-    int32_t pad[3];
+    int32_t cautious;   // cautious weight decay: decay only where W * (lr scale O) >= 0
+    int32_t pad[2];
 };
 
 struct PrepArgs {

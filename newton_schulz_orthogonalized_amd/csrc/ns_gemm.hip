@@ -119,14 +119,25 @@ __device__ __forceinline__ void apply_tile(int local, int TM, int TN, int& ti, i
 // run cut by the block edge goes element by element in a loop that is kept
 // rolled, so the many inlined copies of this stay small.
 // ---------------------------------------------------------------------------
-// lr and wd come from the call's scalars (CallScalars), read once per wave by
-// the last-apply epilogue.
+// The update's scalars, read from the call's CallScalars once per wave by the
+// last-apply epilogue.
+struct UpdScalars {
+    float lr, wd;
+    bool cautious;
+};
+
+// Decoupled decay factor of one element: lr*wd, or with cautious weight decay
+// lr*wd only where the update u = step*v has the sign of x or is zero.
+__device__ __forceinline__ float decay_of(const UpdScalars& us, float decay, float x, float u) {
+    return (us.cautious && x * u < 0.f) ? 0.f : decay;
+}
+
 template <typename TS>
-__device__ __forceinline__ void emit_u8(const GemmArgs& A, const NsProb& P, float lr, float wd, int ur, int uc0,
+__device__ __forceinline__ void emit_u8(const GemmArgs& A, const NsProb& P, const UpdScalars& us, int ur, int uc0,
                                         const float* v) {
     if (ur >= P.hr || uc0 >= P.hc) return;
     const int64_t off = (int64_t)ur * P.ld + uc0;
-    const float decay = lr * wd, step = lr * P.scale;
+    const float decay = us.lr * us.wd, step = us.lr * P.scale;
     if (P.vec && uc0 + 8 <= P.hc) {
         if (P.oout) {
 #pragma unroll
@@ -147,7 +158,10 @@ __device__ __forceinline__ void emit_u8(const GemmArgs& A, const NsProb& P, floa
                     for (int e = 0; e < 4; ++e) x[e] = q[e];
                 }
 #pragma unroll
-                for (int e = 0; e < 4; ++e) x[e] = (x[e] - decay * x[e]) - step * v[4 * h + e];
+                for (int e = 0; e < 4; ++e) {
+                    const float d = decay_of(us, decay, x[e], step * v[4 * h + e]);
+                    x[e] = (x[e] - d * x[e]) - step * v[4 * h + e];
+                }
             } else {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) x[e] = v[4 * h + e];
@@ -172,7 +186,8 @@ __device__ __forceinline__ void emit_u8(const GemmArgs& A, const NsProb& P, floa
         if (A.with_update) {
             TS* w = (TS*)P.param + off + e;
             const float x = to_f32<TS>(*w);
-            *w = from_f32<TS>((x - decay * x) - step * ve);
+            const float d = decay_of(us, decay, x, step * ve);
+            *w = from_f32<TS>((x - d * x) - step * ve);
         } else {
             ((TS*)P.out)[off + e] = from_f32<TS>(ve);
         }
@@ -181,10 +196,10 @@ __device__ __forceinline__ void emit_u8(const GemmArgs& A, const NsProb& P, floa
 
 // The update of emit_u8's vector path with the 8 parameter values already in
 // registers (loaded ahead, see the last-apply epilogue); same arithmetic.
-__device__ __forceinline__ void update8_pre(const NsProb& P, float lr, float wd, int ur, int uc0, const float* v,
+__device__ __forceinline__ void update8_pre(const NsProb& P, const UpdScalars& us, int ur, int uc0, const float* v,
                                             const bf16x4 (&q)[2]) {
     const int64_t off = (int64_t)ur * P.ld + uc0;
-    const float decay = lr * wd, step = lr * P.scale;
+    const float decay = us.lr * us.wd, step = us.lr * P.scale;
     if (P.oout) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) P.oout[off + e] = v[e];
@@ -196,7 +211,8 @@ __device__ __forceinline__ void update8_pre(const NsProb& P, float lr, float wd,
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const float x = (float)q[h][e];
-            o[e] = (bf16)((x - decay * x) - step * v[4 * h + e]);
+            const float d = decay_of(us, decay, x, step * v[4 * h + e]);
+            o[e] = (bf16)((x - d * x) - step * v[4 * h + e]);
         }
         *gp((bf16x4*)(dst + 4 * h)) = o;
     }
@@ -288,10 +304,11 @@ __device__ __forceinline__ void epilogue_mode(const GemmArgs& A, const NsProb& P
     const int lane = threadIdx.x & 63;
     const int g4 = lane >> 4, l16 = lane & 15;
     constexpr int mode = MODE;
-    float lr = 0.f, wd = 0.f;   // the update's scalars (last apply only)
+    UpdScalars us{0.f, 0.f, false};   // the update's scalars (last apply only)
     if constexpr (MODE == GM_APPLY_LAST) {
-        lr = gp(A.cs)->lr;
-        wd = gp(A.cs)->wd;
+        us.lr = gp(A.cs)->lr;
+        us.wd = gp(A.cs)->wd;
+        us.cautious = gp(A.cs)->cautious != 0;
     }
     constexpr bool gram = mode == GM_GRAM || mode == GM_GRAM2;
     const float f = gram && A.first ? P.fold[0] : 1.f;   // the apply takes it through B
@@ -452,7 +469,7 @@ __device__ __forceinline__ void epilogue_mode(const GemmArgs& A, const NsProb& P
                             for (int pass = 0; pass < LPR; ++pass) {
                                 float v[8];
                                 half_row(pass, v);
-                                update8_pre(P, lr, wd, ur0 + pass * RPP + lane / LPR, uc0, v, pre[(fm >> 2) * LPR + pass]);
+                                update8_pre(P, us, ur0 + pass * RPP + lane / LPR, uc0, v, pre[(fm >> 2) * LPR + pass]);
                             }
                         }
                     } else {
@@ -460,7 +477,7 @@ __device__ __forceinline__ void epilogue_mode(const GemmArgs& A, const NsProb& P
                         for (int pass = 0; pass < LPR; ++pass) {
                             float v[8];
                             half_row(pass, v);
-                            emit_u8<TS>(A, P, lr, wd, ur0 + pass * RPP + lane / LPR, uc0, v);
+                            emit_u8<TS>(A, P, us, ur0 + pass * RPP + lane / LPR, uc0, v);
                         }
                     }
                     wave_lds_sync();
@@ -507,7 +524,7 @@ __device__ __forceinline__ void epilogue_mode(const GemmArgs& A, const NsProb& P
                         *(f32x4*)(row + ((q ^ l16) << 2)) = f32x4{v[0], v[1], v[2], v[3]};
                         *(f32x4*)(row + (((q + 1) ^ l16) << 2)) = f32x4{v[4], v[5], v[6], v[7]};
                     } else {
-                        emit_u8<TS>(A, P, lr, wd, c, r0, v);
+                        emit_u8<TS>(A, P, us, c, r0, v);
                     }
                 }
             }
@@ -531,7 +548,7 @@ __device__ __forceinline__ void epilogue_mode(const GemmArgs& A, const NsProb& P
                             for (int it = 0; it < WT / 8; ++it) {
                                 float v[8];
                                 block_row(it, v);
-                                update8_pre(P, lr, wd, col_base + it * 8 + (lane >> 3), uc0, v,
+                                update8_pre(P, us, col_base + it * 8 + (lane >> 3), uc0, v,
                                             pre[(fm >> 2) * (WT / 8) + it]);
                             }
                         }
@@ -540,7 +557,7 @@ __device__ __forceinline__ void epilogue_mode(const GemmArgs& A, const NsProb& P
                         for (int it = 0; it < WT / 8; ++it) {
                             float v[8];
                             block_row(it, v);
-                            emit_u8<TS>(A, P, lr, wd, col_base + it * 8 + (lane >> 3), uc0, v);
+                            emit_u8<TS>(A, P, us, col_base + it * 8 + (lane >> 3), uc0, v);
                         }
                     }
                     wave_lds_sync();
@@ -590,10 +607,10 @@ __device__ __forceinline__ void epilogue_mode(const GemmArgs& A, const NsProb& P
                     }
                 } else {
                     if constexpr (pre_ok) {
-                        if (fast) update8_pre(P, lr, wd, r, c, v, pre[fm * PASSES + pass]);
-                        else emit_u8<TS>(A, P, lr, wd, r, c, v);
+                        if (fast) update8_pre(P, us, r, c, v, pre[fm * PASSES + pass]);
+                        else emit_u8<TS>(A, P, us, r, c, v);
                     } else {
-                        emit_u8<TS>(A, P, lr, wd, r, c, v);
+                        emit_u8<TS>(A, P, us, r, c, v);
                     }
                 }
             }

@@ -49,8 +49,9 @@ class MuonAdamW(torch.optim.Optimizer):
 
     Muon group options: lr, weight_decay, momentum (mu), nesterov, ns_steps,
     coeffs (per-step (a, b, c) or None for the cubic step), precision
-    ("bf16" | "f32"), norm_eps, num_heads (int, or a callable p -> int) and
-    scale (float, or a callable p -> float; 1.0 is plain Muon).
+    ("bf16" | "f32"), norm_eps, num_heads (int, or a callable p -> int),
+    scale (float, or a callable p -> float; 1.0 is plain Muon) and cautious_wd
+    (decay only where it agrees in sign with the update).
     AdamW group options: lr, weight_decay, betas, eps.
     Tensors with more than two dimensions are orthogonalised as
     [shape[0], prod(shape[1:])] matrices.
@@ -58,7 +59,7 @@ class MuonAdamW(torch.optim.Optimizer):
 
     def __init__(self, param_groups: List[Dict], *, lr: float = 0.02, weight_decay: float = 0.0,
                  momentum: float = 0.95, nesterov: bool = True, ns_steps: int = 5, coeffs=None,
-                 precision: str = "bf16", norm_eps: float = 1e-7, num_heads=1, scale=1.0,
+                 precision: str = "bf16", norm_eps: float = 1e-7, num_heads=1, scale=1.0, cautious_wd: bool = False,
                  adamw_lr: float = 3e-4, betas=(0.9, 0.95), eps: float = 1e-8, adamw_weight_decay: float = 0.0):
         groups = []
         for g in param_groups:
@@ -70,7 +71,7 @@ class MuonAdamW(torch.optim.Optimizer):
                 for k, v in (("lr", lr), ("weight_decay", weight_decay), ("momentum", momentum),
                              ("nesterov", nesterov), ("ns_steps", ns_steps), ("coeffs", coeffs),
                              ("precision", precision), ("norm_eps", norm_eps), ("num_heads", num_heads),
-                             ("scale", scale)):
+                             ("scale", scale), ("cautious_wd", cautious_wd)):
                     g.setdefault(k, v)
             else:
                 for k, v in (("lr", adamw_lr), ("weight_decay", adamw_weight_decay), ("betas", betas),
@@ -142,7 +143,7 @@ class MuonAdamW(torch.optim.Optimizer):
             return
         mats, n = _lib.matrices(ps, gs, ms, heads, scales)
         hp, keep = _lib.muon_hparams(g["lr"], g["weight_decay"], g["momentum"], g["nesterov"], g["norm_eps"],
-                                     g["ns_steps"], g["coeffs"], g["precision"])
+                                     g["ns_steps"], g["coeffs"], g["precision"], g.get("cautious_wd", False))
         need = _lib.mu_muon_workspace_size(mats, n, hp)
         ws = self._ws(("muon", id(g)), need, ps[0].device)
         _lib.mu_muon_step(mats, n, hp, ws)

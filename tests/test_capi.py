@@ -56,7 +56,7 @@ def test_header_constants_match_the_binding(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.mu_version() == 1
+    assert lib.mu_version() == 2
     assert lib.mu_status_string(0) == "ok"
     assert "workspace" in lib.mu_status_string(lib.MU_ERR_WORKSPACE)
     assert lib.mu_status_string(99) == "unknown status"
@@ -76,7 +76,7 @@ def _mat(lib, **kw):
 
 def _hp(lib, **kw):
     d = dict(lr=0.02, weight_decay=0.01, mu=0.95, nesterov=1, norm_eps=1e-7, ns_steps=5, coeffs=None,
-             ns_precision=lib.MU_NS_BF16)
+             ns_precision=lib.MU_NS_BF16, cautious_wd=0)
     d.update(kw)
     return lib.MuMuonHparams(**d)
 
@@ -98,6 +98,7 @@ def test_bad_matrix_rejected(lib, kw, code):
 
 def test_bad_hparams_rejected(lib):
     assert _step(lib, [_mat(lib)], _hp(lib, ns_steps=-1)) == lib.MU_ERR_INVALID_ARG
+    assert _step(lib, [_mat(lib)], _hp(lib, cautious_wd=2)) == lib.MU_ERR_INVALID_ARG
     assert _step(lib, [_mat(lib)], _hp(lib, ns_precision=9)) == lib.MU_ERR_DTYPE
     assert _step(lib, [_mat(lib)], _hp(lib, lr=float("nan"))) == lib.MU_ERR_INVALID_ARG
 
