@@ -136,3 +136,34 @@ def test_two_lists_alternating_share_a_workspace():
             torch.cuda.synchronize()
             for (w, _, m), (ww, wm) in zip(sets[j], want[j]):
                 assert torch.equal(w, ww) and torch.equal(m, wm), (rep, j)
+
+
+def test_more_structures_than_the_cache_holds():
+    """Twenty list structures, each called three times (eager, capture,
+    replay), then the first five again after they were evicted from the
+    16-entry cache: every call bit for bit the eager result."""
+    import newton_schulz_orthogonalized_amd as nso
+    shapes = [(64 + 32 * i, 96 + 40 * i) for i in range(20)]
+    ins = [make_matrix_inputs(sh, 43000 + i, torch.bfloat16, 1e-3, 0.02, 1e-3) for i, sh in enumerate(shapes)]
+    snap = [(w.clone(), m.clone()) for w, _, m in ins]
+    want = []
+    for i, (w, g, m) in enumerate(ins):
+        _eager(lambda: nso.muon_step([w], [g], [m], lr=0.02, weight_decay=0.01))
+        want.append((w.clone(), m.clone()))
+        w.copy_(snap[i][0])
+        m.copy_(snap[i][1])
+
+    def check(i):
+        w, g, m = ins[i]
+        w.copy_(snap[i][0])
+        m.copy_(snap[i][1])
+        nso.muon_step([w], [g], [m], lr=0.02, weight_decay=0.01)
+        torch.cuda.synchronize()
+        assert torch.equal(w, want[i][0]) and torch.equal(m, want[i][1]), i
+
+    for i in range(20):
+        for _ in range(3):
+            check(i)
+    for i in range(5):
+        for _ in range(3):
+            check(i)
