@@ -57,12 +57,18 @@ def parse():
     return ap.parse_args()
 
 
-def source_digest() -> str:
-    """Digest of the kernel sources with comments and whitespace removed, so
+KERNEL_SOURCES = ("ns_gemm.hip", "elementwise.hip", "common.hpp", "launch.hpp")
+# the sources each profiled kernel class is built from
+KERNEL_FILES = {"apply": ("ns_gemm.hip", "common.hpp", "launch.hpp"),
+                "gram": ("ns_gemm.hip", "common.hpp", "launch.hpp")}
+
+
+def source_digest(files=KERNEL_SOURCES) -> str:
+    """Digest of kernel sources with comments and whitespace removed, so
     that recorded counter figures stay attached to the code they measured."""
     import re
     h = hashlib.sha256()
-    for f in ("ns_gemm.hip", "elementwise.hip", "common.hpp", "launch.hpp"):
+    for f in files:
         with open(os.path.join(ROOT, "newton_schulz_orthogonalized_amd", "csrc", f)) as fh:
             src = fh.read()
         src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
@@ -73,13 +79,13 @@ def source_digest() -> str:
 
 def traffic_from_profiles(kernel: str):
     """HBM bytes per launch from committed counter summaries, if they were taken
-    on the current kernel sources; else None."""
+    on the current sources of that kernel; else None."""
     path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_llama_8b.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         d = json.load(f)
-    if d.get("source_digest") != source_digest():
+    if d.get("kernel_source_digest") != source_digest(KERNEL_FILES[kernel]):
         return None
     return d.get("bytes_per_launch")
 

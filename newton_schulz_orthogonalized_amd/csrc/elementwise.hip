@@ -187,7 +187,9 @@ __global__ __launch_bounds__(NTHR) void k_prep(PrepArgs A) {
         for (int k = 0; k < 4; ++k) {
             const int64_t off = (int64_t)(ti * TR + rr + RSTEP * k) * P.ld + tj * TC + cc;
             if constexpr (sizeof(TS) == 2) {
-                const bf16x4 q = *(const MU_GLOBAL bf16x4*)((const bf16*)P.src + off);
+                // the gradient is read once: a non-temporal load (8B-shaped
+                // set, same process: 14.97 -> 14.90 ms)
+                const bf16x4 q = __builtin_nontemporal_load((const MU_GLOBAL bf16x4*)((const bf16*)P.src + off));
 #pragma unroll
                 for (int e = 0; e < 4; ++e) gk[k][e] = (float)q[e];
             } else {
@@ -491,7 +493,9 @@ __device__ __forceinline__ void adamw_chunk_bf16(const AdamWDesc& D, int64_t bas
     for (int k = 0; k < RUNS; ++k) {
         const int64_t i0 = base + (int64_t)k * NTHR * 8 + threadIdx.x * 8;
         pq[k] = *(const MU_GLOBAL bf16x8*)((const bf16*)D.param + i0);
-        gq[k] = *(const MU_GLOBAL bf16x8*)((const bf16*)D.grad + i0);
+        // the gradient is read once and never written: a non-temporal load
+        // (A/B on the 8B-shaped AdamW set, same process: +0.8 to +1.2 %)
+        gq[k] = __builtin_nontemporal_load((const MU_GLOBAL bf16x8*)((const bf16*)D.grad + i0));
         mq[k][0] = *(const MU_GLOBAL f32x4*)(D.m + i0);
         mq[k][1] = *(const MU_GLOBAL f32x4*)(D.m + i0 + 4);
         vq[k][0] = *(const MU_GLOBAL f32x4*)(D.v + i0);
