@@ -17,6 +17,10 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmuon_mi355x.so")
 SOURCES = ["capi.hip", "elementwise.hip", "ns_gemm.hip"]
+# The benchmark's ceiling probe (an MFMA loop with clock stamps), a library of
+# its own so that the optimizer library holds only the optimizer.
+PROBE_LIB = os.path.join(HERE, "libmuon_probe.so")
+PROBE_SOURCES = ["probe.hip"]
 ARCH = "gfx950"
 # Per-source extra flags. The Newton-Schulz GEMMs keep 256 accumulator AGPRs
 # and two fragment buffers live; the register-minimising scheduler keeps the
@@ -38,9 +42,9 @@ COMMON = [
 ]
 
 
-def compile_commands(objdir: str) -> list:
+def compile_commands(objdir: str, sources=None) -> list:
     cmds = []
-    for src in SOURCES:
+    for src in (SOURCES if sources is None else sources):
         obj = os.path.join(objdir, src.replace(".hip", ".o"))
         cmds.append([hipcc()] + COMMON + EXTRA.get(src, []) +
                     ["-I", os.path.join(os.path.dirname(HERE), "include"), "-c", os.path.join(CSRC, src), "-o", obj])
@@ -58,10 +62,10 @@ def _run(cmd, verbose):
         print(out, flush=True)
 
 
-def build(verbose: bool = True, out: str = LIB, host_asan: bool = False) -> str:
+def build(verbose: bool = True, out: str = LIB, host_asan: bool = False, sources=None) -> str:
     import tempfile
     with tempfile.TemporaryDirectory(prefix="mu_build_") as objdir:
-        cmds = compile_commands(objdir)
+        cmds = compile_commands(objdir, sources)
         if host_asan:   # the host half of the C ABI only; the sanitizer never reaches device code
             for c in cmds:
                 if c[c.index("-c") + 1].endswith("capi.hip"):
@@ -83,6 +87,7 @@ if __name__ == "__main__":
         build(verbose=True, out=os.path.abspath(sys.argv[2]), host_asan=True)
     elif len(sys.argv) == 1:
         build(verbose=True)
+        build(verbose=True, out=PROBE_LIB, sources=PROBE_SOURCES)
     else:
         sys.exit("usage: python -m newton_schulz_orthogonalized_amd.build [--host-asan OUT.so]")
     sys.exit(0)

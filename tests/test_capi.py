@@ -243,3 +243,15 @@ def test_tie_to_stream_records_only_other_streams(lib):
     finally:
         torch.cuda.Stream = orig
 
+
+
+def test_ceiling_probe_library_loads_and_is_separate():
+    """The benchmark's MFMA ceiling probe is a library of its own: it loads
+    without a GPU, exports its one entry point, and the optimizer library
+    exports nothing of it."""
+    path = os.path.join(ROOT, "newton_schulz_orthogonalized_amd", "libmuon_probe.so")
+    if not os.path.exists(path):
+        pytest.fail("libmuon_probe.so is not built (run __graft_entry__.build())")
+    probe = ctypes.CDLL(path)
+    assert hasattr(probe, "probe_mfma_bf16")
+    assert not hasattr(ctypes.CDLL(LIB), "probe_mfma_bf16")
