@@ -6,7 +6,9 @@ over the rest) on a transformer-shaped parameter set, on one MI355X.
 
 A step is one mu_muon_step over the whole Muon list (momentum, normalisation,
 five Newton-Schulz steps, update) plus one mu_adamw_step over the whole AdamW
-list, with every input resident in HBM. W untimed steps, then K timed steps
+list, with every input resident in HBM. W untimed steps (by default at
+least 3 and at least one second of them, so that short steps are timed at the
+clocks a training loop settles at; the JSON reports the number run), then K timed steps
 between two device synchronisations (`value`, ms per step; repeated calls
 replay their launch sequence from a HIP graph, as in a training loop), then K
 more timed steps with the library's profiler on, whose HIP events around each
@@ -44,7 +46,11 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed warm-up steps (default: at least 3, and at least --warmup-s seconds)")
+    ap.add_argument("--warmup-s", type=float, default=1.0,
+                    help="without --warmup: warm up for at least this long, so that the timed steps run at the "
+                         "clocks a training loop settles at (short steps start at lower clocks)")
     ap.add_argument("--config", default="llama_8b")
     ap.add_argument("--ns-steps", type=int, default=5)
     ap.add_argument("--coeffs", default="cubic", choices=sorted(COEFF_SCHEDULES),
@@ -308,10 +314,20 @@ def main():
             nso.adamw_step(aw["p"], aw["g"], aw["m"], aw["v"], lr=0.02, weight_decay=0.01, beta1=0.9,
                            beta2=0.95, eps=1e-8, step=state["t"], workspace=aw_ws)
 
-    for i in range(args.warmup):
+    tw = time.perf_counter()
+    done = 0
+    while True:
         step()
         torch.cuda.synchronize()
-        print(f"[bench] warmup step {i + 1}/{args.warmup} done", file=sys.stderr, flush=True)
+        done += 1
+        if args.warmup is not None:
+            print(f"[bench] warmup step {done}/{args.warmup} done", file=sys.stderr, flush=True)
+            if done >= args.warmup:
+                break
+        elif done >= 3 and time.perf_counter() - tw >= args.warmup_s:
+            break
+    args.warmup = done
+    print(f"[bench] {done} warm-up steps in {time.perf_counter() - tw:.3f} s", file=sys.stderr, flush=True)
 
     # Timed region 1: the steps as a training loop runs them (a repeated call
     # replays its launch sequence from a HIP graph). `value` comes from here.

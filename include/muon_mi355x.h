@@ -291,7 +291,8 @@ int mu_version(void);
 #define MU_K_QKCLIP 7    /* QK-Clip rescale (bytes assume every head clipped) */
 #define MU_K_FUSED 8     /* every step but the last apply of mp == 128 problems (>= 256 in a call) */
 #define MU_K_RESCALE 9   /* exact 2^e rescale of X0 where ||U||_F is outside [2^-24, 2^24] */
-#define MU_K_COUNT 10
+#define MU_K_TILEMAP 10  /* per call: each GEMM tile's problem and coordinates, resolved once */
+#define MU_K_COUNT 11
 int mu_profile_enable(int on);
 int mu_profile_read(int kernel, double* total_ms, int64_t* launches, double* flops, double* bytes);
 const char* mu_kernel_name(int kernel);

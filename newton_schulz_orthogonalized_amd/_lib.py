@@ -31,8 +31,8 @@ MU_ERR_WORKSPACE = 4
 MU_ERR_HIP = 5
 
 (MU_K_PREP, MU_K_NORM, MU_K_GRAM, MU_K_GRAM2, MU_K_APPLY, MU_K_FINISH, MU_K_ADAMW, MU_K_QKCLIP, MU_K_FUSED,
- MU_K_RESCALE) = range(10)
-MU_K_COUNT = 10
+ MU_K_RESCALE, MU_K_TILEMAP) = range(11)
+MU_K_COUNT = 11
 
 EXPORTED = (
     "mu_muon_workspace_size", "mu_muon_step", "mu_muon_step_noalloc", "mu_ortho_workspace_size",

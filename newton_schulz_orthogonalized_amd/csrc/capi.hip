@@ -125,6 +125,7 @@ struct Group {
     std::vector<int> gram_order;   // group-local problem index at each Gram prefix position
     std::vector<int> apply_order;  // the same for the apply
     std::vector<int> gram_prefix, apply_prefix;
+    size_t gram_tmap, apply_tmap;  // offsets of its tile maps in the workspace
 };
 
 // Gram tile order and XCD windows. The Gram launches walk a group's problems
@@ -171,7 +172,7 @@ struct Plan {
     bool quintic;
     // workspace layout (the uploaded table: call scalars, descriptors, prefixes)
     size_t off_scalars, off_table, off_prep_prefix, off_group_prefix, table_bytes;
-    size_t off_partials, off_fold, off_xexp, off_bufs, total;
+    size_t off_partials, off_fold, off_xexp, off_tmap, off_bufs, total;
     int64_t total_parts;
 };
 
@@ -310,6 +311,14 @@ void build_plan(const std::vector<Item>& items, int ns_dt, const std::vector<Coe
     o = align_up(o + sizeof(float) * P);
     pl.off_xexp = o;
     o = align_up(o + sizeof(int32_t) * P);
+    pl.off_tmap = o;   // written on the device by each call's tile-map launch
+    for (auto& g : pl.groups) {
+        g.gram_tmap = o;
+        if (!g.fused) o += sizeof(TileEntry) * (size_t)g.gram_prefix.back();
+        g.apply_tmap = o;
+        o += sizeof(TileEntry) * (size_t)g.apply_prefix.back();
+    }
+    o = align_up(o);
     pl.off_bufs = o;
     for (auto& pp : pl.probs) o += (pp.d.xt_used ? 4 : 2) * pp.x_bytes + pp.a_bytes * (pl.quintic ? 2 : 1);
     pl.total = o;
@@ -624,6 +633,30 @@ int launch_sequence(const Plan& pl, char* ws, const mu_muon_hparams* hp, int src
             o += sizeof(int) * g.apply_prefix.size();
         }
     }
+    // tile maps of every GEMM launch of the call (the table above is in place)
+    {
+        TileMapArgs ta{};
+        for (size_t gi = 0; gi < pl.groups.size(); ++gi) {
+            const Group& g = pl.groups[gi];
+            for (int sym = 1; sym >= 0; --sym) {
+                if (sym && g.fused) continue;   // no Gram launches: the fused kernel runs them
+                if (ta.nseg >= TILEMAP_SEGS) return fail(MU_ERR_INVALID_ARG, "too many tile groups");
+                TileMapSeg& sg = ta.seg[ta.nseg++];
+                sg.prefix = sym ? gram_pf[gi] : apply_pf[gi];
+                sg.order = sym ? gram_ord[gi] : apply_ord[gi];
+                sg.probs = dprobs + g.first;
+                sg.out = (TileEntry*)(ws + (sym ? g.gram_tmap : g.apply_tmap));
+                sg.nprobs = g.count;
+                sg.start = ta.total;
+                sg.ts = g.tile;
+                sg.sym = sym;
+                ta.total += sym ? g.gram_prefix.back() : g.apply_prefix.back();
+            }
+        }
+        rc = timed_launch(MU_K_TILEMAP, 0.0, 8.0 * ta.total, s, [&] { return launch_tilemap(ta, s); },
+                          "tile map launch");
+        if (rc) return rc;
+    }
     // fused problems: every step but the last apply in one launch
     for (const Group& g : pl.groups) {
         if (!g.fused) continue;
@@ -662,7 +695,6 @@ int launch_sequence(const Plan& pl, char* ws, const mu_muon_hparams* hp, int src
             }
             GemmArgs ga{};
             ga.probs = dprobs + g.first;
-            ga.nprobs = g.count;
             ga.src = src;
             ga.src_dtype = src_dt;
             ga.ca = co[k].a;
@@ -678,8 +710,7 @@ int launch_sequence(const Plan& pl, char* ws, const mu_muon_hparams* hp, int src
             if (g.fused) {
                 GemmArgs ap = ga;
                 ap.mode = GM_APPLY_LAST;
-                ap.prefix = apply_pf[gi];
-                ap.order = apply_ord[gi];
+                ap.tmap = (const TileEntry*)(ws + g.apply_tmap);
                 ap.total_tiles = g.apply_prefix.back();
                 rc = timed_launch(MU_K_APPLY, aflops, abytes, s, [&] { return launch(ap); }, "apply launch");
                 if (rc) return rc;
@@ -687,8 +718,7 @@ int launch_sequence(const Plan& pl, char* ws, const mu_muon_hparams* hp, int src
             }
             GemmArgs gg = ga;
             gg.mode = GM_GRAM;
-            gg.prefix = gram_pf[gi];
-            gg.order = gram_ord[gi];
+            gg.tmap = (const TileEntry*)(ws + g.gram_tmap);
             gg.total_tiles = g.gram_prefix.back();
             gg.first = first ? 1 : 0;
             gg.xcd_window = g.gram_window;
@@ -697,8 +727,7 @@ int launch_sequence(const Plan& pl, char* ws, const mu_muon_hparams* hp, int src
             if (quint) {
                 GemmArgs g2 = ga;
                 g2.mode = GM_GRAM2;
-                g2.prefix = gram_pf[gi];
-                g2.order = gram_ord[gi];
+                g2.tmap = (const TileEntry*)(ws + g.gram_tmap);
                 g2.total_tiles = g.gram_prefix.back();
                 g2.first = first ? 1 : 0;
                 g2.xcd_window = g.gram_window;
@@ -707,8 +736,7 @@ int launch_sequence(const Plan& pl, char* ws, const mu_muon_hparams* hp, int src
             }
             GemmArgs ap = ga;
             ap.mode = last ? GM_APPLY_LAST : GM_APPLY;
-            ap.prefix = apply_pf[gi];
-            ap.order = apply_ord[gi];
+            ap.tmap = (const TileEntry*)(ws + g.apply_tmap);
             ap.total_tiles = g.apply_prefix.back();
             ap.first = first ? 1 : 0;
             rc = timed_launch(MU_K_APPLY, aflops, abytes, s, [&] { return launch(ap); }, "apply launch");
@@ -1357,6 +1385,7 @@ const char* mu_kernel_name(int k) {
         case MU_K_QKCLIP: return "qk_clip";
         case MU_K_FUSED: return "ns_fused";
         case MU_K_RESCALE: return "rescale";
+        case MU_K_TILEMAP: return "tile_map";
         default: return "unknown";
     }
 }

@@ -75,12 +75,16 @@ enum GemmMode : int {
     GM_APPLY_LAST = 3,  // as GM_APPLY, result O goes to the update or to `out`
 };
 
+// Logical tile t of a GEMM launch, resolved once per call by k_tilemap:
+// problem p (an index into GemmArgs::probs) and tile coordinates ti | tj << 16
+// (both below 2^15: a side of at most 2^21 elements in tiles of 64 or more).
+struct TileEntry {
+    int32_t p;
+    int32_t tij;
+};
 struct GemmArgs {
     const NsProb* probs;
-    const int* prefix;   // nprobs+1 cumulative tiles for this mode
-    const int* order;    // problem at each prefix position (the tile order runs
-                         // through the problems in this order); null: identity
-    int nprobs;
+    const TileEntry* tmap;   // one entry per logical tile of this launch
     int total_tiles;
     int mode;
     int src;             // which x[] buffer holds the current X
@@ -95,6 +99,28 @@ struct GemmArgs {
 // tile: 256 or 128 (square tiles, bf16) ; float32 uses 64.
 hipError_t launch_gemm_bf16(const GemmArgs& a, int tile, hipStream_t s);
 hipError_t launch_gemm_f32(const GemmArgs& a, hipStream_t s);
+
+// The tile maps of one call: per segment (a tile group's Gram or apply
+// order), entry t of `out` for logical tile t, found from the segment's tile
+// prefix over its problems (taken in `order`) and the tile enumeration of the
+// GEMM kernels. One thread per tile over all segments.
+constexpr int TILEMAP_SEGS = 8;   // 4 tile groups x (Gram, apply)
+struct TileMapSeg {
+    const int* prefix;     // nprobs+1 cumulative tiles
+    const int* order;      // group-local problem at each prefix position
+    const NsProb* probs;   // the group's problems
+    TileEntry* out;
+    int nprobs;
+    int start;             // first thread of this segment
+    int ts;                // tile size
+    int sym;               // upper-triangle (Gram) enumeration
+};
+struct TileMapArgs {
+    TileMapSeg seg[TILEMAP_SEGS];
+    int nseg;
+    int total;
+};
+hipError_t launch_tilemap(const TileMapArgs& a, hipStream_t s);
 
 // Newton-Schulz for problems with mp == 128 (bf16, cubic steps) up to the last
 // apply, in one launch, one workgroup per problem. X0 is in x[0]; the steps

@@ -10,8 +10,9 @@
 // the apply is a plain product.
 //
 // All products are grouped GEMMs over every (matrix, head) problem of a call:
-// one launch per mode covers all problems, each workgroup finds its problem
-// by binary search over a tile prefix, and workgroup ids are remapped so that
+// one launch per mode covers all problems, each workgroup reads its problem
+// and tile coordinates from the call's tile map (built once per call from the
+// tile prefix over the problems), and workgroup ids are remapped so that
 // neighbouring tiles run on the same XCD (shared L2).
 //
 // The Gram X X^T is "NT" (C = P Q^T, both operands K-contiguous) and reads X
@@ -110,6 +111,24 @@ __device__ __forceinline__ void apply_tile(int local, int TM, int TN, int& ti, i
     const int gm = min(G, TM - g * G);
     ti = g * G + w % gm;
     tj = w / gm;
+}
+
+// Tile maps (see TileMapArgs): the same enumerations as the GEMMs above.
+__global__ __launch_bounds__(NTHR) void k_tilemap(TileMapArgs A) {
+    const int t = blockIdx.x * NTHR + threadIdx.x;
+    if (t >= A.total) return;
+    int s = 0;
+    while (s + 1 < A.nseg && t >= A.seg[s + 1].start) ++s;
+    const TileMapSeg S = A.seg[s];
+    const int local = t - S.start;
+    const int ps = find_prob(S.prefix, S.nprobs, local);
+    const int p = S.order ? S.order[ps] : ps;
+    const int in_prob = local - S.prefix[ps];
+    const int T = S.probs[p].mp / S.ts;
+    int ti, tj;
+    if (S.sym) upper_tile(in_prob, T, ti, tj);
+    else apply_tile(in_prob, T, S.probs[p].np / S.ts, ti, tj);
+    S.out[local] = TileEntry{p, ti | (tj << 16)};
 }
 
 // ---------------------------------------------------------------------------
@@ -694,14 +713,14 @@ __global__ __launch_bounds__(NTHR) void k_gemm_bf16(GemmArgs A) {
     const int wg = SYM ? xcd_remap_window(blockIdx.x, gridDim.x, A.xcd_window)
                        : xcd_remap_window(blockIdx.x, gridDim.x, 256);
     if (wg >= A.total_tiles) return;
-    const int ps = __builtin_amdgcn_readfirstlane(find_prob(A.prefix, A.nprobs, wg));
-    const int p = A.order ? __builtin_amdgcn_readfirstlane(A.order[ps]) : ps;
+    // the tile, resolved ahead by k_tilemap: one load where a search over the
+    // problems' tile prefix took a chain of dependent ones
+    const TileEntry te = A.tmap[wg];
+    const int p = __builtin_amdgcn_readfirstlane(te.p);
+    const int tij = __builtin_amdgcn_readfirstlane(te.tij);
     const NsProb P = A.probs[p];   // by value: held in registers, never re-read after a store
-    const int local = wg - A.prefix[ps];
     const int mode = A.mode;
-    int ti, tj;
-    if (SYM) upper_tile(local, P.mp / TS, ti, tj);
-    else apply_tile(local, P.mp / TS, P.np / TS, ti, tj);
+    const int ti = tij & 0xffff, tj = tij >> 16;
 
     // Gram modes: C = P Q^T over K, P and Q K-blocked with RP and RQ rows.
     // Apply: C = B X, B K-blocked (mp rows, k = mp) and X itself (mp rows,
@@ -930,14 +949,14 @@ __global__ __launch_bounds__(NTHR) void k_gemm_f32(GemmArgs A) {
 
     const int wg = xcd_remap(blockIdx.x, gridDim.x);
     if (wg >= A.total_tiles) return;
-    const int ps = __builtin_amdgcn_readfirstlane(find_prob(A.prefix, A.nprobs, wg));
-    const int p = A.order ? __builtin_amdgcn_readfirstlane(A.order[ps]) : ps;
+    // the tile, resolved ahead by k_tilemap: one load where a search over the
+    // problems' tile prefix took a chain of dependent ones
+    const TileEntry te = A.tmap[wg];
+    const int p = __builtin_amdgcn_readfirstlane(te.p);
+    const int tij = __builtin_amdgcn_readfirstlane(te.tij);
     const NsProb P = A.probs[p];   // by value: held in registers, never re-read after a store
-    const int local = wg - A.prefix[ps];
     const int mode = A.mode;
-    int ti, tj;
-    if (SYM) upper_tile(local, P.mp / TS, ti, tj);
-    else apply_tile(local, P.mp / TS, P.np / TS, ti, tj);
+    const int ti = tij & 0xffff, tj = tij >> 16;
 
     const float *pm, *qm;
     int ldp, ldq, K;
@@ -1307,6 +1326,13 @@ hipError_t launch_gemm_f32(const GemmArgs& a, hipStream_t s) {
         if (sym) hipLaunchKernelGGL((k_gemm_f32<true, float>), dim3(grid), dim3(NTHR), 0, s, a);
         else hipLaunchKernelGGL((k_gemm_f32<false, float>), dim3(grid), dim3(NTHR), 0, s, a);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_tilemap(const TileMapArgs& a, hipStream_t s) {
+    if (a.total <= 0) return hipSuccess;
+    if (a.nseg < 1 || a.nseg > TILEMAP_SEGS) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_tilemap, dim3((unsigned)((a.total + NTHR - 1) / NTHR)), dim3(NTHR), 0, s, a);
     return hipGetLastError();
 }
 
