@@ -85,6 +85,9 @@ struct TileEntry {
 struct GemmArgs {
     const NsProb* probs;
     const TileEntry* tmap;   // one entry per logical tile of this launch
+    int* queues;             // persistent launches: 8 tile counters (one per XCD), zero at launch
+    int grid;                // workgroups launched: one per logical tile (padded to 8), or fewer,
+                             // each then running tiles until every XCD's queue is empty
     int total_tiles;
     int mode;
     int src;             // which x[] buffer holds the current X
@@ -119,6 +122,8 @@ struct TileMapArgs {
     TileMapSeg seg[TILEMAP_SEGS];
     int nseg;
     int total;
+    int* queues;     // the call's tile counters, cleared here
+    int nqueues;
 };
 hipError_t launch_tilemap(const TileMapArgs& a, hipStream_t s);
 

@@ -116,6 +116,7 @@ __device__ __forceinline__ void apply_tile(int local, int TM, int TN, int& ti, i
 // Tile maps (see TileMapArgs): the same enumerations as the GEMMs above.
 __global__ __launch_bounds__(NTHR) void k_tilemap(TileMapArgs A) {
     const int t = blockIdx.x * NTHR + threadIdx.x;
+    if (t < A.nqueues) A.queues[t] = 0;
     if (t >= A.total) return;
     int s = 0;
     while (s + 1 < A.nseg && t >= A.seg[s + 1].start) ++s;
@@ -686,6 +687,31 @@ constexpr int BUF_RAW32 = 0x00020000;
 // s_waitcnt with vmcnt and lgkmcnt(0)
 #define MU_WAIT_VMCNT_LGKM0(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (0 << 8) | (((n) >> 4) << 14))
 
+// Persistent launches. XCD x's queue is the list of tiles it receives in a
+// one-tile-per-workgroup launch (positions x, x+8, .. of that grid through the
+// window remap), handed out in that order by an atomic counter; a workgroup
+// whose queue is empty moves on to the next XCD's. The clocks of the XCDs
+// differ by up to 10 % under the GEMMs, so a fixed share per XCD leaves the
+// fast ones idle at the end of every launch; this way they take over the
+// slow ones' last tiles. Returns -1 once every queue is empty: a queue seen
+// empty stays empty, so one pass over the eight ends the search.
+__device__ __forceinline__ int xcc_id() {
+    return (int)(__builtin_amdgcn_s_getreg((15 << 11) | 20) & 7);   // HW_REG_XCC_ID, bits 3:0
+}
+__device__ __forceinline__ int next_tile(const GemmArgs& A, int& q, int n, int gstat, int win) {
+    const int nper = gstat >> 3;
+    for (int empty = 0;;) {
+        if (n < nper) {
+            const int t = xcd_remap_window(q + 8 * n, gstat, win);
+            if (t < A.total_tiles) return t;
+        } else {
+            if (++empty == 8) return -1;
+            q = (q + 1) & 7;
+        }
+        n = atomicAdd(A.queues + q, 1);
+    }
+}
+
 template <int TS, bool SYM, typename TSRC>
 __global__ __launch_bounds__(NTHR) void k_gemm_bf16(GemmArgs A) {
     constexpr int BK = 32;
@@ -710,9 +736,28 @@ __global__ __launch_bounds__(NTHR) void k_gemm_bf16(GemmArgs A) {
     // tiles per XCD (same-box sweep on the 8B-shaped set, ms per launch:
     // contiguous 40.2, windows of 128: 40.8, 256: 39.9, 512: 40.2, 1024: 40.2;
     // other sets unchanged)
-    const int wg = SYM ? xcd_remap_window(blockIdx.x, gridDim.x, A.xcd_window)
-                       : xcd_remap_window(blockIdx.x, gridDim.x, 256);
-    if (wg >= A.total_tiles) return;
+    const int win = SYM ? A.xcd_window : 256;
+    const int gstat = (A.total_tiles + 7) / 8 * 8;
+    // persistent Gram launches only: the apply kernel's registers are all in
+    // use (its last-apply epilogue loads a whole block of parameters up front),
+    // and the loop spilled 57 of them (apply 1-12 % slower, 8B to per-head set)
+    const bool persist = SYM && A.grid < gstat;
+    __shared__ int s_tile;
+    int q = 0, ticket = 0;   // persistent: thread 0's queue, and the ticket it took for the next tile
+    int wg;
+    if (!persist) {
+        wg = xcd_remap_window(blockIdx.x, gstat, win);
+        if (wg >= A.total_tiles) return;
+    } else {
+        if (threadIdx.x == 0) {
+            q = xcc_id();
+            s_tile = next_tile(A, q, atomicAdd(A.queues + q, 1), gstat, win);
+        }
+        __syncthreads();
+        wg = __builtin_amdgcn_readfirstlane(s_tile);
+        if (wg < 0) return;
+    }
+    for (;;) {
     // the tile, resolved ahead by k_tilemap: one load where a search over the
     // problems' tile prefix took a chain of dependent ones
     const TileEntry te = A.tmap[wg];
@@ -931,7 +976,17 @@ __global__ __launch_bounds__(NTHR) void k_gemm_bf16(GemmArgs A) {
     static_assert(LS * sizeof(bf16) == (WT / 2) * 64 * sizeof(float), "a staging half is WT/2 x 64 floats");
     float* st = (float*)(wave == 0 ? sA0 : wave == 1 ? sA1 : wave == 2 ? sA2 : sA3);
     float* st2 = (float*)(wave == 0 ? sB0 : wave == 1 ? sB1 : wave == 2 ? sB2 : sB3);
+    // the next tile's ticket, taken here so that the epilogue hides its latency
+    // (and after the K loop, whose waits count only the direct loads)
+    if (persist && threadIdx.x == 0) ticket = atomicAdd(A.queues + q, 1);
     epilogue<SYM, bf16, TSRC, F>(A, P, ti, tj, TS, wm0, wn0, acc, st, st2);
+    if (!persist) return;
+    __syncthreads();   // every wave is done with the LDS: its staging is the next tile's ring
+    if (threadIdx.x == 0) s_tile = next_tile(A, q, ticket, gstat, win);
+    __syncthreads();
+    wg = __builtin_amdgcn_readfirstlane(s_tile);
+    if (wg < 0) return;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -1299,7 +1354,7 @@ __global__ __launch_bounds__(NTHR) void k_ns_small(SmallArgs A) {
 
 template <int TS, bool SYM>
 hipError_t launch_bf16_t(const GemmArgs& a, hipStream_t s) {
-    const unsigned grid = (unsigned)((a.total_tiles + 7) / 8 * 8);
+    const unsigned grid = (unsigned)a.grid;
     if (a.src_dtype == DT_BF16) hipLaunchKernelGGL((k_gemm_bf16<TS, SYM, bf16>), dim3(grid), dim3(NTHR), 0, s, a);
     else hipLaunchKernelGGL((k_gemm_bf16<TS, SYM, float>), dim3(grid), dim3(NTHR), 0, s, a);
     return hipGetLastError();
@@ -1309,7 +1364,9 @@ hipError_t launch_bf16_t(const GemmArgs& a, hipStream_t s) {
 
 hipError_t launch_gemm_bf16(const GemmArgs& a, int tile, hipStream_t s) {
     if (a.total_tiles <= 0) return hipSuccess;
+    const int gstat = (a.total_tiles + 7) / 8 * 8;
     const bool sym = a.mode == GM_GRAM || a.mode == GM_GRAM2;
+    if (a.grid < 1 || a.grid > gstat || (a.grid < gstat && (!a.queues || !sym))) return hipErrorInvalidValue;
     if (tile == 256) return sym ? launch_bf16_t<256, true>(a, s) : launch_bf16_t<256, false>(a, s);
     if (tile == 128) return sym ? launch_bf16_t<128, true>(a, s) : launch_bf16_t<128, false>(a, s);
     return hipErrorInvalidValue;
@@ -1330,9 +1387,10 @@ hipError_t launch_gemm_f32(const GemmArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_tilemap(const TileMapArgs& a, hipStream_t s) {
-    if (a.total <= 0) return hipSuccess;
-    if (a.nseg < 1 || a.nseg > TILEMAP_SEGS) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_tilemap, dim3((unsigned)((a.total + NTHR - 1) / NTHR)), dim3(NTHR), 0, s, a);
+    const int n = a.total > a.nqueues ? a.total : a.nqueues;
+    if (n <= 0) return hipSuccess;
+    if (a.nseg < 0 || a.nseg > TILEMAP_SEGS) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_tilemap, dim3((unsigned)((n + NTHR - 1) / NTHR)), dim3(NTHR), 0, s, a);
     return hipGetLastError();
 }
 
