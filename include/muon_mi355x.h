@@ -21,9 +21,10 @@
  * profiling is on, for the no-allocation call, and when the environment
  * variable MU_GRAPHS is 0.
  *
- * Large Gram launches (at least 8 tiles per compute unit) run one workgroup
- * per compute unit, each taking tiles from its XCD's queue and then from the
- * other XCDs' queues; results are bit for bit those of one workgroup per tile,
+ * Large Gram and apply launches (at least 8 tiles per compute unit; not the
+ * last apply, which writes the update) run one workgroup per compute unit,
+ * each taking tiles from its XCD's queue and then from the other XCDs' queues;
+ * results are bit for bit those of one workgroup per tile,
  * which the environment variable MU_PERSIST = 0 selects (read at each call that
  * plans or captures its launches).
  *

@@ -692,10 +692,12 @@ int launch_sequence(const Plan& pl, char* ws, const mu_muon_hparams* hp, int src
                           "tile map launch");
         if (rc) return rc;
     }
-    // Gram launches of at least PERSIST_MIN tiles per workgroup slot run one
-    // workgroup per slot, each taking tiles from its XCD's queue until all are
-    // empty (same process, alternating builds: 8B-shaped Gram 20.99 -> 20.25 ms
-    // per launch, 1B-shaped unchanged); other launches run one workgroup per tile.
+    // Gram and apply launches of at least PERSIST_MIN tiles per workgroup slot
+    // (but not the last apply) run one workgroup per slot, each taking tiles
+    // from its XCD's queue until all are empty. Same process, alternating
+    // builds, ms per launch: 8B-shaped Gram 21.96 -> 20.69, apply (five
+    // launches, four persistent) 40.49 -> 39.71; 1B-shaped Gram 1.973 -> 1.945,
+    // apply 4.107 -> 4.028. Smaller launches run one workgroup per tile.
     int cus = 0;
     rc = cu_count(&cus);
     if (rc) return rc;
@@ -709,8 +711,7 @@ int launch_sequence(const Plan& pl, char* ws, const mu_muon_hparams* hp, int src
         if (ns_dt != DT_BF16) return;
         const int slots = tile == 256 ? cus : 2 * cus;   // workgroups per CU: 1 (256 tiles), 2 (128)
         a.queues = (int*)(ws + pl.off_queues) + 8 * gemm_index++;
-        const bool sym = a.mode == GM_GRAM || a.mode == GM_GRAM2;
-        if (persist_on && sym && a.total_tiles >= PERSIST_MIN * slots) a.grid = slots;
+        if (persist_on && a.mode != GM_APPLY_LAST && a.total_tiles >= PERSIST_MIN * slots) a.grid = slots;
     };
     // fused problems: every step but the last apply in one launch
     for (const Group& g : pl.groups) {

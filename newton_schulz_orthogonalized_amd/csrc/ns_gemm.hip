@@ -651,6 +651,14 @@ __device__ __forceinline__ void epilogue(const GemmArgs& A, const NsProb& P, int
         else epilogue_mode<GM_APPLY_LAST, TX, TS, F>(A, P, ti, tj, TS_, wm0, wn0, acc, st, st2);
     }
 }
+// The bf16 kernel's epilogues: LAST (the last apply) has a kernel of its own.
+template <bool SYM, bool LAST, typename TX, typename TS, int F>
+__device__ __forceinline__ void epilogue_k(const GemmArgs& A, const NsProb& P, int ti, int tj, int TS_, int wm0,
+                                           int wn0, f32x4 (&acc)[F][F], float* st, float* st2) {
+    if constexpr (SYM) epilogue<true, TX, TS, F>(A, P, ti, tj, TS_, wm0, wn0, acc, st, st2);
+    else if constexpr (LAST) epilogue_mode<GM_APPLY_LAST, TX, TS, F>(A, P, ti, tj, TS_, wm0, wn0, acc, st, st2);
+    else epilogue_mode<GM_APPLY, TX, TS, F>(A, P, ti, tj, TS_, wm0, wn0, acc, st, st2);
+}
 
 // ---------------------------------------------------------------------------
 // bf16 kernel
@@ -712,7 +720,7 @@ __device__ __forceinline__ int next_tile(const GemmArgs& A, int& q, int n, int g
     }
 }
 
-template <int TS, bool SYM, typename TSRC>
+template <int TS, bool SYM, typename TSRC, bool LAST>
 __global__ __launch_bounds__(NTHR) void k_gemm_bf16(GemmArgs A) {
     constexpr int BK = 32;
     constexpr int NS = 4;
@@ -738,10 +746,9 @@ __global__ __launch_bounds__(NTHR) void k_gemm_bf16(GemmArgs A) {
     // other sets unchanged)
     const int win = SYM ? A.xcd_window : 256;
     const int gstat = (A.total_tiles + 7) / 8 * 8;
-    // persistent Gram launches only: the apply kernel's registers are all in
-    // use (its last-apply epilogue loads a whole block of parameters up front),
-    // and the loop spilled 57 of them (apply 1-12 % slower, 8B to per-head set)
-    const bool persist = SYM && A.grid < gstat;
+    // not the last apply: its epilogue loads a whole block of parameters up
+    // front, and with the loop its kernel spilled 57 registers (1-12 % slower)
+    const bool persist = !LAST && A.grid < gstat;
     __shared__ int s_tile;
     int q = 0, ticket = 0;   // persistent: thread 0's queue, and the ticket it took for the next tile
     int wg;
@@ -979,7 +986,7 @@ __global__ __launch_bounds__(NTHR) void k_gemm_bf16(GemmArgs A) {
     // the next tile's ticket, taken here so that the epilogue hides its latency
     // (and after the K loop, whose waits count only the direct loads)
     if (persist && threadIdx.x == 0) ticket = atomicAdd(A.queues + q, 1);
-    epilogue<SYM, bf16, TSRC, F>(A, P, ti, tj, TS, wm0, wn0, acc, st, st2);
+    epilogue_k<SYM, LAST, bf16, TSRC, F>(A, P, ti, tj, TS, wm0, wn0, acc, st, st2);
     if (!persist) return;
     __syncthreads();   // every wave is done with the LDS: its staging is the next tile's ring
     if (threadIdx.x == 0) s_tile = next_tile(A, q, ticket, gstat, win);
@@ -1355,8 +1362,15 @@ __global__ __launch_bounds__(NTHR) void k_ns_small(SmallArgs A) {
 template <int TS, bool SYM>
 hipError_t launch_bf16_t(const GemmArgs& a, hipStream_t s) {
     const unsigned grid = (unsigned)a.grid;
-    if (a.src_dtype == DT_BF16) hipLaunchKernelGGL((k_gemm_bf16<TS, SYM, bf16>), dim3(grid), dim3(NTHR), 0, s, a);
-    else hipLaunchKernelGGL((k_gemm_bf16<TS, SYM, float>), dim3(grid), dim3(NTHR), 0, s, a);
+    // the parameter dtype matters only to the last apply's update
+    if (!SYM && a.mode == GM_APPLY_LAST) {
+        if (a.src_dtype == DT_BF16)
+            hipLaunchKernelGGL((k_gemm_bf16<TS, false, bf16, true>), dim3(grid), dim3(NTHR), 0, s, a);
+        else
+            hipLaunchKernelGGL((k_gemm_bf16<TS, false, float, true>), dim3(grid), dim3(NTHR), 0, s, a);
+    } else {
+        hipLaunchKernelGGL((k_gemm_bf16<TS, SYM, bf16, false>), dim3(grid), dim3(NTHR), 0, s, a);
+    }
     return hipGetLastError();
 }
 
@@ -1366,7 +1380,8 @@ hipError_t launch_gemm_bf16(const GemmArgs& a, int tile, hipStream_t s) {
     if (a.total_tiles <= 0) return hipSuccess;
     const int gstat = (a.total_tiles + 7) / 8 * 8;
     const bool sym = a.mode == GM_GRAM || a.mode == GM_GRAM2;
-    if (a.grid < 1 || a.grid > gstat || (a.grid < gstat && (!a.queues || !sym))) return hipErrorInvalidValue;
+    if (a.grid < 1 || a.grid > gstat || (a.grid < gstat && (!a.queues || a.mode == GM_APPLY_LAST)))
+        return hipErrorInvalidValue;
     if (tile == 256) return sym ? launch_bf16_t<256, true>(a, s) : launch_bf16_t<256, false>(a, s);
     if (tile == 128) return sym ? launch_bf16_t<128, true>(a, s) : launch_bf16_t<128, false>(a, s);
     return hipErrorInvalidValue;

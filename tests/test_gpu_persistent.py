@@ -1,12 +1,13 @@
-"""Persistent Gram launches: a Gram launch of at least 8 tiles per compute
-unit runs one workgroup per compute unit, and each takes tiles from its XCD's
-queue (the tiles that XCD would run in a one-workgroup-per-tile launch, in the
-same order), then from the other XCDs' queues. Every tile is computed by one
-workgroup with the same arithmetic, so the result must be bit for bit that of
-the one-workgroup-per-tile launch (MU_PERSIST=0), for cubic steps and for
-quintic steps (whose A A^T pass is a Gram launch as well). Sixteen 4096 x 4096
-matrices give 16 x 136 = 2176 Gram tiles of 256 x 256, above the threshold of
-8 x 256 compute units. (The one-workgroup-per-tile path is held to the
+"""Persistent launches: a Gram or apply launch (but not the last apply) of at
+least 8 tiles per compute unit runs one workgroup per compute unit, and each
+takes tiles from its XCD's queue (the tiles that XCD would run in a
+one-workgroup-per-tile launch, in the same order), then from the other XCDs'
+queues. Every tile is computed by one workgroup with the same arithmetic, so
+the result must be bit for bit that of the one-workgroup-per-tile launch
+(MU_PERSIST=0), for cubic steps and for quintic steps (whose A A^T pass is a
+Gram launch as well). Sixteen 4096 x 4096 matrices give 16 x 136 = 2176 Gram
+tiles and 4096 apply tiles of 256 x 256, above the threshold of 8 x 256
+compute units. (The one-workgroup-per-tile path is held to the
 oracle by every other parity test, among them the 8B-shaped set, whose Gram
 launches are persistent by default.)
 """
@@ -30,7 +31,7 @@ QUINTIC = [(1.875, -1.25, 0.375)] * 5
 
 
 @pytest.mark.parametrize("coeffs", [None, QUINTIC], ids=["cubic", "quintic"])
-def test_persistent_gram_matches_one_workgroup_per_tile(coeffs, monkeypatch):
+def test_persistent_launches_match_one_workgroup_per_tile(coeffs, monkeypatch):
     import newton_schulz_orthogonalized_amd as nso
     from newton_schulz_orthogonalized_amd import _lib as L
     props = torch.cuda.get_device_properties(0)
