@@ -694,6 +694,8 @@ constexpr int BUF_RAW32 = 0x00020000;
 #define MU_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14))
 // s_waitcnt with vmcnt and lgkmcnt(0)
 #define MU_WAIT_VMCNT_LGKM0(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (0 << 8) | (((n) >> 4) << 14))
+// s_waitcnt lgkmcnt(0) only
+#define MU_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14))
 
 // Persistent launches. XCD x's queue is the list of tiles it receives in a
 // one-tile-per-workgroup launch (positions x, x+8, .. of that grid through the
@@ -1103,9 +1105,10 @@ __global__ __launch_bounds__(NTHR) void k_gemm_f32(GemmArgs A) {
 // matrix whose short side is at most 128) in one workgroup, up to the last
 // apply. Such short, wide problems are bound by HBM, and the tiled path moves X
 // through it three times per step (the Gram reads X, the apply reads X and
-// writes X'). Here B (128 x 128) stays in LDS and each step streams X once,
+// writes X'). Here B (128 x 128) stays on chip and each step streams X once,
 // in blocks of 128 columns (one contiguous 32 KB run each):
-//   X'_j = B X_j            (B from LDS, X_j through transposed LDS reads)
+//   X'_j^T = X_j^T B        (X_j through transposed LDS reads, B from
+//                            registers; B is symmetric, so this is (B X_j)^T)
 //   A' += X'_j X'_j^T       (from a K-blocked LDS copy of X'_j, bf16 as stored)
 //   X'_j -> HBM             (that LDS copy, which has X's layout: the next
 //                            step's input)
@@ -1113,38 +1116,39 @@ __global__ __launch_bounds__(NTHR) void k_gemm_f32(GemmArgs A) {
 // A'. The first B = f (a I + b f^2 X0 X0^T) comes from one pass over X0. The
 // B of the last step is copied to the problem's `a` buffer, and the tiled last
 // apply (which fuses the parameter update) finishes the run.
-// X blocks are double-buffered with direct-to-LDS loads. The wait at a block
-// boundary covers the previous block's stores too: loads and stores share
-// vmcnt, which does not order one against the other.
-// 4 waves in 2 x 2, each 64 x 64 of X'_j (64 AGPRs) and of A' (64 AGPRs).
+// LDS traffic is kept low: each wave holds its 64 rows of B in registers for
+// the whole step (loaded from LDS once per step), and computing X'^T puts,
+// after a lane swap, 8 consecutive columns of one row of X' in a lane: one
+// 16-byte chunk of the K-blocked copy, written to LDS straight from registers
+// with no float staging (288 KB of LDS traffic per block, against 480 KB for
+// B X with B read from LDS and X' staged as floats). The loads of block j+1
+// stay in flight through block j's whole epilogue, store and Gram: the
+// barrier after the copy waits for LDS writes only. Per-head set, same
+// process: 1.465 -> 1.399 ms per launch, results bit for bit the same. (Two
+// workgroups per compute unit, with 64-column blocks in 80 KB of LDS, ran 6 %
+// slower.)
+// 4 waves in 2 x 2: the apply 64 x 64 of X'^T (64 AGPRs), the Gram 64 x 64 of
+// A' (64 AGPRs).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(NTHR) void k_ns_small(SmallArgs A) {
-    constexpr int M = 128, BK = 32, WT = 64, F = 4, SP = WT + 4;
+    constexpr int M = 128, BK = 32, BW = 128;
     constexpr int SLICE = M * BK;   // a 32-wide k-slice of a 128-row K-blocked operand (8 KB)
     constexpr int OPB = 4 * SLICE;  // a 128 x 128 operand (32 KB)
-    constexpr int PASSES = WT / 32;
-    __shared__ __attribute__((aligned(1024))) bf16 sB[OPB];   // B, left operand of the apply
-    __shared__ __attribute__((aligned(1024))) bf16 sX0[OPB];  // X^T (or X0) blocks, even j
-    __shared__ __attribute__((aligned(1024))) bf16 sX1[OPB];  // odd j
-    __shared__ __attribute__((aligned(1024))) bf16 sG[OPB];   // X'_j, both operands of the Gram
-    __shared__ __attribute__((aligned(16))) float sT[4 * 16 * SP];
-    __shared__ float sCo[2 * SMALL_MAX_STEPS];   // a_k, b_k: indexed by the step at run time
+    constexpr int XB = 4 * SLICE;   // a 128 x 128 block of X (32 KB)
+    constexpr int FG = 4;           // Gram fragments per wave side (64 x 64)
+    __shared__ __attribute__((aligned(1024))) bf16 sB[OPB];   // B
+    __shared__ __attribute__((aligned(1024))) bf16 sX0[XB];   // X blocks, even j
+    __shared__ __attribute__((aligned(1024))) bf16 sX1[XB];   // odd j
+    __shared__ __attribute__((aligned(1024))) bf16 sG[XB];    // X'_j, both operands of the Gram
 
     if ((int)blockIdx.x >= A.nprobs) return;
     const NsProb P = A.probs[blockIdx.x];   // by value: held in registers
-    const int np = P.np, NB = np / M;
+    const int np = P.np, NB = np / BW;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm0 = (wave >> 1) * WT, wn0 = (wave & 1) * WT;
     const int g4 = lane >> 4, l16 = lane & 15;
-    float* st = sT + wave * 16 * SP;
-    if (tid == 0) {
-#pragma unroll
-        for (int i = 0; i < SMALL_MAX_STEPS; ++i) {
-            sCo[i] = A.ca[i];
-            sCo[SMALL_MAX_STEPS + i] = A.cb[i];
-        }
-    }
+    const int gm0 = (wave >> 1) * 64, gn0 = (wave & 1) * 64;   // Gram: rows / columns of A'
+    const int ar0 = (wave >> 1) * 64, ac0 = (wave & 1) * 64;   // apply: rows / columns of X'_j
 
     // Block j of X (columns 128j .. 128j+127) is one contiguous 32 KB run of
     // X's K-blocked layout (mp = 128): k-panel p (columns 32p ..) is the 8 KB
@@ -1156,9 +1160,9 @@ __global__ __launch_bounds__(NTHR) void k_ns_small(SmallArgs A) {
     const uint32_t lane_xoff = (uint32_t)(256 * (lane >> 4) + 16 * ((lane & 15) ^ (4 * ((lane >> 4) & 1))));
     auto dma_block = [&](bf16* dst, const bf16* base, int j, bool permute) {
         const __amdgpu_buffer_rsrc_t rs =
-            __builtin_amdgcn_make_buffer_rsrc((void*)(base + (int64_t)j * OPB), 0, OPB * 2, BUF_RAW32);
+            __builtin_amdgcn_make_buffer_rsrc((void*)(base + (int64_t)j * XB), 0, XB * 2, BUF_RAW32);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < XB / 512 / 4; ++i) {
             const int b = i * 4 + wave;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDSP void*)(dst + b * 512), 16, permute ? lane_xoff : lane_off,
                                                      (uint32_t)b * 1024u, 0, 0);
@@ -1168,8 +1172,8 @@ __global__ __launch_bounds__(NTHR) void k_ns_small(SmallArgs A) {
     auto frag = [&](const bf16* buf, int sl, int row) -> bf16x8 {
         return *(const bf16x8*)(buf + sl * SLICE + row * BK + lane * 8);
     };
-    // fragment of a permuted X block as the right operand of B X: rows
-    // 32sl + 8(lane>>4) .. +7 (k) of column col0 + (lane&15); two transposed
+    // fragment of a permuted X block as the left operand of X^T B: column
+    // col0 + (lane&15) of X, rows 32sl + 8(lane>>4) .. +7 (k); two transposed
     // reads, lane addressing as in the tiled apply
     const int trs = (lane >> 1) & 1;
     const int tr_row = 8 * ((lane >> 4) & 1) + ((lane & 15) >> 2);
@@ -1182,47 +1186,66 @@ __global__ __launch_bounds__(NTHR) void k_ns_small(SmallArgs A) {
         const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDSP i16x4*)(blk + tr1));
         return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     };
-    f32x4 acc[F][F], accg[F][F];
-    // one MFMA on accumulator tile ij, written out so that the accumulators
-    // stay pinned in AGPRs
-    auto mma_ij = [](auto ij, f32x4 (&c)[F][F], const bf16x8 (&a)[F], const bf16x8 (&b)[F]) {
-        constexpr int i = decltype(ij)::value / F, j = decltype(ij)::value % F;
-        asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c[i][j]) : "v"(a[i]), "v"(b[j]));
+    // apply accumulators: acc[i][jj] = X'^T rows ac0 + 16i .. (columns of X'),
+    // columns ar0 + 16jj .. (rows of X')
+    f32x4 acc[4][4], accg[FG][FG];
+    bf16x8 bR[M / BK][4];   // this wave's rows ar0 .. ar0+63 of B, as the right operand of X^T B
+    // one MFMA, written out so that the accumulators stay pinned in AGPRs
+    auto mma = [](f32x4& c, const bf16x8& a, const bf16x8& b) {
+        asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
     };
-    // C (this wave's 64 x 64) += P Q^T over one 128-wide K block; P rows
-    // wm0.., Q rows wn0.., both K-blocked 128-row operands in LDS
-    auto block_mma = [&](f32x4 (&c)[F][F], const bf16* Pb, const bf16* Qb) {
+    // A' (this wave's 64 x 64) += X'_j X'_j^T over the block's 64 columns
+    auto gram_block = [&](const bf16* Gb) {
 #pragma unroll
-        for (int sl = 0; sl < 4; ++sl) {
-            bf16x8 a[F], b[F];
+        for (int sl = 0; sl < BW / BK; ++sl) {
+            bf16x8 a[FG], b[FG];
 #pragma unroll
-            for (int i = 0; i < F; ++i) {
-                a[i] = frag(Pb, sl, wm0 + i * 16);
-                b[i] = frag(Qb, sl, wn0 + i * 16);
+            for (int i = 0; i < FG; ++i) {
+                a[i] = frag(Gb, sl, gm0 + i * 16);
+                b[i] = frag(Gb, sl, gn0 + i * 16);
             }
-            static_for<0, F * F>([&](auto ij) { mma_ij(ij, c, a, b); });
+#pragma unroll
+            for (int i = 0; i < FG; ++i)
+#pragma unroll
+                for (int jn = 0; jn < FG; ++jn) mma(accg[i][jn], a[i], b[jn]);
         }
     };
-    // C (this wave's 64 x 64 of B X_j) += over the 128 rows of X_j: B from
-    // sB, X_j a permuted block
-    auto apply_mma = [&](f32x4 (&c)[F][F], const bf16* Xb) {
+    // B's rows ar0 .. ar0+63 into registers (B[k][r] = B[r][k]: a right-
+    // operand fragment of column r is row r of B)
+    auto load_b = [&]() {
 #pragma unroll
-        for (int sl = 0; sl < 4; ++sl) {
-            bf16x8 a[F], b[F];
+        for (int sl = 0; sl < M / BK; ++sl)
 #pragma unroll
-            for (int i = 0; i < F; ++i) {
-                a[i] = frag(sB, sl, wm0 + i * 16);
-                b[i] = frag_x(Xb, sl, wn0 + i * 16);
-            }
-            static_for<0, F * F>([&](auto ij) { mma_ij(ij, c, a, b); });
+            for (int jj = 0; jj < 4; ++jj) bR[sl][jj] = frag(sB, sl, ar0 + jj * 16);
+    };
+    // X'_j^T (this wave's 64 x 64) = X_j^T B over the 128 rows of X_j
+    auto apply_block = [&](const bf16* Xb) {
+#pragma unroll
+        for (int sl = 0; sl < M / BK; ++sl) {
+            bf16x8 a[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a[i] = frag_x(Xb, sl, ac0 + i * 16);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) mma(acc[i][jj], a[i], bR[sl][jj]);
         }
     };
-    auto zero = [&](f32x4 (&c)[F][F]) {
+    auto zero_acc = [&]() {
 #pragma unroll
-        for (int i = 0; i < F; ++i)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < F; ++j) c[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int jj = 0; jj < 4; ++jj) acc[i][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
         // two wait states before an MFMA reads the cleared accumulators
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_nop 1");
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto zero_gram = [&]() {
+#pragma unroll
+        for (int i = 0; i < FG; ++i)
+#pragma unroll
+            for (int jn = 0; jn < FG; ++jn) accg[i][jn] = f32x4{0.f, 0.f, 0.f, 0.f};
         __builtin_amdgcn_sched_barrier(0);
         asm volatile("s_nop 1");
         __builtin_amdgcn_sched_barrier(0);
@@ -1234,13 +1257,13 @@ __global__ __launch_bounds__(NTHR) void k_ns_small(SmallArgs A) {
         asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
     };
-    // transposed view of strip fm for the fragment pair (fp, fp+1): w[e] =
-    // C[r0 + e][col], col = wn0 + (fp + (g4&1))*16 + l16, r0 = wm0 + fm*16 + 8*(g4>>1)
-    auto swap_pair = [&](float (&av)[F][4], int fp, float* w) {
+    // the lane swap of two fragments adjacent in columns: lane gets
+    // w[e] = C[r0 + e][col], r0 = 8*(g4>>1) + the pair's first row, col =
+    // (fp + (g4&1))*16 + l16 of the pair's columns
+    auto swap_pair = [&](const float (&v0)[4], const float (&v1)[4], float* w) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(av[fp][e]),
-                                                             __float_as_uint(av[fp + 1][e]), false, false);
+            const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(v0[e]), __float_as_uint(v1[e]), false, false);
             w[e] = __uint_as_float(sw[0]);
             w[4 + e] = __uint_as_float(sw[1]);
         }
@@ -1250,21 +1273,44 @@ __global__ __launch_bounds__(NTHR) void k_ns_small(SmallArgs A) {
     auto build_b = [&](float gs, float gd) {
         mfma_drain();
 #pragma unroll
-        for (int fm = 0; fm < F; ++fm) {
-            float av[F][4];
+        for (int fm = 0; fm < FG; ++fm) {
+            float av[FG][4];
 #pragma unroll
-            for (int fn = 0; fn < F; ++fn)
+            for (int fn = 0; fn < FG; ++fn)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) av[fn][e] = agpr_read(accg[fm][fn][e]);
 #pragma unroll
-            for (int fp = 0; fp < F; fp += 2) {
+            for (int fp = 0; fp < FG; fp += 2) {
                 float w[8];
-                swap_pair(av, fp, w);
-                const int col = wn0 + (fp + (g4 & 1)) * 16 + l16, r0 = wm0 + fm * 16 + 8 * (g4 >> 1);
+                swap_pair(av[fp], av[fp + 1], w);
+                const int col = gn0 + (fp + (g4 & 1)) * 16 + l16, r0 = gm0 + fm * 16 + 8 * (g4 >> 1);
                 bf16x8 q;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) q[e] = (bf16)(gs * w[e] + (col == r0 + e ? gd : 0.f));
                 *(bf16x8*)(sB + kb_off(col, r0, M)) = q;
+            }
+        }
+    };
+    // X'_j from the apply accumulators into sG (K-blocked, 128 rows, 128
+    // columns): after the swap a lane holds columns c0 .. c0+7 of row r
+    auto store_xp = [&]() {
+        mfma_drain();
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float av[4][4];
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) av[jj][e] = agpr_read(acc[i][jj][e]);
+#pragma unroll
+            for (int jp = 0; jp < 4; jp += 2) {
+                float w[8];
+                swap_pair(av[jp], av[jp + 1], w);
+                const int r = ar0 + (jp + (g4 & 1)) * 16 + l16, c0 = ac0 + i * 16 + 8 * (g4 >> 1);
+                bf16x8 q;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) q[e] = (bf16)w[e];
+                *(bf16x8*)(sG + kb_off(r, c0, M)) = q;
             }
         }
     };
@@ -1273,12 +1319,12 @@ __global__ __launch_bounds__(NTHR) void k_ns_small(SmallArgs A) {
     const float f = P.fold[0];
 
     // A0 = X0 X0^T, one pass over X0
-    zero(accg);
+    zero_gram();
     dma_block(sX0, x0, 0, false);
     auto gram0 = [&](int j, bf16* cur, bf16* nxt) {
         __syncthreads();   // block j landed; everyone is done with `nxt`
         if (j + 1 < NB) dma_block(nxt, x0, j + 1, false);
-        block_mma(accg, cur, cur);
+        gram_block(cur);
     };
     for (int j = 0; j < NB; j += 2) {
         gram0(j, sX0, sX1);
@@ -1293,61 +1339,38 @@ __global__ __launch_bounds__(NTHR) void k_ns_small(SmallArgs A) {
         const bf16* xin = (const bf16*)((k & 1) ? P.x[1] : P.x[0]);
         bf16* xout = (bf16*)((k & 1) ? P.x[0] : P.x[1]);
         __syncthreads();   // B written by every wave
-        zero(accg);
+        load_b();
+        zero_gram();
         dma_block(sX0, xin, 0, true);
         auto step_block = [&](int j, bf16* cur, bf16* nxt) {
             __syncthreads();   // block j landed, the previous block's stores done; `nxt` and sG free
             if (j + 1 < NB) dma_block(nxt, xin, j + 1, true);
-            zero(acc);
-            apply_mma(acc, cur);
-            mfma_drain();
-#pragma unroll
-            for (int fm = 0; fm < F; ++fm) {
-                float av[F][4];
-#pragma unroll
-                for (int fn = 0; fn < F; ++fn)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) av[fn][e] = agpr_read(acc[fm][fn][e]);
-                wave_lds_sync();
-#pragma unroll
-                for (int fn = 0; fn < F; ++fn)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) st[(4 * g4 + e) * SP + fn * 16 + l16] = av[fn][e];
-                wave_lds_sync();
-#pragma unroll
-                for (int pass = 0; pass < PASSES; ++pass) {
-                    const int rr = l16, c8 = pass * 32 + g4 * 8;
-                    const f32x4 lo = *(const f32x4*)(st + rr * SP + c8);
-                    const f32x4 hi = *(const f32x4*)(st + rr * SP + c8 + 4);
-                    bf16x8 q;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        q[e] = (bf16)lo[e];
-                        q[4 + e] = (bf16)hi[e];
-                    }
-                    *(bf16x8*)(sG + kb_off(wm0 + fm * 16 + rr, wn0 + c8, M)) = q;
-                }
-            }
-            __syncthreads();   // X'_j complete in sG
+            zero_acc();
+            apply_block(cur);
+            store_xp();
+            // X'_j complete in sG: a barrier on the LDS writes only (a full
+            // __syncthreads would also wait for the loads of block j+1, just
+            // issued, which then could not overlap this block's work)
+            MU_WAIT_LGKM0();
+            __builtin_amdgcn_s_barrier();
             {
                 // sG is X'_j K-blocked with 128 rows, which is exactly the
-                // 32 KB run of X (mp = 128) holding columns 128j .. 128j+127;
-                // stored non-temporally (read back only by the next step):
-                // 2.5 % faster on the per-head set
-                bf16* xd = xout + (int64_t)j * OPB;
+                // 16 KB run of X (mp = 128) holding columns 64j .. 64j+63;
+                // stored non-temporally (read back only by the next step)
+                bf16* xd = xout + (int64_t)j * XB;
 #pragma unroll
-                for (int i = 0; i < OPB / (NTHR * 8); ++i) {
+                for (int i = 0; i < XB / (NTHR * 8); ++i) {
                     const int o = (i * NTHR + tid) * 8;
                     __builtin_nontemporal_store(*(const bf16x8*)(sG + o), gp((bf16x8*)(xd + o)));
                 }
             }
-            block_mma(accg, sG, sG);
+            gram_block(sG);
         };
         for (int j = 0; j < NB; j += 2) {
             step_block(j, sX0, sX1);
             if (j + 1 < NB) step_block(j + 1, sX1, sX0);
         }
-        build_b(sCo[SMALL_MAX_STEPS + k + 1], sCo[k + 1]);
+        build_b(A.cb[k + 1], A.ca[k + 1]);
     }
     // the last step's B -> the problem's `a` buffer (same K-blocked layout)
     __syncthreads();
