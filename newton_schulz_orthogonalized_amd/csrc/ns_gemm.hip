@@ -767,234 +767,234 @@ __global__ __launch_bounds__(NTHR) void k_gemm_bf16(GemmArgs A) {
         if (wg < 0) return;
     }
     for (;;) {
-    // the tile, resolved ahead by k_tilemap: one load where a search over the
-    // problems' tile prefix took a chain of dependent ones
-    const TileEntry te = A.tmap[wg];
-    const int p = __builtin_amdgcn_readfirstlane(te.p);
-    const int tij = __builtin_amdgcn_readfirstlane(te.tij);
-    const NsProb P = A.probs[p];   // by value: held in registers, never re-read after a store
-    const int mode = A.mode;
-    const int ti = tij & 0xffff, tj = tij >> 16;
+        // the tile, resolved ahead by k_tilemap: one load where a search over the
+        // problems' tile prefix took a chain of dependent ones
+        const TileEntry te = A.tmap[wg];
+        const int p = __builtin_amdgcn_readfirstlane(te.p);
+        const int tij = __builtin_amdgcn_readfirstlane(te.tij);
+        const NsProb P = A.probs[p];   // by value: held in registers, never re-read after a store
+        const int mode = A.mode;
+        const int ti = tij & 0xffff, tj = tij >> 16;
 
-    // Gram modes: C = P Q^T over K, P and Q K-blocked with RP and RQ rows.
-    // Apply: C = B X, B K-blocked (mp rows, k = mp) and X itself (mp rows,
-    // k = np) as the right operand, whose k runs down X's rows (see dma_slice
-    // and read_b).
-    const bf16 *pm, *qm;
-    int RP, RQ, K;
-    if (mode == GM_GRAM) {
-        pm = qm = (const bf16*)(A.src ? P.x[1] : P.x[0]); RP = RQ = P.mp; K = P.np;
-    } else if (mode == GM_GRAM2) {
-        pm = qm = (const bf16*)P.a; RP = RQ = P.mp; K = P.mp;
-    } else {
-        pm = (const bf16*)(A.use_b ? P.b : P.a); RP = P.mp;
-        qm = (const bf16*)(A.src ? P.x[1] : P.x[0]); RQ = P.mp; K = P.mp;
-    }
-
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm0 = (wave >> 1) * WT, wn0 = (wave & 1) * WT;
-
-    auto slot_a = [&](auto st) -> bf16* {
-        constexpr int S = decltype(st)::value;
-        if constexpr (S == 0) return sA0;
-        else if constexpr (S == 1) return sA1;
-        else if constexpr (S == 2) return sA2;
-        else return sA3;
-    };
-    auto slot_b = [&](auto st) -> bf16* {
-        constexpr int S = decltype(st)::value;
-        if constexpr (S == 0) return sB0;
-        else if constexpr (S == 1) return sB1;
-        else if constexpr (S == 2) return sB2;
-        else return sB3;
-    };
-
-    // Direct loads. The TS x 32 slice kt of a K-blocked operand tile is NBLK
-    // contiguous 1 KB blocks starting at block kt*R/16 + tile*TS/16; a buffer
-    // resource covering exactly that run (an offset outside it reads zeros
-    // instead of faulting) is built per step from the wave-uniform address.
-    // Block b of the slice goes to block b of the slot, lane l moving bytes
-    // 16l..16l+15: a plain 1 KB copy, eight whole 128-byte lines per
-    // instruction.
-    // The apply's right operand is X: slice kt is rows 32kt .. 32kt+31 of the
-    // tile's TS columns, i.e. row groups 2kt and 2kt+1 of TS/32 k-panels, two
-    // adjacent blocks per panel with panels mp/16 blocks apart. Slot block
-    // 2*panel + group holds it, its 16-byte chunks permuted: chunk (c, r) of
-    // the X block (k chunk c, row r) sits at slot chunk (c, r ^ 4*(c&1)),
-    // which keeps the transposed fragment reads below free of bank conflicts.
-    const uint32_t lane_off = (uint32_t)lane * 16u;
-    const uint32_t lane_xoff = (uint32_t)(256 * (lane >> 4) + 16 * ((lane & 15) ^ (4 * ((lane >> 4) & 1))));
-    const uint32_t x_pan = (uint32_t)(RQ >> 4) * 1024u;   // bytes between k-panels of X
-    auto slice = [&](const bf16* base, int R, int tile, int kt) {
-        return __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(base + ((int64_t)kt * (R >> 4) + (int64_t)tile * (TS >> 4)) * 512), 0, NBLK * 1024, BUF_RAW32);
-    };
-    auto slice_x = [&](int kt) {
-        return __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(qm + ((int64_t)tj * (TS / 32) * (RQ >> 4) + 2 * kt) * 512), 0, (TS / 32 - 1) * x_pan + 2048u,
-            BUF_RAW32);
-    };
-    auto dma_slice = [&](auto st, int kt, auto first, auto count) {
-        constexpr int I0 = decltype(first)::value, NI = decltype(count)::value;
-        const __amdgpu_buffer_rsrc_t ra = slice(pm, RP, ti, kt);
-        __amdgpu_buffer_rsrc_t rb;
-        if constexpr (SYM) rb = slice(qm, RQ, tj, kt);
-        else rb = slice_x(kt);
-        static_for<I0, I0 + NI>([&](auto ic) {
-            constexpr int i = decltype(ic)::value;
-            constexpr bool isA = i < BPW;
-            const int b = (isA ? i : i - BPW) * 4 + wave;
-            bf16* dst = (isA ? slot_a(st) : slot_b(st)) + b * 512;
-            if (isA || SYM)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(isA ? ra : rb, (LDSP void*)dst, 16, lane_off,
-                                                         (uint32_t)b * 1024u, 0, 0);
-            else
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (LDSP void*)dst, 16, lane_xoff,
-                                                         (uint32_t)(b >> 1) * x_pan + (uint32_t)(b & 1) * 1024u, 0, 0);
-        });
-    };
-    auto dma = [&](auto st, int kt) { dma_slice(st, kt, Stage<0>{}, Stage<NDMA>{}); };
-    auto read_a = [&](auto st, int fm) -> bf16x8 {
-        return *(const bf16x8*)(slot_a(st) + (wm0 + fm * 16) * BK + lane * 8);
-    };
-    // Apply fragment fn (X columns wn0 + 16fn ..): lane l needs rows
-    // 8(l>>4) .. +7 of column l&15. ds_read_b64_tr_b16 hands lane i of each
-    // 16-lane group element i%4 of the 4-element run addressed by lane
-    // 4j + i/4 as its element j; lane i addresses row r0 + i/4, columns
-    // 4(i%4) .. +3 (r0 = 8(l>>4), then r0 + 4), so it receives column i of
-    // those four rows. Slot block 2*(wn0/32 + fn/2) + (l>>5), k chunk
-    // 2(fn&1) + ((i>>1)&1).
-    const int trs = (lane >> 1) & 1;
-    const int tr_row = 8 * ((lane >> 4) & 1) + ((lane & 15) >> 2);
-    const uint32_t tr_lane = (uint32_t)(1024 * (lane >> 5) + 256 * trs + 8 * (lane & 1));
-    const uint32_t tr0 = tr_lane + 16u * (uint32_t)(tr_row + 4 * trs);
-    const uint32_t tr1 = tr_lane + 16u * (uint32_t)(tr_row + 4 * (trs ^ 1));
-    auto read_b = [&](auto st, int fn) -> bf16x8 {
-        if constexpr (SYM) {
-            return *(const bf16x8*)(slot_b(st) + (wn0 + fn * 16) * BK + lane * 8);
+        // Gram modes: C = P Q^T over K, P and Q K-blocked with RP and RQ rows.
+        // Apply: C = B X, B K-blocked (mp rows, k = mp) and X itself (mp rows,
+        // k = np) as the right operand, whose k runs down X's rows (see dma_slice
+        // and read_b).
+        const bf16 *pm, *qm;
+        int RP, RQ, K;
+        if (mode == GM_GRAM) {
+            pm = qm = (const bf16*)(A.src ? P.x[1] : P.x[0]); RP = RQ = P.mp; K = P.np;
+        } else if (mode == GM_GRAM2) {
+            pm = qm = (const bf16*)P.a; RP = RQ = P.mp; K = P.mp;
         } else {
-            const char* blk = (const char*)slot_b(st) + (wn0 / 32 + fn / 2) * 2048 + (fn & 1) * 512;
-            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDSP i16x4*)(blk + tr0));
-            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDSP i16x4*)(blk + tr1));
-            return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            pm = (const bf16*)(A.use_b ? P.b : P.a); RP = P.mp;
+            qm = (const bf16*)(A.src ? P.x[1] : P.x[0]); RQ = P.mp; K = P.mp;
         }
-    };
 
-    f32x4 acc[F][F];
-#pragma unroll
-    for (int i = 0; i < F; ++i)
-#pragma unroll
-        for (int j = 0; j < F; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int tid = threadIdx.x, lane = tid & 63;
+        const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+        const int wm0 = (wave >> 1) * WT, wn0 = (wave & 1) * WT;
 
-    bf16x8 a0[F], b0[F], a1[F], b1[F];
-    const int KT = K / BK;   // a multiple of NS: K is a multiple of 128
-
-    dma(Stage<0>{}, 0);
-    dma(Stage<1>{}, 1);
-    dma(Stage<2>{}, 2);
-    dma(Stage<3>{}, 3);
-    MU_WAIT_VMCNT((NS - 1) * NDMA);
-    __builtin_amdgcn_s_barrier();
-#pragma unroll
-    for (int fn = 0; fn < F; ++fn) b0[fn] = read_b(Stage<0>{}, fn);
-#pragma unroll
-    for (int fm = 0; fm < F; ++fm) a0[fm] = read_a(Stage<0>{}, fm);
-
-    // The body is emitted in the exact issue order wanted and fenced with
-    // sched_barrier, so the MFMA stream is never starved: with one wave per
-    // SIMD the matrix core drains within a couple of MFMAs of any gap. Next
-    // fragments are read B first: phase A of the next step needs all of B and
-    // the first HEAD rows of A. Slice indices past the end are clamped, so the
-    // last loads refill slots nobody reads again instead of branching.
-    constexpr int HEAD = F / 4 > 0 ? F / 4 : 1;
-    constexpr int G = 2 * F;                 // fragment reads per step
-    constexpr int NMB = (F - HEAD) * F;      // MFMAs after the barrier
-    // one MFMA on accumulator tile idx (row-major over the F x F fragments);
-    // the instruction is written out so that the accumulators stay pinned in
-    // AGPRs across the loop (the builtin lets the allocator shuffle them)
-    auto mma_acc = [](auto idx, f32x4 (&c)[F][F], const bf16x8 (&af)[F], const bf16x8 (&bfv)[F]) {
-        constexpr int fm = decltype(idx)::value / F, fn = decltype(idx)::value % F;
-        asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c[fm][fn]) : "v"(af[fm]), "v"(bfv[fn]));
-    };
-    auto mma = [&](auto idx, const bf16x8 (&af)[F], const bf16x8 (&bfv)[F]) { mma_acc(idx, acc, af, bfv); };
-    auto step = [&](auto domma, auto st, int kt, const bf16x8 (&ac)[F], const bf16x8 (&bc)[F], bf16x8 (&an)[F],
-                    bf16x8 (&bn)[F]) {
-        constexpr int DM = decltype(domma)::value;
-        constexpr bool DO = DM != 0;
-        // one MFMA, or none for a fragment below the diagonal (DM == 2)
-        auto mmaw = [&](auto j) {
-            constexpr int idx = decltype(j)::value;
-            if constexpr (DM != 2 || idx / F <= idx % F) mma(j, ac, bc);
+        auto slot_a = [&](auto st) -> bf16* {
+            constexpr int S = decltype(st)::value;
+            if constexpr (S == 0) return sA0;
+            else if constexpr (S == 1) return sA1;
+            else if constexpr (S == 2) return sA2;
+            else return sA3;
         };
-        constexpr int S = decltype(st)::value;
-        using SN = Stage<(S + 1) % NS>;
-        if constexpr (S == 0) {
-            // loop head: two wait states after the accumulator zeroing
-            // (a VALU write read as SrcC), which the compiler cannot see here
-            asm volatile("s_nop 1");
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        if constexpr (DO) static_for<0, HEAD * F>([&](auto j) { mmaw(j); });
-        __builtin_amdgcn_sched_barrier(0);
-        MU_WAIT_VMCNT_LGKM0((NS - 2) * NDMA);
-        __builtin_amdgcn_s_barrier();
-        const int kn = min(kt + NS, KT - 1);
-        static_for<0, G>([&](auto gc) {
-            constexpr int g = decltype(gc)::value;
-            // the loads of this group: i with i*G/NDMA == g
-            constexpr int i0 = (g * NDMA + G - 1) / G, i1 = ((g + 1) * NDMA + G - 1) / G;
-            if constexpr (i1 > i0) dma_slice(st, kn, Stage<i0>{}, Stage<i1 - i0>{});
-            if constexpr (DO) {
-                if constexpr (g < F) bn[g] = read_b(SN{}, g);
-                else an[g - F] = read_a(SN{}, g - F);
-                static_for<HEAD * F + g * NMB / G, HEAD * F + (g + 1) * NMB / G>([&](auto j) { mmaw(j); });
+        auto slot_b = [&](auto st) -> bf16* {
+            constexpr int S = decltype(st)::value;
+            if constexpr (S == 0) return sB0;
+            else if constexpr (S == 1) return sB1;
+            else if constexpr (S == 2) return sB2;
+            else return sB3;
+        };
+
+        // Direct loads. The TS x 32 slice kt of a K-blocked operand tile is NBLK
+        // contiguous 1 KB blocks starting at block kt*R/16 + tile*TS/16; a buffer
+        // resource covering exactly that run (an offset outside it reads zeros
+        // instead of faulting) is built per step from the wave-uniform address.
+        // Block b of the slice goes to block b of the slot, lane l moving bytes
+        // 16l..16l+15: a plain 1 KB copy, eight whole 128-byte lines per
+        // instruction.
+        // The apply's right operand is X: slice kt is rows 32kt .. 32kt+31 of the
+        // tile's TS columns, i.e. row groups 2kt and 2kt+1 of TS/32 k-panels, two
+        // adjacent blocks per panel with panels mp/16 blocks apart. Slot block
+        // 2*panel + group holds it, its 16-byte chunks permuted: chunk (c, r) of
+        // the X block (k chunk c, row r) sits at slot chunk (c, r ^ 4*(c&1)),
+        // which keeps the transposed fragment reads below free of bank conflicts.
+        const uint32_t lane_off = (uint32_t)lane * 16u;
+        const uint32_t lane_xoff = (uint32_t)(256 * (lane >> 4) + 16 * ((lane & 15) ^ (4 * ((lane >> 4) & 1))));
+        const uint32_t x_pan = (uint32_t)(RQ >> 4) * 1024u;   // bytes between k-panels of X
+        auto slice = [&](const bf16* base, int R, int tile, int kt) {
+            return __builtin_amdgcn_make_buffer_rsrc(
+                (void*)(base + ((int64_t)kt * (R >> 4) + (int64_t)tile * (TS >> 4)) * 512), 0, NBLK * 1024, BUF_RAW32);
+        };
+        auto slice_x = [&](int kt) {
+            return __builtin_amdgcn_make_buffer_rsrc(
+                (void*)(qm + ((int64_t)tj * (TS / 32) * (RQ >> 4) + 2 * kt) * 512), 0, (TS / 32 - 1) * x_pan + 2048u,
+                BUF_RAW32);
+        };
+        auto dma_slice = [&](auto st, int kt, auto first, auto count) {
+            constexpr int I0 = decltype(first)::value, NI = decltype(count)::value;
+            const __amdgpu_buffer_rsrc_t ra = slice(pm, RP, ti, kt);
+            __amdgpu_buffer_rsrc_t rb;
+            if constexpr (SYM) rb = slice(qm, RQ, tj, kt);
+            else rb = slice_x(kt);
+            static_for<I0, I0 + NI>([&](auto ic) {
+                constexpr int i = decltype(ic)::value;
+                constexpr bool isA = i < BPW;
+                const int b = (isA ? i : i - BPW) * 4 + wave;
+                bf16* dst = (isA ? slot_a(st) : slot_b(st)) + b * 512;
+                if (isA || SYM)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(isA ? ra : rb, (LDSP void*)dst, 16, lane_off,
+                                                             (uint32_t)b * 1024u, 0, 0);
+                else
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        rb, (LDSP void*)dst, 16, lane_xoff, (uint32_t)(b >> 1) * x_pan + (uint32_t)(b & 1) * 1024u, 0, 0);
+            });
+        };
+        auto dma = [&](auto st, int kt) { dma_slice(st, kt, Stage<0>{}, Stage<NDMA>{}); };
+        auto read_a = [&](auto st, int fm) -> bf16x8 {
+            return *(const bf16x8*)(slot_a(st) + (wm0 + fm * 16) * BK + lane * 8);
+        };
+        // Apply fragment fn (X columns wn0 + 16fn ..): lane l needs rows
+        // 8(l>>4) .. +7 of column l&15. ds_read_b64_tr_b16 hands lane i of each
+        // 16-lane group element i%4 of the 4-element run addressed by lane
+        // 4j + i/4 as its element j; lane i addresses row r0 + i/4, columns
+        // 4(i%4) .. +3 (r0 = 8(l>>4), then r0 + 4), so it receives column i of
+        // those four rows. Slot block 2*(wn0/32 + fn/2) + (l>>5), k chunk
+        // 2(fn&1) + ((i>>1)&1).
+        const int trs = (lane >> 1) & 1;
+        const int tr_row = 8 * ((lane >> 4) & 1) + ((lane & 15) >> 2);
+        const uint32_t tr_lane = (uint32_t)(1024 * (lane >> 5) + 256 * trs + 8 * (lane & 1));
+        const uint32_t tr0 = tr_lane + 16u * (uint32_t)(tr_row + 4 * trs);
+        const uint32_t tr1 = tr_lane + 16u * (uint32_t)(tr_row + 4 * (trs ^ 1));
+        auto read_b = [&](auto st, int fn) -> bf16x8 {
+            if constexpr (SYM) {
+                return *(const bf16x8*)(slot_b(st) + (wn0 + fn * 16) * BK + lane * 8);
+            } else {
+                const char* blk = (const char*)slot_b(st) + (wn0 / 32 + fn / 2) * 2048 + (fn & 1) * 512;
+                const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDSP i16x4*)(blk + tr0));
+                const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDSP i16x4*)(blk + tr1));
+                return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
             }
+        };
+
+        f32x4 acc[F][F];
+#pragma unroll
+        for (int i = 0; i < F; ++i)
+#pragma unroll
+            for (int j = 0; j < F; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+        bf16x8 a0[F], b0[F], a1[F], b1[F];
+        const int KT = K / BK;   // a multiple of NS: K is a multiple of 128
+
+        dma(Stage<0>{}, 0);
+        dma(Stage<1>{}, 1);
+        dma(Stage<2>{}, 2);
+        dma(Stage<3>{}, 3);
+        MU_WAIT_VMCNT((NS - 1) * NDMA);
+        __builtin_amdgcn_s_barrier();
+#pragma unroll
+        for (int fn = 0; fn < F; ++fn) b0[fn] = read_b(Stage<0>{}, fn);
+#pragma unroll
+        for (int fm = 0; fm < F; ++fm) a0[fm] = read_a(Stage<0>{}, fm);
+
+        // The body is emitted in the exact issue order wanted and fenced with
+        // sched_barrier, so the MFMA stream is never starved: with one wave per
+        // SIMD the matrix core drains within a couple of MFMAs of any gap. Next
+        // fragments are read B first: phase A of the next step needs all of B and
+        // the first HEAD rows of A. Slice indices past the end are clamped, so the
+        // last loads refill slots nobody reads again instead of branching.
+        constexpr int HEAD = F / 4 > 0 ? F / 4 : 1;
+        constexpr int G = 2 * F;                 // fragment reads per step
+        constexpr int NMB = (F - HEAD) * F;      // MFMAs after the barrier
+        // one MFMA on accumulator tile idx (row-major over the F x F fragments);
+        // the instruction is written out so that the accumulators stay pinned in
+        // AGPRs across the loop (the builtin lets the allocator shuffle them)
+        auto mma_acc = [](auto idx, f32x4 (&c)[F][F], const bf16x8 (&af)[F], const bf16x8 (&bfv)[F]) {
+            constexpr int fm = decltype(idx)::value / F, fn = decltype(idx)::value % F;
+            asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c[fm][fn]) : "v"(af[fm]), "v"(bfv[fn]));
+        };
+        auto mma = [&](auto idx, const bf16x8 (&af)[F], const bf16x8 (&bfv)[F]) { mma_acc(idx, acc, af, bfv); };
+        auto step = [&](auto domma, auto st, int kt, const bf16x8 (&ac)[F], const bf16x8 (&bc)[F], bf16x8 (&an)[F],
+                        bf16x8 (&bn)[F]) {
+            constexpr int DM = decltype(domma)::value;
+            constexpr bool DO = DM != 0;
+            // one MFMA, or none for a fragment below the diagonal (DM == 2)
+            auto mmaw = [&](auto j) {
+                constexpr int idx = decltype(j)::value;
+                if constexpr (DM != 2 || idx / F <= idx % F) mma(j, ac, bc);
+            };
+            constexpr int S = decltype(st)::value;
+            using SN = Stage<(S + 1) % NS>;
+            if constexpr (S == 0) {
+                // loop head: two wait states after the accumulator zeroing
+                // (a VALU write read as SrcC), which the compiler cannot see here
+                asm volatile("s_nop 1");
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if constexpr (DO) static_for<0, HEAD * F>([&](auto j) { mmaw(j); });
             __builtin_amdgcn_sched_barrier(0);
-        });
-    };
-    auto kloop = [&](auto domma) {
-        for (int kt = 0; kt < KT; kt += NS) {
-            step(domma, Stage<0>{}, kt, a0, b0, a1, b1);
-            step(domma, Stage<1>{}, kt + 1, a1, b1, a0, b0);
-            step(domma, Stage<2>{}, kt + 2, a0, b0, a1, b1);
-            step(domma, Stage<3>{}, kt + 3, a1, b1, a0, b0);
+            MU_WAIT_VMCNT_LGKM0((NS - 2) * NDMA);
+            __builtin_amdgcn_s_barrier();
+            const int kn = min(kt + NS, KT - 1);
+            static_for<0, G>([&](auto gc) {
+                constexpr int g = decltype(gc)::value;
+                // the loads of this group: i with i*G/NDMA == g
+                constexpr int i0 = (g * NDMA + G - 1) / G, i1 = ((g + 1) * NDMA + G - 1) / G;
+                if constexpr (i1 > i0) dma_slice(st, kn, Stage<i0>{}, Stage<i1 - i0>{});
+                if constexpr (DO) {
+                    if constexpr (g < F) bn[g] = read_b(SN{}, g);
+                    else an[g - F] = read_a(SN{}, g - F);
+                    static_for<HEAD * F + g * NMB / G, HEAD * F + (g + 1) * NMB / G>([&](auto j) { mmaw(j); });
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            });
+        };
+        auto kloop = [&](auto domma) {
+            for (int kt = 0; kt < KT; kt += NS) {
+                step(domma, Stage<0>{}, kt, a0, b0, a1, b1);
+                step(domma, Stage<1>{}, kt + 1, a1, b1, a0, b0);
+                step(domma, Stage<2>{}, kt + 2, a0, b0, a1, b1);
+                step(domma, Stage<3>{}, kt + 3, a1, b1, a0, b0);
+            }
+        };
+        // On a diagonal Gram tile the wave below the diagonal would compute the
+        // transpose of the wave above it: it only keeps the loads and barriers
+        // going, and the epilogue of the wave above writes both quadrants. The
+        // two waves on the diagonal compute only their fragments on or above it
+        // and mirror those. Under the power limit the saved MFMA work (3 % of the
+        // 8B-shaped Gram for the skipped quadrant) gave 0.7 %.
+        if constexpr (SYM) {
+            if (ti == tj && wm0 > wn0) kloop(Stage<0>{});
+            else if (ti == tj && wm0 == wn0) kloop(Stage<2>{});
+            else kloop(Stage<1>{});
+        } else {
+            kloop(Stage<1>{});
         }
-    };
-    // On a diagonal Gram tile the wave below the diagonal would compute the
-    // transpose of the wave above it: it only keeps the loads and barriers
-    // going, and the epilogue of the wave above writes both quadrants. The
-    // two waves on the diagonal compute only their fragments on or above it
-    // and mirror those. Under the power limit the saved MFMA work (3 % of the
-    // 8B-shaped Gram for the skipped quadrant) gave 0.7 %.
-    if constexpr (SYM) {
-        if (ti == tj && wm0 > wn0) kloop(Stage<0>{});
-        else if (ti == tj && wm0 == wn0) kloop(Stage<2>{});
-        else kloop(Stage<1>{});
-    } else {
-        kloop(Stage<1>{});
-    }
-    // The MFMAs above are opaque to the compiler's hazard recognizer: give the
-    // last ones the wait states (>= passes + 2) that an accumulator read needs.
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-    MU_WAIT_VMCNT(0);
-    __syncthreads();
-    // epilogue staging: two slot arrays per wave
-    static_assert(LS * sizeof(bf16) == (WT / 2) * 64 * sizeof(float), "a staging half is WT/2 x 64 floats");
-    float* st = (float*)(wave == 0 ? sA0 : wave == 1 ? sA1 : wave == 2 ? sA2 : sA3);
-    float* st2 = (float*)(wave == 0 ? sB0 : wave == 1 ? sB1 : wave == 2 ? sB2 : sB3);
-    // the next tile's ticket, taken here so that the epilogue hides its latency
-    // (and after the K loop, whose waits count only the direct loads)
-    if (persist && threadIdx.x == 0) ticket = atomicAdd(A.queues + q, 1);
-    epilogue_k<SYM, LAST, bf16, TSRC, F>(A, P, ti, tj, TS, wm0, wn0, acc, st, st2);
-    if (!persist) return;
-    __syncthreads();   // every wave is done with the LDS: its staging is the next tile's ring
-    if (threadIdx.x == 0) s_tile = next_tile(A, q, ticket, gstat, win);
-    __syncthreads();
-    wg = __builtin_amdgcn_readfirstlane(s_tile);
-    if (wg < 0) return;
+        // The MFMAs above are opaque to the compiler's hazard recognizer: give the
+        // last ones the wait states (>= passes + 2) that an accumulator read needs.
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        MU_WAIT_VMCNT(0);
+        __syncthreads();
+        // epilogue staging: two slot arrays per wave
+        static_assert(LS * sizeof(bf16) == (WT / 2) * 64 * sizeof(float), "a staging half is WT/2 x 64 floats");
+        float* st = (float*)(wave == 0 ? sA0 : wave == 1 ? sA1 : wave == 2 ? sA2 : sA3);
+        float* st2 = (float*)(wave == 0 ? sB0 : wave == 1 ? sB1 : wave == 2 ? sB2 : sB3);
+        // the next tile's ticket, taken here so that the epilogue hides its latency
+        // (and after the K loop, whose waits count only the direct loads)
+        if (persist && threadIdx.x == 0) ticket = atomicAdd(A.queues + q, 1);
+        epilogue_k<SYM, LAST, bf16, TSRC, F>(A, P, ti, tj, TS, wm0, wn0, acc, st, st2);
+        if (!persist) return;
+        __syncthreads();   // every wave is done with the LDS: its staging is the next tile's ring
+        if (threadIdx.x == 0) s_tile = next_tile(A, q, ticket, gstat, win);
+        __syncthreads();
+        wg = __builtin_amdgcn_readfirstlane(s_tile);
+        if (wg < 0) return;
     }
 }
 
@@ -1164,8 +1164,8 @@ __global__ __launch_bounds__(NTHR) void k_ns_small(SmallArgs A) {
 #pragma unroll
         for (int i = 0; i < XB / 512 / 4; ++i) {
             const int b = i * 4 + wave;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDSP void*)(dst + b * 512), 16, permute ? lane_xoff : lane_off,
-                                                     (uint32_t)b * 1024u, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDSP void*)(dst + b * 512), 16,
+                                                     permute ? lane_xoff : lane_off, (uint32_t)b * 1024u, 0, 0);
         }
     };
     // fragment of a K-blocked 128-row operand: rows row .. row+15, k-panel sl
@@ -1263,7 +1263,8 @@ __global__ __launch_bounds__(NTHR) void k_ns_small(SmallArgs A) {
     auto swap_pair = [&](const float (&v0)[4], const float (&v1)[4], float* w) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(v0[e]), __float_as_uint(v1[e]), false, false);
+            const auto sw =
+                __builtin_amdgcn_permlane16_swap(__float_as_uint(v0[e]), __float_as_uint(v1[e]), false, false);
             w[e] = __uint_as_float(sw[0]);
             w[4 + e] = __uint_as_float(sw[1]);
         }
