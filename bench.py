@@ -70,8 +70,9 @@ KERNEL_FILES = {"apply": ("ns_gemm.hip", "common.hpp", "launch.hpp"),
 
 
 def source_digest(files=KERNEL_SOURCES) -> str:
-    """Digest of kernel sources with comments and whitespace removed, so
-    that recorded counter figures stay attached to the code they measured."""
+    """Digest of kernel sources with comments and all whitespace removed, so
+    that recorded counter figures stay attached to the code they measured
+    (and survive reformatting)."""
     import re
     h = hashlib.sha256()
     for f in files:
@@ -79,7 +80,7 @@ def source_digest(files=KERNEL_SOURCES) -> str:
             src = fh.read()
         src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
         src = re.sub(r"//[^\n]*", " ", src)
-        h.update(" ".join(src.split()).encode())
+        h.update("".join(src.split()).encode())
     return h.hexdigest()[:16]
 
 
