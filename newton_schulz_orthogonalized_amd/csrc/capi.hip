@@ -704,14 +704,18 @@ int launch_sequence(const Plan& pl, char* ws, const mu_muon_hparams* hp, int src
     const char* pe = std::getenv("MU_PERSIST");   // MU_PERSIST=0: one workgroup per tile everywhere
     const bool persist_on = !(pe && pe[0] == '0');
     int gemm_index = 0;
-    auto place = [&](GemmArgs& a, int tile) {
+    // grid and tile counters of one GEMM launch; false if the plan counted
+    // fewer launches than the sequence issues (the counters would overrun)
+    auto place = [&](GemmArgs& a, int tile) -> bool {
         const int gstat = (a.total_tiles + 7) / 8 * 8;
         a.grid = gstat;
         a.queues = nullptr;
-        if (ns_dt != DT_BF16) return;
+        if (ns_dt != DT_BF16) return true;
+        if (gemm_index >= pl.n_gemm) return false;
         const int slots = tile == 256 ? cus : 2 * cus;   // workgroups per CU: 1 (256 tiles), 2 (128)
         a.queues = (int*)(ws + pl.off_queues) + 8 * gemm_index++;
         if (persist_on && a.mode != GM_APPLY_LAST && a.total_tiles >= PERSIST_MIN * slots) a.grid = slots;
+        return true;
     };
     // fused problems: every step but the last apply in one launch
     for (const Group& g : pl.groups) {
@@ -768,7 +772,7 @@ int launch_sequence(const Plan& pl, char* ws, const mu_muon_hparams* hp, int src
                 ap.mode = GM_APPLY_LAST;
                 ap.tmap = (const TileEntry*)(ws + g.apply_tmap);
                 ap.total_tiles = g.apply_prefix.back();
-                place(ap, g.tile);
+                if (!place(ap, g.tile)) return fail(MU_ERR_INVALID_ARG, "internal: GEMM launch count");
                 rc = timed_launch(MU_K_APPLY, aflops, abytes, s, [&] { return launch(ap); }, "apply launch");
                 if (rc) return rc;
                 continue;
@@ -779,7 +783,7 @@ int launch_sequence(const Plan& pl, char* ws, const mu_muon_hparams* hp, int src
             gg.total_tiles = g.gram_prefix.back();
             gg.first = first ? 1 : 0;
             gg.xcd_window = g.gram_window;
-            place(gg, g.tile);
+            if (!place(gg, g.tile)) return fail(MU_ERR_INVALID_ARG, "internal: GEMM launch count");
             rc = timed_launch(MU_K_GRAM, gflops, 0.0, s, [&] { return launch(gg); }, "gram launch");
             if (rc) return rc;
             if (quint) {
@@ -789,7 +793,7 @@ int launch_sequence(const Plan& pl, char* ws, const mu_muon_hparams* hp, int src
                 g2.total_tiles = g.gram_prefix.back();
                 g2.first = first ? 1 : 0;
                 g2.xcd_window = g.gram_window;
-                place(g2, g.tile);
+                if (!place(g2, g.tile)) return fail(MU_ERR_INVALID_ARG, "internal: GEMM launch count");
                 rc = timed_launch(MU_K_GRAM2, g2flops, 0.0, s, [&] { return launch(g2); }, "gram2 launch");
                 if (rc) return rc;
             }
@@ -798,7 +802,7 @@ int launch_sequence(const Plan& pl, char* ws, const mu_muon_hparams* hp, int src
             ap.tmap = (const TileEntry*)(ws + g.apply_tmap);
             ap.total_tiles = g.apply_prefix.back();
             ap.first = first ? 1 : 0;
-            place(ap, g.tile);
+            if (!place(ap, g.tile)) return fail(MU_ERR_INVALID_ARG, "internal: GEMM launch count");
             rc = timed_launch(MU_K_APPLY, aflops, abytes, s, [&] { return launch(ap); }, "apply launch");
             if (rc) return rc;
         }
