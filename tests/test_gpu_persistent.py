@@ -63,3 +63,42 @@ def test_persistent_launches_match_one_workgroup_per_tile(coeffs, monkeypatch):
     for i in range(len(shapes)):
         assert torch.equal(o_pers[i], o_tile[i]), i
         assert torch.equal(w_pers[i], w_tile[i]), i
+
+
+def test_persistent_128_tiles_match_one_workgroup_per_tile(monkeypatch):
+    """The 128 x 128 tile kernel (two workgroups per compute unit) in a
+    persistent apply: 256 blocks of 200 x 4096 (short side padded to 256,
+    tile 128, not the fused path) give 256 x 64 = 16384 apply tiles, above
+    8 x 512 slots; the Gram (768 tiles) stays one workgroup per tile. Tall
+    and wide blocks alike."""
+    import newton_schulz_orthogonalized_amd as nso
+    from newton_schulz_orthogonalized_amd import _lib as L
+    props = torch.cuda.get_device_properties(0)
+    shapes = [(200, 4096) if i % 2 else (4096, 200) for i in range(256)]
+    if 256 * 64 < 8 * 2 * props.multi_processor_count:
+        pytest.skip("fewer apply tiles than the persistent threshold on this device")
+    print("[persistent] 256 x (200, 4096) / (4096, 200), 128 tiles", flush=True)
+    ins = [make_matrix_inputs(sh, 46000 + i, torch.bfloat16, 1e-3, 0.02, 1e-3) for i, sh in enumerate(shapes)]
+    w0 = [w.clone() for w, _, _ in ins]
+    m0 = [m.clone() for _, _, m in ins]
+    oo = [torch.zeros(sh, dtype=torch.float32, device="cuda") for sh in shapes]
+
+    def run(persist):
+        monkeypatch.setenv("MU_PERSIST", "1" if persist else "0")
+        for (w, _, m), a, b in zip(ins, w0, m0):
+            w.copy_(a)
+            m.copy_(b)
+        L.mu_profile_enable(True)
+        try:
+            nso.muon_step([x[0] for x in ins], [x[1] for x in ins], [x[2] for x in ins], lr=0.02,
+                          weight_decay=0.01, ortho_outs=oo)
+            torch.cuda.synchronize()
+        finally:
+            L.mu_profile_enable(False)
+        return [w.clone() for w, _, _ in ins], [o.clone() for o in oo]
+
+    w_tile, o_tile = run(False)
+    w_pers, o_pers = run(True)
+    for i in range(len(shapes)):
+        assert torch.equal(o_pers[i], o_tile[i]), i
+        assert torch.equal(w_pers[i], w_tile[i]), i
