@@ -180,7 +180,14 @@ struct Plan {
 };
 
 int choose_tile(int ns_dt, int64_t m, int64_t n) {
-    if (ns_dt == DT_F32) return 64;
+    if (ns_dt == DT_F32) {
+        // 128 x 128 tiles halve the operand traffic per flop where the short
+        // side fills them; 64 x 64 otherwise
+        if (m < 128) return 64;
+        const double w128 = (double)round_up(m, 128) * round_up(m, 128) * round_up(n, 128);
+        const double w64 = (double)round_up(m, 64) * round_up(m, 64) * round_up(n, 64);
+        return w128 <= 1.15 * w64 ? 128 : 64;
+    }
     if (m < 256) return 128;
     // prefer 256 unless its padding costs clearly more than 128's
     const double w256 = (double)round_up(m, 256) * round_up(m, 256) * round_up(n, 256);
@@ -764,7 +771,7 @@ int launch_sequence(const Plan& pl, char* ws, const mu_muon_hparams* hp, int src
             ga.cs = dcs;
             ga.with_update = step_mode ? 1 : 0;
             auto launch = [&](const GemmArgs& a) {
-                return ns_dt == DT_BF16 ? launch_gemm_bf16(a, g.tile, s) : launch_gemm_f32(a, s);
+                return ns_dt == DT_BF16 ? launch_gemm_bf16(a, g.tile, s) : launch_gemm_f32(a, g.tile, s);
             };
             // Gram (the fused launch left a fused group's last B in `a`)
             if (g.fused) {

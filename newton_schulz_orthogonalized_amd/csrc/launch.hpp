@@ -99,9 +99,9 @@ struct GemmArgs {
     float ca, cb, cc;    // step coefficients
     const CallScalars* cs;   // lr and wd of the last apply's update
 };
-// tile: 256 or 128 (square tiles, bf16) ; float32 uses 64.
+// tile: 256 or 128 (square tiles, bf16); float32: 128 or 64.
 hipError_t launch_gemm_bf16(const GemmArgs& a, int tile, hipStream_t s);
-hipError_t launch_gemm_f32(const GemmArgs& a, hipStream_t s);
+hipError_t launch_gemm_f32(const GemmArgs& a, int tile, hipStream_t s);
 
 // The tile maps of one call: per segment (a tile group's Gram or apply
 // order), entry t of `out` for logical tile t, found from the segment's tile

@@ -1004,11 +1004,12 @@ __global__ __launch_bounds__(NTHR) void k_gemm_bf16(GemmArgs A) {
 // k = 4*(l>>4) + s in MFMA s for both operands (any permutation of k shared by
 // both operands leaves the sum unchanged).
 // ---------------------------------------------------------------------------
-template <bool SYM, typename TSRC>
+template <int TS, bool SYM, typename TSRC>
 __global__ __launch_bounds__(NTHR) void k_gemm_f32(GemmArgs A) {
-    constexpr int TS = 64, BK = 32, WT = 32, F = 2;
+    constexpr int BK = 32, WT = TS / 2, F = WT / 16;
     constexpr int SPK = BK + 4;
     constexpr int LA = TS * SPK;
+    constexpr int NL = TS * BK / 4 / NTHR;   // 16-byte loads per operand per thread and step
     __shared__ __attribute__((aligned(16))) float smem[2 * 2 * LA];
 
     const int wg = xcd_remap(blockIdx.x, gridDim.x);
@@ -1038,11 +1039,11 @@ __global__ __launch_bounds__(NTHR) void k_gemm_f32(GemmArgs A) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm0 = (wave >> 1) * WT, wn0 = (wave & 1) * WT;
 
-    f32x4 ga[2], gb[2];
+    f32x4 ga[NL], gb[NL];
     auto gload = [&](int kt) {
         const int k0 = kt * BK;
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
+        for (int s = 0; s < NL; ++s) {
             const int q = s * NTHR + tid;
             ga[s] = *gp((const f32x4*)(pt + (int64_t)(q >> 3) * ldp + k0 + (q & 7) * 4));
             gb[s] = *gp((const f32x4*)(qt + (int64_t)(q >> 3) * ldq + k0 + (q & 7) * 4));
@@ -1052,7 +1053,7 @@ __global__ __launch_bounds__(NTHR) void k_gemm_f32(GemmArgs A) {
         float* as = smem + stage * 2 * LA;
         float* bs = as + LA;
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
+        for (int s = 0; s < NL; ++s) {
             const int q = s * NTHR + tid;
             *(f32x4*)(as + (q >> 3) * SPK + (q & 7) * 4) = ga[s];
             *(f32x4*)(bs + (q >> 3) * SPK + (q & 7) * 4) = gb[s];
@@ -1097,7 +1098,16 @@ __global__ __launch_bounds__(NTHR) void k_gemm_f32(GemmArgs A) {
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
-    epilogue<SYM, float, TSRC, F>(A, P, ti, tj, TS, wm0, wn0, acc, smem + wave * 16 * (WT + 4), nullptr);
+    // epilogue staging per wave: the 16-row strip, and with 4 x 4 fragments
+    // the last apply's two halves of WT/2 x 64 floats
+    if constexpr (F % 4 == 0) {
+        constexpr int STG = (WT / 2) * 64;
+        static_assert(STG >= 16 * (WT + 4) && 8 * STG <= 2 * 2 * LA, "staging fits the stage buffers");
+        float* st = smem + wave * 2 * STG;
+        epilogue<SYM, float, TSRC, F>(A, P, ti, tj, TS, wm0, wn0, acc, st, st + STG);
+    } else {
+        epilogue<SYM, float, TSRC, F>(A, P, ti, tj, TS, wm0, wn0, acc, smem + wave * 16 * (WT + 4), nullptr);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -1411,18 +1421,25 @@ hipError_t launch_gemm_bf16(const GemmArgs& a, int tile, hipStream_t s) {
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_gemm_f32(const GemmArgs& a, hipStream_t s) {
-    if (a.total_tiles <= 0) return hipSuccess;
+template <int TS>
+hipError_t launch_f32_t(const GemmArgs& a, hipStream_t s) {
     const bool sym = a.mode == GM_GRAM || a.mode == GM_GRAM2;
     const unsigned grid = (unsigned)((a.total_tiles + 7) / 8 * 8);
     if (a.src_dtype == DT_BF16) {
-        if (sym) hipLaunchKernelGGL((k_gemm_f32<true, bf16>), dim3(grid), dim3(NTHR), 0, s, a);
-        else hipLaunchKernelGGL((k_gemm_f32<false, bf16>), dim3(grid), dim3(NTHR), 0, s, a);
+        if (sym) hipLaunchKernelGGL((k_gemm_f32<TS, true, bf16>), dim3(grid), dim3(NTHR), 0, s, a);
+        else hipLaunchKernelGGL((k_gemm_f32<TS, false, bf16>), dim3(grid), dim3(NTHR), 0, s, a);
     } else {
-        if (sym) hipLaunchKernelGGL((k_gemm_f32<true, float>), dim3(grid), dim3(NTHR), 0, s, a);
-        else hipLaunchKernelGGL((k_gemm_f32<false, float>), dim3(grid), dim3(NTHR), 0, s, a);
+        if (sym) hipLaunchKernelGGL((k_gemm_f32<TS, true, float>), dim3(grid), dim3(NTHR), 0, s, a);
+        else hipLaunchKernelGGL((k_gemm_f32<TS, false, float>), dim3(grid), dim3(NTHR), 0, s, a);
     }
     return hipGetLastError();
+}
+
+hipError_t launch_gemm_f32(const GemmArgs& a, int tile, hipStream_t s) {
+    if (a.total_tiles <= 0) return hipSuccess;
+    if (tile == 64) return launch_f32_t<64>(a, s);
+    if (tile == 128) return launch_f32_t<128>(a, s);
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_tilemap(const TileMapArgs& a, hipStream_t s) {
