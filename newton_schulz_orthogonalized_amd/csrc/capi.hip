@@ -181,9 +181,12 @@ struct Plan {
 
 int choose_tile(int ns_dt, int64_t m, int64_t n) {
     if (ns_dt == DT_F32) {
-        // 128 x 128 tiles halve the operand traffic per flop where the short
-        // side fills them; 64 x 64 otherwise
-        if (m < 128) return 64;
+        // 128 x 128 tiles halve the operand traffic per flop, which pays on
+        // large blocks (Llama-1B-shaped set 6.5 % faster); on small ones the
+        // four times fewer workgroups cost more (float32 128 x 256: 0.11 ->
+        // 0.23 ms per step; GPT-2-shaped, m = 768: 0.8 % faster), so 64 x 64
+        // below a short side of 1024
+        if (m < 1024) return 64;
         const double w128 = (double)round_up(m, 128) * round_up(m, 128) * round_up(n, 128);
         const double w64 = (double)round_up(m, 64) * round_up(m, 64) * round_up(n, 64);
         return w128 <= 1.15 * w64 ? 128 : 64;

@@ -90,6 +90,26 @@ def test_fp32_config_step_128x256():
     assert abs(norms[0] - ref["norms"][0]) <= 1e-5 * ref["norms"][0]
 
 
+@pytest.mark.parametrize("shape", [(1024, 1536), (1536, 1024), (1100, 1300), (1300, 1100)])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32-param", "bf16-param"])
+def test_f32_step_large_tiles(shape, dtype):
+    """Float32 Newton-Schulz on blocks whose short side takes the 128 x 128
+    float32 tiles (exact and ragged, wide and tall; the last apply's staged
+    update for float32 and bf16 parameters): M, O, the update and the norm
+    against the oracle."""
+    print(f"[f32 step, 128 tiles] shape={shape} dtype={dtype}", flush=True)
+    w0, w1, m1, o, norms, ref = _step_case(shape, dtype, "f32", 7100, gstd=1e-3, wstd=0.02, mstd=1e-3)
+    assert O.rel_fro(m1, ref["m"]) <= MOM_TOL
+    assert O.rel_fro(o, ref["o"]) <= F32_TOL
+    assert tile_rel_fro(o, ref["o"], 128) <= F32_TOL
+    assert abs(norms[0] - ref["norms"][0]) <= 1e-5 * ref["norms"][0]
+    if dtype == torch.float32:
+        assert O.rel_fro(w1 - w0, ref["w"] - w0) <= F32_TOL
+    else:   # the update with the GPU's O, rounded once to bf16
+        want = w0 - 0.02 * 0.01 * w0 - 0.02 * o
+        assert np.all(np.abs(w1 - want) <= bf16_ulp(want) * 0.5 + 8 * 2.0 ** -24 * (np.abs(w0) + 0.02 * np.abs(o)))
+
+
 @pytest.mark.parametrize("shape", [(768, 2304), (2304, 768), (768, 768), (300, 77), (129, 1000)])
 def test_bf16_step(shape):
     print(f"[bf16 step] shape={shape}", flush=True)
