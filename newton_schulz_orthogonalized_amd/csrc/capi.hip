@@ -115,7 +115,36 @@ struct ProbPlan {
     int item;          // the list entry it comes from
     int tile;          // GEMM tile edge
     size_t x_bytes, a_bytes;
+    bool gs = false;   // Gram-side steps (see below)
+    void* sq[2] = {nullptr, nullptr};   // Gram-side: the two Q buffers (mp x mp)
+    void* bc = nullptr;                 // Gram-side: the second B buffer (the first is d.b)
 };
+
+// Gram-side steps. For a wide block with np > 2 mp the first R cubic steps
+// run on the m x m side: with A_k = X_k X_k^T and B_k = a_k I + b_k A_k, every
+// X_k is Q_k X_0 for the polynomial Q_k = B_{k-1} .. B_0 in A_0, and
+//   A_{k+1} = B_k A_k B_k = B_k (B_k A_k),   Q_{k+1} = B_k Q_k,
+// because polynomials in A_0 commute. Step k < R - 1 then costs three m x m
+// products (T = B_k A_k, Q_{k+1}, A_{k+1} = B_k T) instead of an m x m x n
+// Gram and an m x m x n apply, and X_R = Q_R X_0 is formed once (the restart),
+// after which the remaining steps run as usual from an exactly formed X_R and
+// its own Gram. In exact arithmetic every X_k is the same matrix; in bf16 the
+// restart bounds the drift between the carried A_k and Q_k, and no later than
+// step 4, as the error of the result then stays at that of the plain steps
+// (CPU emulation of both in bf16 against float64 on Gaussian, power-law and
+// rank-one-dominated inputs). Flops per block, cubic steps S, restart R:
+// plain 3 S m^2 n; Gram-side m^2 n + (6 R - 6) m^3 + 2 m^2 n + 3 (S - R) m^2 n,
+// fewer by 3 (R - 1)(m^2 n - 2 m^3), so only blocks with n > 2m take them; and
+// only large ones (mp >= GS_MIN_M), since the extra launches of small sets
+// cost more than they save. MU_GRAMSIDE=0 turns them off.
+constexpr int GS_MIN_M = 1024;
+constexpr int GS_MAX_RESTART = 4;
+bool gramside_enabled() {
+    const char* e = std::getenv("MU_GRAMSIDE");
+    return !(e && e[0] == '0');
+}
+// Restart step R for S cubic steps (0: no Gram-side steps).
+int gs_restart(size_t steps) { return steps >= 3 ? (int)std::min<size_t>(steps - 1, GS_MAX_RESTART) : 0; }
 
 struct Group {
     int tile;
@@ -126,6 +155,14 @@ struct Group {
     std::vector<int> apply_order;  // the same for the apply
     std::vector<int> gram_prefix, apply_prefix;
     size_t gram_tmap, apply_tmap;  // offsets of its tile maps in the workspace
+    // Gram-side groups: the m x m products of all problems run through extra
+    // descriptors (one list per launch, in launch order, as indices into the
+    // descriptor table) over tile maps of one (sq) or two (sq2) mp x mp
+    // products per problem, in table order
+    bool gs = false;
+    std::vector<int> aux_lists;
+    std::vector<int> sq_prefix, sq2_prefix;
+    size_t sq_tmap = 0, sq2_tmap = 0;
 };
 
 // Gram tile order and XCD windows. The Gram launches walk a group's problems
@@ -172,6 +209,8 @@ struct Plan {
     std::vector<Group> groups;
     int ns_dt;
     bool quintic;
+    int gs_R = 0;                 // restart step of the Gram-side groups
+    int n_aux = 0;                // their extra descriptors (after the problems' own)
     // workspace layout (the uploaded table: call scalars, descriptors, prefixes)
     size_t off_scalars, off_table, off_prep_prefix, off_group_prefix, table_bytes;
     size_t off_partials, off_fold, off_xexp, off_tmap, off_queues, off_bufs, total;
@@ -263,17 +302,24 @@ void build_plan(const std::vector<Item>& items, int ns_dt, const std::vector<Coe
     // X^T buffers: read by the fp32 apply and by the finish kernel
     // (ns_steps == 0, tall blocks); the bf16 kernels read X only
     for (auto& pp : all) pp.d.xt_used = (ns_dt == DT_F32 || co.empty()) ? 1 : 0;
+    // Gram-side blocks: bf16, every step cubic, 256 tiles, wide enough to gain
+    pl.gs_R = (ns_dt == DT_BF16 && !pl.quintic && gramside_enabled()) ? gs_restart(co.size()) : 0;
+    for (auto& pp : all)
+        pp.gs = pl.gs_R > 0 && pp.tile == 256 && pp.d.mp >= GS_MIN_M && pp.d.np > 2 * pp.d.mp;
     pl.probs.clear();
     pl.groups.clear();
-    for (int gi = 0; gi < 4; ++gi) {
-        const int t = gi == 0 ? 256 : gi == 3 ? 64 : 128;
-        const bool fused = gi == 2;
+    pl.n_aux = 0;
+    // groups: 256 tiles, 256 Gram-side, 128, 128 fused, 64
+    for (int gi = 0; gi < 5; ++gi) {
+        const int t = gi <= 1 ? 256 : gi == 4 ? 64 : 128;
+        const bool fused = gi == 3, gs = gi == 1;
         Group g;
         g.tile = t;
         g.fused = fused;
+        g.gs = gs;
         g.first = (int)pl.probs.size();
         for (auto& pp : all)
-            if (pp.tile == t && is_fused(pp) == fused) pl.probs.push_back(pp);
+            if (pp.tile == t && is_fused(pp) == fused && pp.gs == gs) pl.probs.push_back(pp);
         g.count = (int)pl.probs.size() - g.first;
         if (g.count == 0) continue;
         g.gram_order.resize(g.count);
@@ -297,8 +343,37 @@ void build_plan(const std::vector<Item>& items, int ns_dt, const std::vector<Coe
             g.apply_prefix.push_back(g.apply_prefix.back() + T * (d.np / t));
         }
         g.gram_window = gram_window_for(pl.probs, g.first, g.count, g.gram_prefix.back());
+        if (gs) {
+            g.sq_prefix.assign(1, 0);
+            g.sq2_prefix.assign(1, 0);
+            for (int i = 0; i < g.count; ++i) {
+                const int T = pl.probs[g.first + i].d.mp / t;
+                g.sq_prefix.push_back(g.sq_prefix.back() + T * T);
+                g.sq2_prefix.push_back(g.sq2_prefix.back() + T * T);
+                g.sq2_prefix.push_back(g.sq2_prefix.back() + T * T);
+            }
+            // descriptor lists, in launch order (indices past the problems'
+            // own descriptors; filled in by carve): T_0, D_0, then T_k with
+            // Q_{k+1} and D_k for k = 1 .. R-2, then Q_R and the restart
+            const int R = pl.gs_R;
+            auto list = [&](int per) {
+                g.aux_lists.push_back(pl.n_aux);
+                pl.n_aux += per * g.count;
+            };
+            list(1);
+            list(1);
+            for (int k = 1; k <= R - 2; ++k) {
+                list(2);
+                list(1);
+            }
+            list(1);
+            list(1);
+        }
         pl.groups.push_back(std::move(g));
     }
+    // aux indices are relative to the end of the problems' own descriptors
+    for (auto& g : pl.groups)
+        for (int& li : g.aux_lists) li += (int)pl.probs.size();
     pl.prep_prefix.assign(1, 0);
     pl.total_parts = 0;
     for (auto& pp : pl.probs) {
@@ -311,11 +386,13 @@ void build_plan(const std::vector<Item>& items, int ns_dt, const std::vector<Coe
     pl.off_scalars = o;
     o += sizeof(CallScalars);
     pl.off_table = o;
-    o += sizeof(NsProb) * P;
+    o += sizeof(NsProb) * (P + (size_t)pl.n_aux);
     pl.off_prep_prefix = o;
     o += sizeof(int) * (P + 1);
     pl.off_group_prefix = o;
-    for (auto& g : pl.groups) o += sizeof(int) * (g.gram_order.size() + g.apply_order.size() + g.gram_prefix.size() + g.apply_prefix.size());
+    for (auto& g : pl.groups)
+        o += sizeof(int) * (g.gram_order.size() + g.apply_order.size() + g.gram_prefix.size() + g.apply_prefix.size() +
+                            g.sq_prefix.size() + g.sq2_prefix.size());
     pl.table_bytes = o;
     o = align_up(o);
     pl.off_partials = o;
@@ -330,19 +407,32 @@ void build_plan(const std::vector<Item>& items, int ns_dt, const std::vector<Coe
         if (!g.fused) o += sizeof(TileEntry) * (size_t)g.gram_prefix.back();
         g.apply_tmap = o;
         o += sizeof(TileEntry) * (size_t)g.apply_prefix.back();
+        if (g.gs) {
+            g.sq_tmap = o;
+            o += sizeof(TileEntry) * (size_t)g.sq_prefix.back();
+            g.sq2_tmap = o;
+            if (pl.gs_R >= 3) o += sizeof(TileEntry) * (size_t)g.sq2_prefix.back();
+        }
     }
     o = align_up(o);
     // the tile counters of persistent launches, one set of eight per GEMM
     // launch in the order launch_sequence issues them
     pl.n_gemm = 0;
-    if (ns_dt == DT_BF16)
+    if (ns_dt == DT_BF16) {
         for (size_t k = 0; k < co.size(); ++k)
             for (auto& g : pl.groups)
-                pl.n_gemm += g.fused ? (k + 1 == co.size() ? 1 : 0) : (co[k].c != 0.f ? 3 : 2);
+                if (!g.gs) pl.n_gemm += g.fused ? (k + 1 == co.size() ? 1 : 0) : (co[k].c != 0.f ? 3 : 2);
+        for (auto& g : pl.groups)   // first Gram, 2 (R - 1) m x m launches, Q_R, restart, 2 (S - R)
+            if (g.gs) pl.n_gemm += 2 * (int)co.size() + 1;
+    }
     pl.off_queues = o;
     o = align_up(o + sizeof(int) * 8 * (size_t)pl.n_gemm);
     pl.off_bufs = o;
-    for (auto& pp : pl.probs) o += (pp.d.xt_used ? 4 : 2) * pp.x_bytes + pp.a_bytes * (pl.quintic ? 2 : 1);
+    // per problem: X ping-pong (and X^T), a (and b for quintic steps); a
+    // Gram-side problem adds b, two Q buffers and a second B buffer (A_k and
+    // T_k live in its second X buffer, which is free until the restart)
+    for (auto& pp : pl.probs)
+        o += (pp.d.xt_used ? 4 : 2) * pp.x_bytes + pp.a_bytes * (pl.quintic ? 2 : pp.gs ? 5 : 1);
     pl.total = o;
 }
 
@@ -382,11 +472,19 @@ void carve(Plan& pl, char* ws, std::vector<char>& host_table) {
         }
         d.a = ws + o;
         o += pl.probs[i].a_bytes;
-        if (pl.quintic) {
+        if (pl.quintic || pl.probs[i].gs) {
             d.b = ws + o;
             o += pl.probs[i].a_bytes;
         } else {
             d.b = nullptr;
+        }
+        if (pl.probs[i].gs) {
+            for (int j = 0; j < 2; ++j) {
+                pl.probs[i].sq[j] = ws + o;
+                o += pl.probs[i].a_bytes;
+            }
+            pl.probs[i].bc = ws + o;
+            o += pl.probs[i].a_bytes;
         }
         d.partials = partials + part;
         part += d.nparts;
@@ -396,6 +494,50 @@ void carve(Plan& pl, char* ws, std::vector<char>& host_table) {
     host_table.assign(pl.table_bytes, 0);
     char* h = host_table.data();
     for (size_t i = 0; i < pl.probs.size(); ++i) std::memcpy(h + pl.off_table + i * sizeof(NsProb), &pl.probs[i].d, sizeof(NsProb));
+    // Gram-side descriptors: an mp x mp product C = L R (L read as `a`, R as
+    // x[0], C written to x[1], the dual apply's B' to b), or the restart
+    // X_R = Q_R X_0 over the block's own X buffers
+    for (const Group& g : pl.groups) {
+        if (!g.gs) continue;
+        const int R = pl.gs_R;
+        int li = 0;
+        auto put_list = [&](int per, auto&& make) {
+            NsProb* dst = (NsProb*)(h + pl.off_table) + g.aux_lists[li++];
+            for (int i = 0; i < g.count; ++i)
+                for (int j = 0; j < per; ++j) dst[per * i + j] = make(pl.probs[g.first + i], j);
+        };
+        auto sqd = [](const NsProb& d, void* l, void* r, void* out, void* bout) {
+            NsProb q = d;
+            q.np = d.mp;
+            q.a = l;
+            q.b = bout;
+            q.x[0] = r;
+            q.x[1] = out;
+            q.xt[0] = q.xt[1] = nullptr;
+            return q;
+        };
+        // per problem: A_k in x[1], T_k after it; B_k alternating between b
+        // and bc; Q_1 = f B_0 is the first Gram's `a`, Q_{k+1} goes to sq[(k+1) % 2]
+        auto A_of = [](const ProbPlan& pp) { return pp.d.x[1]; };
+        auto T_of = [](const ProbPlan& pp) { return (void*)((char*)pp.d.x[1] + pp.a_bytes); };
+        auto B_of = [](const ProbPlan& pp, int k) { return (k & 1) ? pp.bc : pp.d.b; };
+        auto Q_of = [](const ProbPlan& pp, int k) { return k == 1 ? pp.d.a : pp.sq[k & 1]; };
+        put_list(1, [&](const ProbPlan& pp, int) { return sqd(pp.d, B_of(pp, 0), A_of(pp), T_of(pp), nullptr); });
+        put_list(1, [&](const ProbPlan& pp, int) { return sqd(pp.d, B_of(pp, 0), T_of(pp), A_of(pp), B_of(pp, 1)); });
+        for (int k = 1; k <= R - 2; ++k) {
+            put_list(2, [&](const ProbPlan& pp, int j) {
+                return j == 0 ? sqd(pp.d, B_of(pp, k), A_of(pp), T_of(pp), nullptr)
+                              : sqd(pp.d, B_of(pp, k), Q_of(pp, k), Q_of(pp, k + 1), nullptr);
+            });
+            put_list(1, [&](const ProbPlan& pp, int) { return sqd(pp.d, B_of(pp, k), T_of(pp), A_of(pp), B_of(pp, k + 1)); });
+        }
+        put_list(1, [&](const ProbPlan& pp, int) { return sqd(pp.d, B_of(pp, R - 1), Q_of(pp, R - 1), Q_of(pp, R), nullptr); });
+        put_list(1, [&](const ProbPlan& pp, int) {
+            NsProb q = pp.d;
+            q.a = Q_of(pp, R);
+            return q;
+        });
+    }
     std::memcpy(h + pl.off_prep_prefix, pl.prep_prefix.data(), sizeof(int) * pl.prep_prefix.size());
     size_t o2 = pl.off_group_prefix;
     for (auto& g : pl.groups) {
@@ -407,6 +549,10 @@ void carve(Plan& pl, char* ws, std::vector<char>& host_table) {
         o2 += sizeof(int) * g.gram_prefix.size();
         std::memcpy(h + o2, g.apply_prefix.data(), sizeof(int) * g.apply_prefix.size());
         o2 += sizeof(int) * g.apply_prefix.size();
+        if (!g.sq_prefix.empty()) std::memcpy(h + o2, g.sq_prefix.data(), sizeof(int) * g.sq_prefix.size());
+        o2 += sizeof(int) * g.sq_prefix.size();
+        if (!g.sq2_prefix.empty()) std::memcpy(h + o2, g.sq2_prefix.data(), sizeof(int) * g.sq2_prefix.size());
+        o2 += sizeof(int) * g.sq2_prefix.size();
     }
 }
 
@@ -662,7 +808,7 @@ int launch_sequence(const Plan& pl, char* ws, const mu_muon_hparams* hp, int src
     }
 
     // group-level device pointers
-    std::vector<const int*> gram_ord, apply_ord, gram_pf, apply_pf;
+    std::vector<const int*> gram_ord, apply_ord, gram_pf, apply_pf, sq_pf, sq2_pf;
     {
         size_t o = pl.off_group_prefix;
         for (auto& g : pl.groups) {
@@ -674,6 +820,10 @@ int launch_sequence(const Plan& pl, char* ws, const mu_muon_hparams* hp, int src
             o += sizeof(int) * g.gram_prefix.size();
             apply_pf.push_back((const int*)(ws + o));
             o += sizeof(int) * g.apply_prefix.size();
+            sq_pf.push_back((const int*)(ws + o));
+            o += sizeof(int) * g.sq_prefix.size();
+            sq2_pf.push_back((const int*)(ws + o));
+            o += sizeof(int) * g.sq2_prefix.size();
         }
     }
     // tile maps of every GEMM launch of the call (the table above is in place)
@@ -694,6 +844,21 @@ int launch_sequence(const Plan& pl, char* ws, const mu_muon_hparams* hp, int src
                 sg.ts = g.tile;
                 sg.sym = sym;
                 ta.total += sym ? g.gram_prefix.back() : g.apply_prefix.back();
+            }
+            // Gram-side groups: one and two mp x mp products per problem,
+            // in table order (the shapes of every such list)
+            for (int two = 0; g.gs && two <= (pl.gs_R >= 3 ? 1 : 0); ++two) {
+                if (ta.nseg >= TILEMAP_SEGS) return fail(MU_ERR_INVALID_ARG, "too many tile groups");
+                TileMapSeg& sg = ta.seg[ta.nseg++];
+                sg.prefix = two ? sq2_pf[gi] : sq_pf[gi];
+                sg.order = nullptr;
+                sg.probs = dprobs + g.aux_lists[two ? 2 : 0];
+                sg.out = (TileEntry*)(ws + (two ? g.sq2_tmap : g.sq_tmap));
+                sg.nprobs = two ? 2 * g.count : g.count;
+                sg.start = ta.total;
+                sg.ts = g.tile;
+                sg.sym = 0;
+                ta.total += two ? g.sq2_prefix.back() : g.sq_prefix.back();
             }
         }
         ta.queues = (int*)(ws + pl.off_queues);
@@ -754,6 +919,7 @@ int launch_sequence(const Plan& pl, char* ws, const mu_muon_hparams* hp, int src
         const bool quint = co[k].c != 0.f;
         for (size_t gi = 0; gi < pl.groups.size(); ++gi) {
             const Group& g = pl.groups[gi];
+            if (g.gs) continue;               // launched below
             if (g.fused && !last) continue;   // done by the fused launch
             double gflops = 0, g2flops = 0, aflops = 0, abytes = 0;
             for (int i = g.first; i < g.first + g.count; ++i) {
@@ -818,6 +984,94 @@ int launch_sequence(const Plan& pl, char* ws, const mu_muon_hparams* hp, int src
         }
         src ^= 1;
     }
+    // Gram-side groups (see gs_restart): the first Gram (dual), the m x m
+    // steps, Q_R, the restart X_R = Q_R X_0, then the plain steps R .. S-1
+    for (const Group& g : pl.groups) {
+        if (!g.gs) continue;
+        const int R = pl.gs_R, S = hp->ns_steps;
+        double fg = 0, fsq = 0, fap = 0, frs = 0, bsq = 0, bap = 0, bup = 0;
+        for (int i = g.first; i < g.first + g.count; ++i) {
+            const double m = pl.probs[i].d.m, n = pl.probs[i].d.n;
+            fg += m * (m + 1) * n;
+            fsq += 2 * m * m * m;
+            fap += 2 * m * m * n + 3 * m * n;
+            frs += 2 * m * m * n;
+            bsq += 2 * m * m * ns_es;
+            bap += 2 * m * n * ns_es;
+            bup += m * n * (ns_es + (step_mode ? 2 * src_es : src_es));
+        }
+        GemmArgs base{};
+        base.src_dtype = src_dt;
+        base.cs = dcs;
+        base.with_update = step_mode ? 1 : 0;
+        const NsProb* own = dprobs + g.first;
+        auto go = [&](GemmArgs a, int kernel, double fl, double by, const char* what) -> int {
+            if (!place(a, g.tile)) return fail(MU_ERR_INVALID_ARG, "internal: GEMM launch count");
+            return timed_launch(kernel, fl, by, s, [&] { return launch_gemm_bf16(a, g.tile, s); }, what);
+        };
+        auto gram = [&](int mode, int sstep, int first, int k) {
+            GemmArgs a = base;
+            a.mode = mode;
+            a.probs = own;
+            a.src = sstep;
+            a.first = first;
+            a.ca = co[k].a;
+            a.cb = co[k].b;
+            a.tmap = (const TileEntry*)(ws + g.gram_tmap);
+            a.total_tiles = g.gram_prefix.back();
+            a.xcd_window = g.gram_window;
+            return a;
+        };
+        auto sq = [&](int mode, int list, bool two, int k) {
+            GemmArgs a = base;
+            a.mode = mode;
+            a.probs = dprobs + g.aux_lists[list];
+            a.ca = co[k].a;
+            a.cb = co[k].b;
+            a.tmap = (const TileEntry*)(ws + (two ? g.sq2_tmap : g.sq_tmap));
+            a.total_tiles = two ? g.sq2_prefix.back() : g.sq_prefix.back();
+            return a;
+        };
+        rc = go(gram(GM_GRAM_DUAL, 0, 1, 0), MU_K_GRAM, fg, 0.0, "gram launch");
+        if (rc) return rc;
+        int li = 0;
+        for (int k = 0; k <= R - 2; ++k) {
+            const bool two = k >= 1;   // T_k, and Q_{k+1} from k = 1 on (Q_1 is the first Gram's B)
+            rc = go(sq(GM_APPLY, li++, two, k), MU_K_APPLY, two ? 2 * fsq : fsq, two ? 2 * bsq : bsq, "apply launch");
+            if (rc) return rc;
+            // A_{k+1} = B_k T_k, and B_{k+1} with step k+1's coefficients
+            rc = go(sq(GM_APPLY_DUAL, li++, false, k + 1), MU_K_APPLY, fsq, 1.5 * bsq, "apply launch");
+            if (rc) return rc;
+        }
+        rc = go(sq(GM_APPLY, li++, false, R - 1), MU_K_APPLY, fsq, bsq, "apply launch");   // Q_R
+        if (rc) return rc;
+        {   // X_R = Q_R X_0, over the blocks' own shapes and apply tile map
+            GemmArgs a = base;
+            a.mode = GM_APPLY;
+            a.probs = dprobs + g.aux_lists[li++];
+            a.tmap = (const TileEntry*)(ws + g.apply_tmap);
+            a.total_tiles = g.apply_prefix.back();
+            rc = go(a, MU_K_APPLY, frs, bap, "apply launch");
+            if (rc) return rc;
+        }
+        int gsrc = 1;   // X_R is in x[1]
+        for (int k = R; k < S; ++k) {
+            const bool last = k + 1 == S;
+            rc = go(gram(GM_GRAM, gsrc, 0, k), MU_K_GRAM, fg, 0.0, "gram launch");
+            if (rc) return rc;
+            GemmArgs a = base;
+            a.mode = last ? GM_APPLY_LAST : GM_APPLY;
+            a.probs = own;
+            a.src = gsrc;
+            a.ca = co[k].a;
+            a.cb = co[k].b;
+            a.tmap = (const TileEntry*)(ws + g.apply_tmap);
+            a.total_tiles = g.apply_prefix.back();
+            rc = go(a, MU_K_APPLY, fap, last ? bup : bap, "apply launch");
+            if (rc) return rc;
+            gsrc ^= 1;
+        }
+    }
     return MU_OK;
 }
 
@@ -876,6 +1130,7 @@ std::vector<unsigned char> call_key(const std::vector<Item>& items, const mu_muo
     put(k, src_dt);
     put(k, hp->ns_precision);
     put(k, hp->ns_steps);
+    put(k, (int)gramside_enabled());
     for (const Coeff& c : coeffs_of(hp)) put(k, c);
     put(k, ws);
     put(k, ws_bytes);

@@ -73,7 +73,14 @@ enum GemmMode : int {
     GM_GRAM2 = 1,       // B = f (a I + b A + c A A^T)                                               (upper, mirrored)
     GM_APPLY = 2,       // X' = B X, B the matrix the Gram pass(es) left (f = 1/||U|| on the first step, else 1)
     GM_APPLY_LAST = 3,  // as GM_APPLY, result O goes to the update or to `out`
+    // Gram-side steps (see the planner): the first Gram of a wide block also
+    // keeps A0 = f^2 X X^T (-> x[src^1], mp x mp) and the unfolded
+    // B0 = a I + b A0 (-> b) besides B = f B0 (-> a); and an m x m product
+    // C = B X whose epilogue also forms the next step's B' = a I + b C (-> b)
+    GM_GRAM_DUAL = 4,
+    GM_APPLY_DUAL = 5,
 };
+inline bool gemm_mode_sym(int mode) { return mode == GM_GRAM || mode == GM_GRAM2 || mode == GM_GRAM_DUAL; }
 
 // Logical tile t of a GEMM launch, resolved once per call by k_tilemap:
 // problem p (an index into GemmArgs::probs) and tile coordinates ti | tj << 16
@@ -107,7 +114,7 @@ hipError_t launch_gemm_f32(const GemmArgs& a, int tile, hipStream_t s);
 // order), entry t of `out` for logical tile t, found from the segment's tile
 // prefix over its problems (taken in `order`) and the tile enumeration of the
 // GEMM kernels. One thread per tile over all segments.
-constexpr int TILEMAP_SEGS = 8;   // 4 tile groups x (Gram, apply)
+constexpr int TILEMAP_SEGS = 12;  // tile groups x (Gram, apply), plus the m x m maps of Gram-side steps
 struct TileMapSeg {
     const int* prefix;     // nprobs+1 cumulative tiles
     const int* order;      // group-local problem at each prefix position

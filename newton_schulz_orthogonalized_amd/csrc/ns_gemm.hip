@@ -275,6 +275,10 @@ __device__ __forceinline__ void wave_lds_sync() { asm volatile("" ::: "memory");
 //   A^2 pass             B = f (a I + b A + c A A^T)  -> P.b (mirrored)
 //   apply                X' = B X                     -> X' (and X'^T, fp32 only)
 //   last apply           O = B X -> parameter update (or output)
+//   dual Gram (first step of a Gram-side block): B = f (a I + b f^2 X X^T)
+//                        -> P.a, and also A0 = f^2 X X^T -> X' buffer (mp x mp),
+//                        B0 = a I + b f^2 X X^T -> P.b (all mirrored)
+//   dual apply (m x m)   C = B X -> X', and B' = a I + b C -> P.b
 // On the first step X holds U itself, and f (a X0 + b (X0 X0^T) X0) with
 // X0 = f U is exactly B U for these B. Folding a I and f into B keeps X and
 // any scaling out of the apply epilogue; padding stays zero because a padded
@@ -330,7 +334,9 @@ __device__ __forceinline__ void epilogue_mode(const GemmArgs& A, const NsProb& P
         us.wd = gp(A.cs)->wd;
         us.cautious = gp(A.cs)->cautious != 0;
     }
-    constexpr bool gram = mode == GM_GRAM || mode == GM_GRAM2;
+    constexpr bool dual = mode == GM_GRAM_DUAL;
+    constexpr bool adual = mode == GM_APPLY_DUAL;
+    constexpr bool gram = mode == GM_GRAM || mode == GM_GRAM2 || dual;
     const float f = gram && A.first ? P.fold[0] : 1.f;   // the apply takes it through B
     const bool diag = gram && ti == tj;
     if (diag && wm0 > wn0) return;   // below the diagonal: written by the mirror of the quadrant above
@@ -379,9 +385,14 @@ __device__ __forceinline__ void epilogue_mode(const GemmArgs& A, const NsProb& P
     // Gram scale and diagonal term
     // Gram scale gs, diagonal term gd, and (A^2 pass) the factor on A
     float gs = f * f, gd = 0.f, ga = A.cb;
-    if (mode == GM_GRAM && !A.use_b) { gs = A.cb * f * f * f; gd = A.ca * f; }
+    if ((mode == GM_GRAM || dual) && !A.use_b) { gs = A.cb * f * f * f; gd = A.ca * f; }
     if (mode == GM_GRAM2) { gs = A.cc * f; gd = A.ca * f; ga = A.cb * f; }
     TX* gdst = (TX*)(mode == GM_GRAM2 ? P.b : P.a);
+    // the dual modes' extra outputs: A0 (scale f^2) and the unfolded B0
+    // (scale b f^2, diagonal a) of the dual Gram; B' = a I + b C of the dual apply
+    const float s_a0 = dual ? f * f : 0.f, s_b0 = dual ? A.cb * f * f : 0.f;
+    TX* a0dst = dual ? (TX*)(A.src ? P.x[0] : P.x[1]) : nullptr;
+    TX* b0dst = (dual || adual) ? (TX*)P.b : nullptr;
     // A^2 pass: B = gd I + ga A + gs A A^T takes A over the whole block. The
     // stored A is exactly symmetric (the Gram writes both triangles from the
     // same values), so the four accumulator rows r .. r+3 of a lane's column
@@ -530,6 +541,14 @@ __device__ __forceinline__ void epilogue_mode(const GemmArgs& A, const NsProb& P
 #pragma unroll
                         for (int e = 0; e < 8; ++e) v[e] = a2 ? w[e] : gs * w[e];
                         store8<TX>(tdst(gdst, mp, mp, c, r0, fm, fp), v);
+                        if constexpr (dual) {
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) v[e] = s_a0 * w[e];
+                            store8<TX>(tdst(a0dst, mp, mp, c, r0, fm, fp), v);
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) v[e] = s_b0 * w[e];
+                            store8<TX>(tdst(b0dst, mp, mp, c, r0, fm, fp), v);
+                        }
                     }
                 } else {
 #pragma unroll
@@ -602,6 +621,20 @@ __device__ __forceinline__ void epilogue_mode(const GemmArgs& A, const NsProb& P
                 // a diagonal wave block stores its fragments on or above the
                 // diagonal only (this lane's fragment: c8 / 16)
                 if (tri && c8 / 16 < fm) continue;
+                if constexpr (dual) {
+                    float u[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) u[e] = s_a0 * v[e];
+                    store8<TX>(rdst(a0dst, mp, mp, r, c, fm, pass), u);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) u[e] = s_b0 * v[e];
+                    if (diag) {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            if (r == c + e) u[e] += A.ca;
+                    }
+                    store8<TX>(rdst(b0dst, mp, mp, r, c, fm, pass), u);
+                }
                 if constexpr (!a2) {   // (the A^2 pass staged B's values)
 #pragma unroll
                     for (int e = 0; e < 8; ++e) v[e] *= gs;
@@ -614,6 +647,12 @@ __device__ __forceinline__ void epilogue_mode(const GemmArgs& A, const NsProb& P
                 store8<TX>(rdst(gdst, mp, mp, r, c, fm, pass), v);
             } else {
                 if constexpr (!last) {
+                    if constexpr (adual) {   // B' = a I + b C (the block is square: np == mp)
+                        float u[8];
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) u[e] = A.cb * v[e] + (ti == tj && r == c + e ? A.ca : 0.f);
+                        store8<TX>(rdst(b0dst, mp, mp, r, c, fm, pass), u);
+                    }
                     // X' is read back only by the next step's launches:
                     // stored non-temporally (0.1 ms per launch faster on
                     // the 8B-shaped set, same box)
@@ -643,6 +682,7 @@ __device__ __forceinline__ void epilogue_mode(const GemmArgs& A, const NsProb& P
 template <bool SYM, typename TX, typename TS, int F>
 __device__ __forceinline__ void epilogue(const GemmArgs& A, const NsProb& P, int ti, int tj, int TS_, int wm0,
                                          int wn0, f32x4 (&acc)[F][F], float* st, float* st2) {
+    // (the float32 kernel's: the dual modes run in bf16 only)
     if constexpr (SYM) {
         if (A.mode == GM_GRAM) epilogue_mode<GM_GRAM, TX, TS, F>(A, P, ti, tj, TS_, wm0, wn0, acc, st, st2);
         else epilogue_mode<GM_GRAM2, TX, TS, F>(A, P, ti, tj, TS_, wm0, wn0, acc, st, st2);
@@ -651,12 +691,19 @@ __device__ __forceinline__ void epilogue(const GemmArgs& A, const NsProb& P, int
         else epilogue_mode<GM_APPLY_LAST, TX, TS, F>(A, P, ti, tj, TS_, wm0, wn0, acc, st, st2);
     }
 }
-// The bf16 kernel's epilogues: LAST (the last apply) has a kernel of its own.
-template <bool SYM, bool LAST, typename TX, typename TS, int F>
+// The bf16 kernel's epilogues, one kernel instance each (EPI): the Gram and
+// A^2 pass or the plain apply (0); the last apply, or for Gram kernels the
+// dual Gram (1); the dual apply (2). The modes of one instance share its code,
+// and the others' code stays out of the instances the plain steps run.
+template <bool SYM, int EPI, typename TX, typename TS, int F>
 __device__ __forceinline__ void epilogue_k(const GemmArgs& A, const NsProb& P, int ti, int tj, int TS_, int wm0,
                                            int wn0, f32x4 (&acc)[F][F], float* st, float* st2) {
-    if constexpr (SYM) epilogue<true, TX, TS, F>(A, P, ti, tj, TS_, wm0, wn0, acc, st, st2);
-    else if constexpr (LAST) epilogue_mode<GM_APPLY_LAST, TX, TS, F>(A, P, ti, tj, TS_, wm0, wn0, acc, st, st2);
+    if constexpr (SYM && EPI == 1) epilogue_mode<GM_GRAM_DUAL, TX, TS, F>(A, P, ti, tj, TS_, wm0, wn0, acc, st, st2);
+    else if constexpr (SYM) {
+        if (A.mode == GM_GRAM) epilogue_mode<GM_GRAM, TX, TS, F>(A, P, ti, tj, TS_, wm0, wn0, acc, st, st2);
+        else epilogue_mode<GM_GRAM2, TX, TS, F>(A, P, ti, tj, TS_, wm0, wn0, acc, st, st2);
+    } else if constexpr (EPI == 1) epilogue_mode<GM_APPLY_LAST, TX, TS, F>(A, P, ti, tj, TS_, wm0, wn0, acc, st, st2);
+    else if constexpr (EPI == 2) epilogue_mode<GM_APPLY_DUAL, TX, TS, F>(A, P, ti, tj, TS_, wm0, wn0, acc, st, st2);
     else epilogue_mode<GM_APPLY, TX, TS, F>(A, P, ti, tj, TS_, wm0, wn0, acc, st, st2);
 }
 
@@ -722,7 +769,7 @@ __device__ __forceinline__ int next_tile(const GemmArgs& A, int& q, int n, int g
     }
 }
 
-template <int TS, bool SYM, typename TSRC, bool LAST>
+template <int TS, bool SYM, typename TSRC, int EPI>
 __global__ __launch_bounds__(NTHR) void k_gemm_bf16(GemmArgs A) {
     constexpr int BK = 32;
     constexpr int NS = 4;
@@ -750,7 +797,7 @@ __global__ __launch_bounds__(NTHR) void k_gemm_bf16(GemmArgs A) {
     const int gstat = (A.total_tiles + 7) / 8 * 8;
     // not the last apply: its epilogue loads a whole block of parameters up
     // front, and with the loop its kernel spilled 57 registers (1-12 % slower)
-    const bool persist = !LAST && A.grid < gstat;
+    const bool persist = !(EPI == 1 && !SYM) && A.grid < gstat;
     __shared__ int s_tile;
     int q = 0, ticket = 0;   // persistent: thread 0's queue, and the ticket it took for the next tile
     int wg;
@@ -782,7 +829,7 @@ __global__ __launch_bounds__(NTHR) void k_gemm_bf16(GemmArgs A) {
         // and read_b).
         const bf16 *pm, *qm;
         int RP, RQ, K;
-        if (mode == GM_GRAM) {
+        if (mode == GM_GRAM || (EPI == 1 && SYM)) {   // Gram, dual Gram
             pm = qm = (const bf16*)(A.src ? P.x[1] : P.x[0]); RP = RQ = P.mp; K = P.np;
         } else if (mode == GM_GRAM2) {
             pm = qm = (const bf16*)P.a; RP = RQ = P.mp; K = P.mp;
@@ -988,7 +1035,7 @@ __global__ __launch_bounds__(NTHR) void k_gemm_bf16(GemmArgs A) {
         // the next tile's ticket, taken here so that the epilogue hides its latency
         // (and after the K loop, whose waits count only the direct loads)
         if (persist && threadIdx.x == 0) ticket = atomicAdd(A.queues + q, 1);
-        epilogue_k<SYM, LAST, bf16, TSRC, F>(A, P, ti, tj, TS, wm0, wn0, acc, st, st2);
+        epilogue_k<SYM, EPI, bf16, TSRC, F>(A, P, ti, tj, TS, wm0, wn0, acc, st, st2);
         if (!persist) return;
         __syncthreads();   // every wave is done with the LDS: its staging is the next tile's ring
         if (threadIdx.x == 0) s_tile = next_tile(A, q, ticket, gstat, win);
@@ -1399,11 +1446,13 @@ hipError_t launch_bf16_t(const GemmArgs& a, hipStream_t s) {
     // the parameter dtype matters only to the last apply's update
     if (!SYM && a.mode == GM_APPLY_LAST) {
         if (a.src_dtype == DT_BF16)
-            hipLaunchKernelGGL((k_gemm_bf16<TS, false, bf16, true>), dim3(grid), dim3(NTHR), 0, s, a);
+            hipLaunchKernelGGL((k_gemm_bf16<TS, false, bf16, 1>), dim3(grid), dim3(NTHR), 0, s, a);
         else
-            hipLaunchKernelGGL((k_gemm_bf16<TS, false, float, true>), dim3(grid), dim3(NTHR), 0, s, a);
+            hipLaunchKernelGGL((k_gemm_bf16<TS, false, float, 1>), dim3(grid), dim3(NTHR), 0, s, a);
+    } else if (a.mode == GM_GRAM_DUAL || a.mode == GM_APPLY_DUAL) {
+        hipLaunchKernelGGL((k_gemm_bf16<TS, SYM, bf16, SYM ? 1 : 2>), dim3(grid), dim3(NTHR), 0, s, a);
     } else {
-        hipLaunchKernelGGL((k_gemm_bf16<TS, SYM, bf16, false>), dim3(grid), dim3(NTHR), 0, s, a);
+        hipLaunchKernelGGL((k_gemm_bf16<TS, SYM, bf16, 0>), dim3(grid), dim3(NTHR), 0, s, a);
     }
     return hipGetLastError();
 }
@@ -1413,7 +1462,7 @@ hipError_t launch_bf16_t(const GemmArgs& a, hipStream_t s) {
 hipError_t launch_gemm_bf16(const GemmArgs& a, int tile, hipStream_t s) {
     if (a.total_tiles <= 0) return hipSuccess;
     const int gstat = (a.total_tiles + 7) / 8 * 8;
-    const bool sym = a.mode == GM_GRAM || a.mode == GM_GRAM2;
+    const bool sym = gemm_mode_sym(a.mode);
     if (a.grid < 1 || a.grid > gstat || (a.grid < gstat && (!a.queues || a.mode == GM_APPLY_LAST)))
         return hipErrorInvalidValue;
     if (tile == 256) return sym ? launch_bf16_t<256, true>(a, s) : launch_bf16_t<256, false>(a, s);
@@ -1423,7 +1472,7 @@ hipError_t launch_gemm_bf16(const GemmArgs& a, int tile, hipStream_t s) {
 
 template <int TS>
 hipError_t launch_f32_t(const GemmArgs& a, hipStream_t s) {
-    const bool sym = a.mode == GM_GRAM || a.mode == GM_GRAM2;
+    const bool sym = gemm_mode_sym(a.mode);
     const unsigned grid = (unsigned)((a.total_tiles + 7) / 8 * 8);
     if (a.src_dtype == DT_BF16) {
         if (sym) hipLaunchKernelGGL((k_gemm_f32<TS, true, bf16>), dim3(grid), dim3(NTHR), 0, s, a);
@@ -1437,6 +1486,7 @@ hipError_t launch_f32_t(const GemmArgs& a, hipStream_t s) {
 
 hipError_t launch_gemm_f32(const GemmArgs& a, int tile, hipStream_t s) {
     if (a.total_tiles <= 0) return hipSuccess;
+    if (a.mode == GM_GRAM_DUAL || a.mode == GM_APPLY_DUAL) return hipErrorInvalidValue;   // bf16 only
     if (tile == 64) return launch_f32_t<64>(a, s);
     if (tile == 128) return launch_f32_t<128>(a, s);
     return hipErrorInvalidValue;

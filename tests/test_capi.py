@@ -120,6 +120,40 @@ def test_workspace_checks(lib):
     assert _step(lib, [_mat(lib)], _hp(lib), ws=A + (9 << 24) + 16, nbytes=need.value) == lib.MU_ERR_WORKSPACE
 
 
+def test_gram_side_workspace(lib, monkeypatch):
+    """Gram-side steps (wide bf16 blocks, n > 2m, m >= 1024, three or more cubic
+    steps) add exactly four m x m buffers per block (a second B, two Q, the
+    unfolded B0) plus their descriptors and tile maps; every other block and
+    schedule plans as with MU_GRAMSIDE=0."""
+    def need(rows, cols, **kw):
+        arr = (lib.MuMatrix * 1)(_mat(lib, rows=rows, cols=cols, dtype=lib.MU_BF16))
+        n = ctypes.c_size_t(0)
+        assert lib.LIB.mu_muon_workspace_size(arr, 1, ctypes.byref(_hp(lib, **kw)), ctypes.byref(n)) == 0
+        return n.value
+
+    cases = [((1024, 4096), {}, True), ((4096, 1024), {}, True), ((1000, 2600), {}, True),
+             ((1024, 4096), dict(ns_steps=3), True), ((1024, 1024), {}, False), ((512, 4096), {}, False),
+             ((1024, 2048), {}, False), ((1024, 4096), dict(ns_steps=2), False),
+             ((1024, 4096), dict(ns_precision=lib.MU_NS_F32), False)]
+    for (r, c), kw, gains in cases:
+        monkeypatch.delenv("MU_GRAMSIDE", raising=False)
+        on = need(r, c, **kw)
+        monkeypatch.setenv("MU_GRAMSIDE", "0")
+        off = need(r, c, **kw)
+        mp = 1024
+        extra = 4 * mp * mp * 2
+        if gains:
+            assert extra <= on - off < extra + (64 << 10), ((r, c), kw, on - off)
+        else:
+            assert on == off, ((r, c), kw)
+    # quintic steps: no Gram-side steps
+    co = (ctypes.c_float * 15)(*([1.875, -1.25, 0.375] * 5))
+    monkeypatch.delenv("MU_GRAMSIDE", raising=False)
+    on = need(1024, 4096, coeffs=co)
+    monkeypatch.setenv("MU_GRAMSIDE", "0")
+    assert need(1024, 4096, coeffs=co) == on
+
+
 def test_empty_list_is_ok_without_device(lib):
     arr = (lib.MuMatrix * 1)()
     assert lib.LIB.mu_muon_step(arr, 0, ctypes.byref(_hp(lib)), None, 0, None) == 0

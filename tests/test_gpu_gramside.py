@@ -1,0 +1,128 @@
+"""Gram-side Newton-Schulz steps on the GPU against the CPU oracle.
+
+Wide blocks (n > 2m, m >= 1024, bf16, cubic steps) run their first steps on
+the m x m side: A_{k+1} = B_k (B_k A_k), Q_{k+1} = B_k Q_k, then X_R = Q_R X_0
+and the remaining steps as usual. In exact arithmetic that is the iteration
+of the MuonClip Optimizer page ("Newton-Schulz Orthogonalization"), so the
+oracle is the plain iteration and the bar is the bf16 tolerance. The same
+inputs with MU_GRAMSIDE=0 (every step on X) meet the same bar.
+"""
+
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import check_w_against_oracle, make_matrix_inputs, need_gpu, tile_rel_fro, to_np
+from oracle import muon_oracle as O
+from workloads import as_dtype, host_normal
+
+pytestmark = pytest.mark.gpu
+
+BF16_TOL = 2e-2
+MOM_TOL = 1e-6
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    need_gpu()
+    yield
+    os.environ.pop("MU_GRAMSIDE", None)
+
+
+def nso():
+    import newton_schulz_orthogonalized_amd as m
+    return m
+
+
+def _ortho_check(x, steps=5, coeffs=None, heads=1, label=""):
+    out, = nso().orthogonalize([x.cuda()], heads=[heads], ns_steps=steps, coeffs=coeffs, precision="bf16")
+    torch.cuda.synchronize()
+    ref, _ = O.orthogonalize_ref(to_np(x), heads=heads, coeffs=coeffs if coeffs is not None else
+                                 O.default_coeffs(steps))
+    o = to_np(out)
+    err, terr = O.rel_fro(o, ref), tile_rel_fro(o, ref)
+    print(f"[gram-side] {label} shape={tuple(x.shape)} steps={steps} heads={heads} "
+          f"relF={err:.3e} worst tile={terr:.3e}", flush=True)
+    assert np.isfinite(o).all()
+    assert err <= BF16_TOL
+    assert terr <= BF16_TOL
+    return err
+
+
+@pytest.mark.parametrize("shape", [(1024, 4096), (4096, 1024), (1000, 2600), (2600, 1000)])
+def test_five_steps(shape):
+    x = as_dtype(host_normal(shape, 31000 + shape[0]), torch.bfloat16)
+    _ortho_check(x, 5, label="gaussian")
+
+
+@pytest.mark.parametrize("steps", [3, 4, 7])
+def test_restart_positions(steps):
+    """Restart after 2, 3 and 4 Gram-side steps (3, 4 and 7 steps in all)."""
+    x = as_dtype(host_normal((1000, 2600), 31100 + steps), torch.bfloat16)
+    _ortho_check(x, steps, label="ragged")
+
+
+def test_per_step_coefficients():
+    """Each step's own (a, b): B_{k+1} is formed with step k+1's pair in the dual
+    apply's epilogue, so an off-by-one there fails against the oracle."""
+    co = [(1.5 + 0.06 * k, -0.5 - 0.03 * k, 0.0) for k in range(6)]
+    x = as_dtype(host_normal((1024, 3000), 31200), torch.bfloat16)
+    _ortho_check(x, 6, coeffs=co, label="per-step coefficients")
+
+
+def test_heads():
+    x = as_dtype(host_normal((2048, 4096), 31300), torch.bfloat16)
+    _ortho_check(x, 5, heads=2, label="two heads")
+
+
+def test_rank_one_dominated():
+    m, n = 1024, 4096
+    u, v = host_normal(m, 31400), host_normal(n, 31401)
+    x = as_dtype(np.outer(u, v) + 0.01 * host_normal((m, n), 31402), torch.bfloat16)
+    _ortho_check(x, 5, label="rank-1 + 1 % noise")
+
+
+def test_muon_step_mixed_list_on_and_off():
+    """One Muon call over Gram-side blocks and plain ones (square, short, tall),
+    with and without Gram-side steps: both against the oracle's O, M and W."""
+    shapes = [(1024, 4096), (1024, 1024), (4096, 1024), (256, 1024), (1000, 2600)]
+    results = {}
+    for mode in ("on", "off"):
+        if mode == "off":
+            os.environ["MU_GRAMSIDE"] = "0"
+        ws, gs, ms, oo, keep = [], [], [], [], []
+        for i, sh in enumerate(shapes):
+            w, g, m = make_matrix_inputs(sh, 31500 + 10 * i, torch.bfloat16, 1e-3, 0.02, 1e-3)
+            keep.append((to_np(w), to_np(g), to_np(m)))
+            ws.append(w); gs.append(g); ms.append(m)
+            oo.append(torch.zeros(sh, dtype=torch.float32, device="cuda"))
+        nso().muon_step(ws, gs, ms, lr=0.02, weight_decay=0.01, ortho_outs=oo)
+        torch.cuda.synchronize()
+        results[mode] = [to_np(o) for o in oo]
+        for i, sh in enumerate(shapes):
+            w0, g0, m0 = keep[i]
+            ref = O.muon_step_ref(w0, g0, m0, lr=0.02, weight_decay=0.01)
+            o = results[mode][i]
+            err = O.rel_fro(o, ref["o"])
+            print(f"[gram-side step {mode}] {sh}: O relF {err:.3e}", flush=True)
+            assert err <= BF16_TOL
+            assert tile_rel_fro(o, ref["o"]) <= BF16_TOL
+            assert O.rel_fro(to_np(ms[i]), ref["m"]) <= MOM_TOL
+            check_w_against_oracle(to_np(ws[i]), w0, o, ref["w"], ref["o"], 0.02)
+    # blocks that never take Gram-side steps run the same kernels either way
+    for i in (1, 3):
+        assert np.array_equal(results["on"][i], results["off"][i]), shapes[i]
+
+
+def test_repeated_calls_replay_bit_for_bit():
+    """The second call of a structure replays the captured launch sequence
+    (all Gram-side launches included): bit for bit the first call's result."""
+    x = as_dtype(host_normal((1024, 4096), 31600), torch.bfloat16).cuda()
+    outs = []
+    for _ in range(3):
+        out, = nso().orthogonalize([x], precision="bf16")
+        torch.cuda.synchronize()
+        outs.append(out.clone())
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[1], outs[2])
