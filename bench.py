@@ -370,6 +370,11 @@ def main():
     ns_flops = sum(prof[k]["flops"] for k in ns_kinds) / K
     peak = PEAK_BF16_TFLOPS if precision == "bf16" else PEAK_F32_TFLOPS
     ns_tflops = ns_flops / (ns_ms * 1e-3) / 1e12 if ns_ms > 0 else 0.0
+    # the plain iteration's flops (every step a Gram and an apply on X); the
+    # library's Gram-side steps reach the same result with fewer, so this
+    # rate is the method's work retired per second, not a kernel's rate
+    method_flops = ps.ns_flops(args.ns_steps, sum(1 for c in coeffs if c[2] != 0.0))
+    ns_method_tflops = method_flops / (ns_ms * 1e-3) / 1e12 if ns_ms > 0 else 0.0
     adamw_gbs = prof["adamw"]["bytes"] / (prof["adamw"]["ms"] * 1e-3) / 1e9 if prof["adamw"]["ms"] > 0 else None
     prep_gbs = prof["prep"]["bytes"] / (prof["prep"]["ms"] * 1e-3) / 1e9 if prof["prep"]["ms"] > 0 else None
     kernels = {k: {"ms_per_launch": (v["ms"] / v["launches"]) if v["launches"] else None,
@@ -409,6 +414,8 @@ def main():
                                                           "ns_fused")) / K,
         "adamw_ms_per_step": prof["adamw"]["ms"] / K,
         "ns_ms_per_step": ns_ms, "ns_tflops": ns_tflops, "ns_frac_peak": ns_tflops / peak,
+        "ns_flops_per_step": ns_flops, "ns_method_flops_per_step": method_flops,
+        "ns_method_tflops": ns_method_tflops,
         "adamw_gbs": adamw_gbs, "adamw_frac_hbm": (adamw_gbs / PEAK_HBM_GBS) if adamw_gbs else None,
         "prep_gbs": prep_gbs, "prep_frac_hbm": (prep_gbs / PEAK_HBM_GBS) if prep_gbs else None,
         "kernels": kernels, "roofline": roof, "source_digest": source_digest(),

@@ -118,25 +118,32 @@ struct ProbPlan {
     bool gs = false;   // Gram-side steps (see below)
     void* sq[2] = {nullptr, nullptr};   // Gram-side: the two Q buffers (mp x mp)
     void* bc = nullptr;                 // Gram-side: the second B buffer (the first is d.b)
+    void* ss = nullptr;                 // Gram-side: S_k = B_k^2
+    void* sa = nullptr;                 // Gram-side: A_k for odd k (even k: the second X buffer)
 };
 
-// Gram-side steps. For a wide block with np > 2 mp the first R cubic steps
-// run on the m x m side: with A_k = X_k X_k^T and B_k = a_k I + b_k A_k, every
-// X_k is Q_k X_0 for the polynomial Q_k = B_{k-1} .. B_0 in A_0, and
-//   A_{k+1} = B_k A_k B_k = B_k (B_k A_k),   Q_{k+1} = B_k Q_k,
-// because polynomials in A_0 commute. Step k < R - 1 then costs three m x m
-// products (T = B_k A_k, Q_{k+1}, A_{k+1} = B_k T) instead of an m x m x n
-// Gram and an m x m x n apply, and X_R = Q_R X_0 is formed once (the restart),
-// after which the remaining steps run as usual from an exactly formed X_R and
-// its own Gram. In exact arithmetic every X_k is the same matrix; in bf16 the
-// restart bounds the drift between the carried A_k and Q_k, and no later than
-// step 4, as the error of the result then stays at that of the plain steps
-// (CPU emulation of both in bf16 against float64 on Gaussian, power-law and
-// rank-one-dominated inputs). Flops per block, cubic steps S, restart R:
-// plain 3 S m^2 n; Gram-side m^2 n + (6 R - 6) m^3 + 2 m^2 n + 3 (S - R) m^2 n,
-// fewer by 3 (R - 1)(m^2 n - 2 m^3), so only blocks with n > 2m take them; and
-// only large ones (mp >= GS_MIN_M), since the extra launches of small sets
-// cost more than they save. MU_GRAMSIDE=0 turns them off.
+// Gram-side steps. For a wide block (n > m) the first R cubic steps run on
+// the m x m side: with A_k = X_k X_k^T and B_k = a_k I + b_k A_k, every X_k
+// is Q_k X_0 for the polynomial Q_k = B_{k-1} .. B_0 in A_0, and
+//   A_{k+1} = B_k A_k B_k = (B_k B_k) A_k,   Q_{k+1} = B_k Q_k,
+// because polynomials in A_0 commute. They are also symmetric, so each of
+// these products is a symmetric one computed on its upper tiles and mirrored
+// (C = P Q^T, both operands read by rows): step k < R - 1 costs three m x m
+// x m half products (S_k = B_k B_k^T, A_{k+1} = S_k A_k^T, Q_{k+1} = B_k Q_k^T)
+// instead of an m x m x n Gram and an m x m x n apply. X_R = Q_R X_0 is
+// formed once (the restart), after which the remaining steps run as usual
+// from an exactly formed X_R and its own Gram. In exact arithmetic every X_k
+// is the same matrix; in bf16 the restart bounds the drift between the
+// carried A_k and Q_k, and no later than step 4, as the error of the result
+// then stays at or below that of the plain steps (CPU emulation of both in
+// bf16 against float64 on Gaussian, power-law and rank-one-dominated inputs;
+// without a restart, rank-one-dominated inputs went past 2e-2). Flops per
+// block, cubic steps S, restart R: plain 3 S m^2 n; Gram-side
+// m^2 n + (3 R - 3) m^3 + 2 m^2 n + 3 (S - R) m^2 n, fewer by
+// 3 (R - 1)(m^2 n - m^3) for every n > m. Only large blocks (mp >= GS_MIN_M)
+// take them: the extra launches cost small sets more than they save
+// (GPT-2-shaped set with m = 768 included: 1.366 -> 1.459 ms per step, with
+// the earlier form of these steps). MU_GRAMSIDE=0 turns them off.
 constexpr int GS_MIN_M = 1024;
 constexpr int GS_MAX_RESTART = 4;
 bool gramside_enabled() {
@@ -305,7 +312,7 @@ void build_plan(const std::vector<Item>& items, int ns_dt, const std::vector<Coe
     // Gram-side blocks: bf16, every step cubic, 256 tiles, wide enough to gain
     pl.gs_R = (ns_dt == DT_BF16 && !pl.quintic && gramside_enabled()) ? gs_restart(co.size()) : 0;
     for (auto& pp : all)
-        pp.gs = pl.gs_R > 0 && pp.tile == 256 && pp.d.mp >= GS_MIN_M && pp.d.np > 2 * pp.d.mp;
+        pp.gs = pl.gs_R > 0 && pp.tile == 256 && pp.d.mp >= GS_MIN_M && pp.d.np > pp.d.mp;
     pl.probs.clear();
     pl.groups.clear();
     pl.n_aux = 0;
@@ -346,15 +353,15 @@ void build_plan(const std::vector<Item>& items, int ns_dt, const std::vector<Coe
         if (gs) {
             g.sq_prefix.assign(1, 0);
             g.sq2_prefix.assign(1, 0);
-            for (int i = 0; i < g.count; ++i) {
-                const int T = pl.probs[g.first + i].d.mp / t;
-                g.sq_prefix.push_back(g.sq_prefix.back() + T * T);
-                g.sq2_prefix.push_back(g.sq2_prefix.back() + T * T);
-                g.sq2_prefix.push_back(g.sq2_prefix.back() + T * T);
+            for (int i = 0; i < g.count; ++i) {   // upper tiles of mp x mp products
+                const int T = pl.probs[g.first + i].d.mp / t, U = T * (T + 1) / 2;
+                g.sq_prefix.push_back(g.sq_prefix.back() + U);
+                g.sq2_prefix.push_back(g.sq2_prefix.back() + U);
+                g.sq2_prefix.push_back(g.sq2_prefix.back() + U);
             }
             // descriptor lists, in launch order (indices past the problems'
-            // own descriptors; filled in by carve): T_0, D_0, then T_k with
-            // Q_{k+1} and D_k for k = 1 .. R-2, then Q_R and the restart
+            // own descriptors; filled in by carve): S_0, A_1, then S_k with
+            // Q_{k+1} and A_{k+1} for k = 1 .. R-2, then Q_R and the restart
             const int R = pl.gs_R;
             auto list = [&](int per) {
                 g.aux_lists.push_back(pl.n_aux);
@@ -429,10 +436,10 @@ void build_plan(const std::vector<Item>& items, int ns_dt, const std::vector<Coe
     o = align_up(o + sizeof(int) * 8 * (size_t)pl.n_gemm);
     pl.off_bufs = o;
     // per problem: X ping-pong (and X^T), a (and b for quintic steps); a
-    // Gram-side problem adds b, two Q buffers and a second B buffer (A_k and
-    // T_k live in its second X buffer, which is free until the restart)
+    // Gram-side problem adds b, a second B buffer, two Q buffers, S and one A
+    // buffer (the other A_k live in its second X buffer, free until the restart)
     for (auto& pp : pl.probs)
-        o += (pp.d.xt_used ? 4 : 2) * pp.x_bytes + pp.a_bytes * (pl.quintic ? 2 : pp.gs ? 5 : 1);
+        o += (pp.d.xt_used ? 4 : 2) * pp.x_bytes + pp.a_bytes * (pl.quintic ? 2 : pp.gs ? 7 : 1);
     pl.total = o;
 }
 
@@ -485,6 +492,10 @@ void carve(Plan& pl, char* ws, std::vector<char>& host_table) {
             }
             pl.probs[i].bc = ws + o;
             o += pl.probs[i].a_bytes;
+            pl.probs[i].ss = ws + o;
+            o += pl.probs[i].a_bytes;
+            pl.probs[i].sa = ws + o;
+            o += pl.probs[i].a_bytes;
         }
         d.partials = partials + part;
         part += d.nparts;
@@ -494,9 +505,9 @@ void carve(Plan& pl, char* ws, std::vector<char>& host_table) {
     host_table.assign(pl.table_bytes, 0);
     char* h = host_table.data();
     for (size_t i = 0; i < pl.probs.size(); ++i) std::memcpy(h + pl.off_table + i * sizeof(NsProb), &pl.probs[i].d, sizeof(NsProb));
-    // Gram-side descriptors: an mp x mp product C = L R (L read as `a`, R as
-    // x[0], C written to x[1], the dual apply's B' to b), or the restart
-    // X_R = Q_R X_0 over the block's own X buffers
+    // Gram-side descriptors: a symmetric mp x mp product C = P Q^T (P read as
+    // x[0], Q as x[1], C written to a, B' = a I + b C to b where set), or the
+    // restart X_R = Q_R X_0 over the block's own X buffers
     for (const Group& g : pl.groups) {
         if (!g.gs) continue;
         const int R = pl.gs_R;
@@ -506,32 +517,32 @@ void carve(Plan& pl, char* ws, std::vector<char>& host_table) {
             for (int i = 0; i < g.count; ++i)
                 for (int j = 0; j < per; ++j) dst[per * i + j] = make(pl.probs[g.first + i], j);
         };
-        auto sqd = [](const NsProb& d, void* l, void* r, void* out, void* bout) {
-            NsProb q = d;
-            q.np = d.mp;
-            q.a = l;
-            q.b = bout;
-            q.x[0] = r;
-            q.x[1] = out;
-            q.xt[0] = q.xt[1] = nullptr;
-            return q;
+        auto pr = [](const NsProb& d, void* p, void* q, void* c, void* bout) {
+            NsProb e = d;
+            e.np = d.mp;
+            e.x[0] = p;
+            e.x[1] = q;
+            e.a = c;
+            e.b = bout;
+            e.xt[0] = e.xt[1] = nullptr;
+            return e;
         };
-        // per problem: A_k in x[1], T_k after it; B_k alternating between b
-        // and bc; Q_1 = f B_0 is the first Gram's `a`, Q_{k+1} goes to sq[(k+1) % 2]
-        auto A_of = [](const ProbPlan& pp) { return pp.d.x[1]; };
-        auto T_of = [](const ProbPlan& pp) { return (void*)((char*)pp.d.x[1] + pp.a_bytes); };
+        // per problem: A_k in the second X buffer (even k) or sa (odd k); B_k
+        // in b (even k) or bc (odd k); Q_1 = f B_0 is the first Gram's `a`,
+        // Q_k (k >= 2) in sq[k % 2]; S_k in ss
+        auto A_of = [](const ProbPlan& pp, int k) { return (k & 1) ? pp.sa : pp.d.x[1]; };
         auto B_of = [](const ProbPlan& pp, int k) { return (k & 1) ? pp.bc : pp.d.b; };
         auto Q_of = [](const ProbPlan& pp, int k) { return k == 1 ? pp.d.a : pp.sq[k & 1]; };
-        put_list(1, [&](const ProbPlan& pp, int) { return sqd(pp.d, B_of(pp, 0), A_of(pp), T_of(pp), nullptr); });
-        put_list(1, [&](const ProbPlan& pp, int) { return sqd(pp.d, B_of(pp, 0), T_of(pp), A_of(pp), B_of(pp, 1)); });
-        for (int k = 1; k <= R - 2; ++k) {
-            put_list(2, [&](const ProbPlan& pp, int j) {
-                return j == 0 ? sqd(pp.d, B_of(pp, k), A_of(pp), T_of(pp), nullptr)
-                              : sqd(pp.d, B_of(pp, k), Q_of(pp, k), Q_of(pp, k + 1), nullptr);
+        for (int k = 0; k <= R - 2; ++k) {
+            put_list(k == 0 ? 1 : 2, [&](const ProbPlan& pp, int j) {
+                return j == 0 ? pr(pp.d, B_of(pp, k), B_of(pp, k), pp.ss, nullptr)
+                              : pr(pp.d, B_of(pp, k), Q_of(pp, k), Q_of(pp, k + 1), nullptr);
             });
-            put_list(1, [&](const ProbPlan& pp, int) { return sqd(pp.d, B_of(pp, k), T_of(pp), A_of(pp), B_of(pp, k + 1)); });
+            put_list(1, [&](const ProbPlan& pp, int) {
+                return pr(pp.d, pp.ss, A_of(pp, k), A_of(pp, k + 1), B_of(pp, k + 1));
+            });
         }
-        put_list(1, [&](const ProbPlan& pp, int) { return sqd(pp.d, B_of(pp, R - 1), Q_of(pp, R - 1), Q_of(pp, R), nullptr); });
+        put_list(1, [&](const ProbPlan& pp, int) { return pr(pp.d, B_of(pp, R - 1), Q_of(pp, R - 1), Q_of(pp, R), nullptr); });
         put_list(1, [&](const ProbPlan& pp, int) {
             NsProb q = pp.d;
             q.a = Q_of(pp, R);
@@ -845,8 +856,8 @@ int launch_sequence(const Plan& pl, char* ws, const mu_muon_hparams* hp, int src
                 sg.sym = sym;
                 ta.total += sym ? g.gram_prefix.back() : g.apply_prefix.back();
             }
-            // Gram-side groups: one and two mp x mp products per problem,
-            // in table order (the shapes of every such list)
+            // Gram-side groups: the upper tiles of one and of two mp x mp
+            // products per problem, in table order (the shapes of every such list)
             for (int two = 0; g.gs && two <= (pl.gs_R >= 3 ? 1 : 0); ++two) {
                 if (ta.nseg >= TILEMAP_SEGS) return fail(MU_ERR_INVALID_ARG, "too many tile groups");
                 TileMapSeg& sg = ta.seg[ta.nseg++];
@@ -857,7 +868,7 @@ int launch_sequence(const Plan& pl, char* ws, const mu_muon_hparams* hp, int src
                 sg.nprobs = two ? 2 * g.count : g.count;
                 sg.start = ta.total;
                 sg.ts = g.tile;
-                sg.sym = 0;
+                sg.sym = 1;
                 ta.total += two ? g.sq2_prefix.back() : g.sq_prefix.back();
             }
         }
@@ -993,7 +1004,7 @@ int launch_sequence(const Plan& pl, char* ws, const mu_muon_hparams* hp, int src
         for (int i = g.first; i < g.first + g.count; ++i) {
             const double m = pl.probs[i].d.m, n = pl.probs[i].d.n;
             fg += m * (m + 1) * n;
-            fsq += 2 * m * m * m;
+            fsq += m * (m + 1) * m;
             fap += 2 * m * m * n + 3 * m * n;
             frs += 2 * m * m * n;
             bsq += 2 * m * m * ns_es;
@@ -1030,20 +1041,22 @@ int launch_sequence(const Plan& pl, char* ws, const mu_muon_hparams* hp, int src
             a.cb = co[k].b;
             a.tmap = (const TileEntry*)(ws + (two ? g.sq2_tmap : g.sq_tmap));
             a.total_tiles = two ? g.sq2_prefix.back() : g.sq_prefix.back();
+            a.xcd_window = a.total_tiles < 4 * MI355X_CUS ? GW_SMALL : GW_MID;   // K = mp: short
             return a;
         };
         rc = go(gram(GM_GRAM_DUAL, 0, 1, 0), MU_K_GRAM, fg, 0.0, "gram launch");
         if (rc) return rc;
+        // the m x m products are timed as the A A^T pass's class (gram2)
         int li = 0;
         for (int k = 0; k <= R - 2; ++k) {
-            const bool two = k >= 1;   // T_k, and Q_{k+1} from k = 1 on (Q_1 is the first Gram's B)
-            rc = go(sq(GM_APPLY, li++, two, k), MU_K_APPLY, two ? 2 * fsq : fsq, two ? 2 * bsq : bsq, "apply launch");
+            const bool two = k >= 1;   // S_k, and Q_{k+1} from k = 1 on (Q_1 is the first Gram's B)
+            rc = go(sq(GM_GRAM_PAIR, li++, two, k), MU_K_GRAM2, two ? 2 * fsq : fsq, two ? 2 * bsq : bsq, "gram2 launch");
             if (rc) return rc;
-            // A_{k+1} = B_k T_k, and B_{k+1} with step k+1's coefficients
-            rc = go(sq(GM_APPLY_DUAL, li++, false, k + 1), MU_K_APPLY, fsq, 1.5 * bsq, "apply launch");
+            // A_{k+1} = S_k A_k, and B_{k+1} with step k+1's coefficients
+            rc = go(sq(GM_GRAM_PAIR, li++, false, k + 1), MU_K_GRAM2, fsq, 1.5 * bsq, "gram2 launch");
             if (rc) return rc;
         }
-        rc = go(sq(GM_APPLY, li++, false, R - 1), MU_K_APPLY, fsq, bsq, "apply launch");   // Q_R
+        rc = go(sq(GM_GRAM_PAIR, li++, false, R - 1), MU_K_GRAM2, fsq, bsq, "gram2 launch");   // Q_R
         if (rc) return rc;
         {   // X_R = Q_R X_0, over the blocks' own shapes and apply tile map
             GemmArgs a = base;

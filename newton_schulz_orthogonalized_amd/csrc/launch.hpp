@@ -75,12 +75,14 @@ enum GemmMode : int {
     GM_APPLY_LAST = 3,  // as GM_APPLY, result O goes to the update or to `out`
     // Gram-side steps (see the planner): the first Gram of a wide block also
     // keeps A0 = f^2 X X^T (-> x[src^1], mp x mp) and the unfolded
-    // B0 = a I + b A0 (-> b) besides B = f B0 (-> a); and an m x m product
-    // C = B X whose epilogue also forms the next step's B' = a I + b C (-> b)
+    // B0 = a I + b A0 (-> b) besides B = f B0 (-> a); and the symmetric
+    // product C = P Q^T of two mp x mp operands (P = x[0], Q = x[1]) whose
+    // result is symmetric (both are polynomials in one symmetric matrix):
+    // upper tiles, mirrored, C -> a and, where b is set, B' = a I + b C -> b
     GM_GRAM_DUAL = 4,
-    GM_APPLY_DUAL = 5,
+    GM_GRAM_PAIR = 5,
 };
-inline bool gemm_mode_sym(int mode) { return mode == GM_GRAM || mode == GM_GRAM2 || mode == GM_GRAM_DUAL; }
+inline bool gemm_mode_sym(int mode) { return mode != GM_APPLY && mode != GM_APPLY_LAST; }
 
 // Logical tile t of a GEMM launch, resolved once per call by k_tilemap:
 // problem p (an index into GemmArgs::probs) and tile coordinates ti | tj << 16

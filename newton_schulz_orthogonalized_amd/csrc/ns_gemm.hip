@@ -278,7 +278,9 @@ __device__ __forceinline__ void wave_lds_sync() { asm volatile("" ::: "memory");
 //   dual Gram (first step of a Gram-side block): B = f (a I + b f^2 X X^T)
 //                        -> P.a, and also A0 = f^2 X X^T -> X' buffer (mp x mp),
 //                        B0 = a I + b f^2 X X^T -> P.b (all mirrored)
-//   dual apply (m x m)   C = B X -> X', and B' = a I + b C -> P.b
+//   pair product         C = P Q^T (P = x[0], Q = x[1], mp x mp, C symmetric)
+//                        -> P.a, and B' = a I + b C -> P.b where P.b is set
+//                        (both mirrored)
 // On the first step X holds U itself, and f (a X0 + b (X0 X0^T) X0) with
 // X0 = f U is exactly B U for these B. Folding a I and f into B keeps X and
 // any scaling out of the apply epilogue; padding stays zero because a padded
@@ -335,8 +337,8 @@ __device__ __forceinline__ void epilogue_mode(const GemmArgs& A, const NsProb& P
         us.cautious = gp(A.cs)->cautious != 0;
     }
     constexpr bool dual = mode == GM_GRAM_DUAL;
-    constexpr bool adual = mode == GM_APPLY_DUAL;
-    constexpr bool gram = mode == GM_GRAM || mode == GM_GRAM2 || dual;
+    constexpr bool pair = mode == GM_GRAM_PAIR;
+    constexpr bool gram = mode == GM_GRAM || mode == GM_GRAM2 || dual || pair;
     const float f = gram && A.first ? P.fold[0] : 1.f;   // the apply takes it through B
     const bool diag = gram && ti == tj;
     if (diag && wm0 > wn0) return;   // below the diagonal: written by the mirror of the quadrant above
@@ -386,13 +388,15 @@ __device__ __forceinline__ void epilogue_mode(const GemmArgs& A, const NsProb& P
     // Gram scale gs, diagonal term gd, and (A^2 pass) the factor on A
     float gs = f * f, gd = 0.f, ga = A.cb;
     if ((mode == GM_GRAM || dual) && !A.use_b) { gs = A.cb * f * f * f; gd = A.ca * f; }
+    if (pair) { gs = 1.f; gd = 0.f; }
     if (mode == GM_GRAM2) { gs = A.cc * f; gd = A.ca * f; ga = A.cb * f; }
     TX* gdst = (TX*)(mode == GM_GRAM2 ? P.b : P.a);
-    // the dual modes' extra outputs: A0 (scale f^2) and the unfolded B0
-    // (scale b f^2, diagonal a) of the dual Gram; B' = a I + b C of the dual apply
-    const float s_a0 = dual ? f * f : 0.f, s_b0 = dual ? A.cb * f * f : 0.f;
+    // the extra outputs: A0 (scale f^2) and the unfolded B0 (scale b f^2,
+    // diagonal a) of the dual Gram; B' = a I + b C of a pair product
+    const float s_a0 = dual ? f * f : 0.f, s_b0 = dual ? A.cb * f * f : pair ? A.cb : 0.f;
     TX* a0dst = dual ? (TX*)(A.src ? P.x[0] : P.x[1]) : nullptr;
-    TX* b0dst = (dual || adual) ? (TX*)P.b : nullptr;
+    TX* b0dst = (dual || pair) ? (TX*)P.b : nullptr;
+    const bool with_b0 = dual || (pair && P.b != nullptr);
     // A^2 pass: B = gd I + ga A + gs A A^T takes A over the whole block. The
     // stored A is exactly symmetric (the Gram writes both triangles from the
     // same values), so the four accumulator rows r .. r+3 of a lane's column
@@ -545,6 +549,8 @@ __device__ __forceinline__ void epilogue_mode(const GemmArgs& A, const NsProb& P
 #pragma unroll
                             for (int e = 0; e < 8; ++e) v[e] = s_a0 * w[e];
                             store8<TX>(tdst(a0dst, mp, mp, c, r0, fm, fp), v);
+                        }
+                        if ((dual || pair) && with_b0) {
 #pragma unroll
                             for (int e = 0; e < 8; ++e) v[e] = s_b0 * w[e];
                             store8<TX>(tdst(b0dst, mp, mp, c, r0, fm, fp), v);
@@ -621,11 +627,13 @@ __device__ __forceinline__ void epilogue_mode(const GemmArgs& A, const NsProb& P
                 // a diagonal wave block stores its fragments on or above the
                 // diagonal only (this lane's fragment: c8 / 16)
                 if (tri && c8 / 16 < fm) continue;
-                if constexpr (dual) {
+                if ((dual || pair) && with_b0) {
                     float u[8];
+                    if constexpr (dual) {
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) u[e] = s_a0 * v[e];
-                    store8<TX>(rdst(a0dst, mp, mp, r, c, fm, pass), u);
+                        for (int e = 0; e < 8; ++e) u[e] = s_a0 * v[e];
+                        store8<TX>(rdst(a0dst, mp, mp, r, c, fm, pass), u);
+                    }
 #pragma unroll
                     for (int e = 0; e < 8; ++e) u[e] = s_b0 * v[e];
                     if (diag) {
@@ -647,12 +655,6 @@ __device__ __forceinline__ void epilogue_mode(const GemmArgs& A, const NsProb& P
                 store8<TX>(rdst(gdst, mp, mp, r, c, fm, pass), v);
             } else {
                 if constexpr (!last) {
-                    if constexpr (adual) {   // B' = a I + b C (the block is square: np == mp)
-                        float u[8];
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) u[e] = A.cb * v[e] + (ti == tj && r == c + e ? A.ca : 0.f);
-                        store8<TX>(rdst(b0dst, mp, mp, r, c, fm, pass), u);
-                    }
                     // X' is read back only by the next step's launches:
                     // stored non-temporally (0.1 ms per launch faster on
                     // the 8B-shaped set, same box)
@@ -693,17 +695,18 @@ __device__ __forceinline__ void epilogue(const GemmArgs& A, const NsProb& P, int
 }
 // The bf16 kernel's epilogues, one kernel instance each (EPI): the Gram and
 // A^2 pass or the plain apply (0); the last apply, or for Gram kernels the
-// dual Gram (1); the dual apply (2). The modes of one instance share its code,
-// and the others' code stays out of the instances the plain steps run.
+// dual Gram (1); the pair product (Gram kernels, 2). The modes of one
+// instance share its code, and the others' code stays out of the instances
+// the plain steps run.
 template <bool SYM, int EPI, typename TX, typename TS, int F>
 __device__ __forceinline__ void epilogue_k(const GemmArgs& A, const NsProb& P, int ti, int tj, int TS_, int wm0,
                                            int wn0, f32x4 (&acc)[F][F], float* st, float* st2) {
     if constexpr (SYM && EPI == 1) epilogue_mode<GM_GRAM_DUAL, TX, TS, F>(A, P, ti, tj, TS_, wm0, wn0, acc, st, st2);
+    else if constexpr (SYM && EPI == 2) epilogue_mode<GM_GRAM_PAIR, TX, TS, F>(A, P, ti, tj, TS_, wm0, wn0, acc, st, st2);
     else if constexpr (SYM) {
         if (A.mode == GM_GRAM) epilogue_mode<GM_GRAM, TX, TS, F>(A, P, ti, tj, TS_, wm0, wn0, acc, st, st2);
         else epilogue_mode<GM_GRAM2, TX, TS, F>(A, P, ti, tj, TS_, wm0, wn0, acc, st, st2);
     } else if constexpr (EPI == 1) epilogue_mode<GM_APPLY_LAST, TX, TS, F>(A, P, ti, tj, TS_, wm0, wn0, acc, st, st2);
-    else if constexpr (EPI == 2) epilogue_mode<GM_APPLY_DUAL, TX, TS, F>(A, P, ti, tj, TS_, wm0, wn0, acc, st, st2);
     else epilogue_mode<GM_APPLY, TX, TS, F>(A, P, ti, tj, TS_, wm0, wn0, acc, st, st2);
 }
 
@@ -831,6 +834,8 @@ __global__ __launch_bounds__(NTHR) void k_gemm_bf16(GemmArgs A) {
         int RP, RQ, K;
         if (mode == GM_GRAM || (EPI == 1 && SYM)) {   // Gram, dual Gram
             pm = qm = (const bf16*)(A.src ? P.x[1] : P.x[0]); RP = RQ = P.mp; K = P.np;
+        } else if (SYM && EPI == 2) {   // pair product: P = x[0], Q = x[1]
+            pm = (const bf16*)P.x[0]; qm = (const bf16*)P.x[1]; RP = RQ = P.mp; K = P.np;
         } else if (mode == GM_GRAM2) {
             pm = qm = (const bf16*)P.a; RP = RQ = P.mp; K = P.mp;
         } else {
@@ -1449,8 +1454,10 @@ hipError_t launch_bf16_t(const GemmArgs& a, hipStream_t s) {
             hipLaunchKernelGGL((k_gemm_bf16<TS, false, bf16, 1>), dim3(grid), dim3(NTHR), 0, s, a);
         else
             hipLaunchKernelGGL((k_gemm_bf16<TS, false, float, 1>), dim3(grid), dim3(NTHR), 0, s, a);
-    } else if (a.mode == GM_GRAM_DUAL || a.mode == GM_APPLY_DUAL) {
-        hipLaunchKernelGGL((k_gemm_bf16<TS, SYM, bf16, SYM ? 1 : 2>), dim3(grid), dim3(NTHR), 0, s, a);
+    } else if (SYM && a.mode == GM_GRAM_DUAL) {
+        hipLaunchKernelGGL((k_gemm_bf16<TS, true, bf16, 1>), dim3(grid), dim3(NTHR), 0, s, a);
+    } else if (SYM && a.mode == GM_GRAM_PAIR) {
+        hipLaunchKernelGGL((k_gemm_bf16<TS, true, bf16, 2>), dim3(grid), dim3(NTHR), 0, s, a);
     } else {
         hipLaunchKernelGGL((k_gemm_bf16<TS, SYM, bf16, 0>), dim3(grid), dim3(NTHR), 0, s, a);
     }
@@ -1486,7 +1493,7 @@ hipError_t launch_f32_t(const GemmArgs& a, hipStream_t s) {
 
 hipError_t launch_gemm_f32(const GemmArgs& a, int tile, hipStream_t s) {
     if (a.total_tiles <= 0) return hipSuccess;
-    if (a.mode == GM_GRAM_DUAL || a.mode == GM_APPLY_DUAL) return hipErrorInvalidValue;   // bf16 only
+    if (a.mode == GM_GRAM_DUAL || a.mode == GM_GRAM_PAIR) return hipErrorInvalidValue;   // bf16 only
     if (tile == 64) return launch_f32_t<64>(a, s);
     if (tile == 128) return launch_f32_t<128>(a, s);
     return hipErrorInvalidValue;

@@ -1,8 +1,9 @@
 """Gram-side Newton-Schulz steps on the GPU against the CPU oracle.
 
-Wide blocks (n > 2m, m >= 1024, bf16, cubic steps) run their first steps on
-the m x m side: A_{k+1} = B_k (B_k A_k), Q_{k+1} = B_k Q_k, then X_R = Q_R X_0
-and the remaining steps as usual. In exact arithmetic that is the iteration
+Wide blocks (n > m, m >= 1024, bf16, cubic steps) run their first steps on
+the m x m side: A_{k+1} = (B_k B_k) A_k, Q_{k+1} = B_k Q_k (symmetric products
+of commuting matrices, computed on their upper tiles), then X_R = Q_R X_0 and
+the remaining steps as usual. In exact arithmetic that is the iteration
 of the MuonClip Optimizer page ("Newton-Schulz Orthogonalization"), so the
 oracle is the plain iteration and the bar is the bf16 tolerance. The same
 inputs with MU_GRAMSIDE=0 (every step on X) meet the same bar.
@@ -51,7 +52,7 @@ def _ortho_check(x, steps=5, coeffs=None, heads=1, label=""):
     return err
 
 
-@pytest.mark.parametrize("shape", [(1024, 4096), (4096, 1024), (1000, 2600), (2600, 1000)])
+@pytest.mark.parametrize("shape", [(1024, 4096), (4096, 1024), (1000, 2600), (2600, 1000), (1024, 1300)])
 def test_five_steps(shape):
     x = as_dtype(host_normal(shape, 31000 + shape[0]), torch.bfloat16)
     _ortho_check(x, 5, label="gaussian")
@@ -65,8 +66,9 @@ def test_restart_positions(steps):
 
 
 def test_per_step_coefficients():
-    """Each step's own (a, b): B_{k+1} is formed with step k+1's pair in the dual
-    apply's epilogue, so an off-by-one there fails against the oracle."""
+    """Each step's own (a, b): B_{k+1} is formed with step k+1's pair in the
+    epilogue of the product that forms A_{k+1}, so an off-by-one there fails
+    against the oracle."""
     co = [(1.5 + 0.06 * k, -0.5 - 0.03 * k, 0.0) for k in range(6)]
     x = as_dtype(host_normal((1024, 3000), 31200), torch.bfloat16)
     _ortho_check(x, 6, coeffs=co, label="per-step coefficients")
@@ -87,7 +89,7 @@ def test_rank_one_dominated():
 def test_muon_step_mixed_list_on_and_off():
     """One Muon call over Gram-side blocks and plain ones (square, short, tall),
     with and without Gram-side steps: both against the oracle's O, M and W."""
-    shapes = [(1024, 4096), (1024, 1024), (4096, 1024), (256, 1024), (1000, 2600)]
+    shapes = [(1024, 4096), (1024, 1024), (4096, 1024), (256, 1024), (1000, 2600), (2048, 1400)]
     results = {}
     for mode in ("on", "off"):
         if mode == "off":
