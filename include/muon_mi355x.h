@@ -28,6 +28,19 @@
  * which the environment variable MU_PERSIST = 0 selects (read at each call that
  * plans or captures its launches).
  *
+ * Gram-side steps: with bf16 Newton-Schulz and three or more cubic steps, a
+ * wide block (short side m >= 1024, long side n > m) runs its first steps on
+ * the m x m side. Every iterate is X_k = Q_k X_0 for a polynomial Q_k in
+ * A_0 = X_0 X_0^T, so A_{k+1} = (B_k B_k) A_k and Q_{k+1} = B_k Q_k are
+ * products of commuting symmetric matrices (computed on their upper tiles);
+ * X_R = Q_R X_0 is formed before the last step (R = min(steps - 1, 4)), which
+ * then runs as usual. This is the same iteration in exact arithmetic, with
+ * fewer flops for every n > m, and the result is rounded differently (its
+ * error against the float64 iteration stays within the bf16 tolerance). It
+ * needs six more m x m buffers per such block in the workspace (the workspace
+ * queries include them). The environment variable MU_GRAMSIDE = 0 plans every
+ * block with a Gram and an apply per step (read whenever a call or a query plans).
+ *
  * Layout rules common to every entry point:
  *   - every tensor is dense, row-major, with no padding between rows;
  *   - parameter, gradient and state buffers of one entry must not overlap each
@@ -291,7 +304,8 @@ int mu_version(void);
 #define MU_K_NORM 1      /* per-head norm finalisation */
 #define MU_K_GRAM 2      /* A = X X^T (upper tiles, mirrored); writes B = aI + bA on cubic steps */
 #define MU_K_GRAM2 3     /* A A^T for the quintic term; writes B = aI + bA + cA^2 */
-                         /* (on the first step B also carries the factor 1/||U||) */
+                         /* (on the first step B also carries the factor 1/||U||); */
+                         /* also the m x m products of Gram-side steps */
 #define MU_K_APPLY 4     /* B X (last step fuses the update) */
 #define MU_K_FINISH 5    /* update when ns_steps == 0 */
 #define MU_K_ADAMW 6     /* AdamW */

@@ -538,8 +538,10 @@ void carve(Plan& pl, char* ws, std::vector<char>& host_table) {
                 return j == 0 ? pr(pp.d, B_of(pp, k), B_of(pp, k), pp.ss, nullptr)
                               : pr(pp.d, B_of(pp, k), Q_of(pp, k), Q_of(pp, k + 1), nullptr);
             });
+            // (A_{R-1} itself is not needed: the last of these writes B_{R-1} alone)
             put_list(1, [&](const ProbPlan& pp, int) {
-                return pr(pp.d, pp.ss, A_of(pp, k), A_of(pp, k + 1), B_of(pp, k + 1));
+                return k + 1 < R - 1 ? pr(pp.d, pp.ss, A_of(pp, k), A_of(pp, k + 1), B_of(pp, k + 1))
+                                     : pr(pp.d, pp.ss, A_of(pp, k), B_of(pp, k + 1), nullptr);
             });
         }
         put_list(1, [&](const ProbPlan& pp, int) { return pr(pp.d, B_of(pp, R - 1), Q_of(pp, R - 1), Q_of(pp, R), nullptr); });
@@ -1053,7 +1055,10 @@ int launch_sequence(const Plan& pl, char* ws, const mu_muon_hparams* hp, int src
             rc = go(sq(GM_GRAM_PAIR, li++, two, k), MU_K_GRAM2, two ? 2 * fsq : fsq, two ? 2 * bsq : bsq, "gram2 launch");
             if (rc) return rc;
             // A_{k+1} = S_k A_k, and B_{k+1} with step k+1's coefficients
-            rc = go(sq(GM_GRAM_PAIR, li++, false, k + 1), MU_K_GRAM2, fsq, 1.5 * bsq, "gram2 launch");
+            // (B_{R-1} alone on the last of them)
+            GemmArgs a2 = sq(GM_GRAM_PAIR, li++, false, k + 1);
+            a2.use_b = k + 1 == R - 1 ? 1 : 0;
+            rc = go(a2, MU_K_GRAM2, fsq, 1.5 * bsq, "gram2 launch");
             if (rc) return rc;
         }
         rc = go(sq(GM_GRAM_PAIR, li++, false, R - 1), MU_K_GRAM2, fsq, bsq, "gram2 launch");   // Q_R

@@ -79,6 +79,7 @@ enum GemmMode : int {
     // product C = P Q^T of two mp x mp operands (P = x[0], Q = x[1]) whose
     // result is symmetric (both are polynomials in one symmetric matrix):
     // upper tiles, mirrored, C -> a and, where b is set, B' = a I + b C -> b
+    // (with use_b: B' alone -> a)
     GM_GRAM_DUAL = 4,
     GM_GRAM_PAIR = 5,
 };

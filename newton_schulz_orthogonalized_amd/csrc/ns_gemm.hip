@@ -280,7 +280,7 @@ __device__ __forceinline__ void wave_lds_sync() { asm volatile("" ::: "memory");
 //                        B0 = a I + b f^2 X X^T -> P.b (all mirrored)
 //   pair product         C = P Q^T (P = x[0], Q = x[1], mp x mp, C symmetric)
 //                        -> P.a, and B' = a I + b C -> P.b where P.b is set
-//                        (both mirrored)
+//                        (both mirrored); with use_b only B' -> P.a
 // On the first step X holds U itself, and f (a X0 + b (X0 X0^T) X0) with
 // X0 = f U is exactly B U for these B. Folding a I and f into B keeps X and
 // any scaling out of the apply epilogue; padding stays zero because a padded
@@ -388,7 +388,7 @@ __device__ __forceinline__ void epilogue_mode(const GemmArgs& A, const NsProb& P
     // Gram scale gs, diagonal term gd, and (A^2 pass) the factor on A
     float gs = f * f, gd = 0.f, ga = A.cb;
     if ((mode == GM_GRAM || dual) && !A.use_b) { gs = A.cb * f * f * f; gd = A.ca * f; }
-    if (pair) { gs = 1.f; gd = 0.f; }
+    if (pair) { gs = A.use_b ? A.cb : 1.f; gd = A.use_b ? A.ca : 0.f; }   // use_b: B' alone, to a
     if (mode == GM_GRAM2) { gs = A.cc * f; gd = A.ca * f; ga = A.cb * f; }
     TX* gdst = (TX*)(mode == GM_GRAM2 ? P.b : P.a);
     // the extra outputs: A0 (scale f^2) and the unfolded B0 (scale b f^2,
@@ -396,7 +396,7 @@ __device__ __forceinline__ void epilogue_mode(const GemmArgs& A, const NsProb& P
     const float s_a0 = dual ? f * f : 0.f, s_b0 = dual ? A.cb * f * f : pair ? A.cb : 0.f;
     TX* a0dst = dual ? (TX*)(A.src ? P.x[0] : P.x[1]) : nullptr;
     TX* b0dst = (dual || pair) ? (TX*)P.b : nullptr;
-    const bool with_b0 = dual || (pair && P.b != nullptr);
+    const bool with_b0 = dual || (pair && !A.use_b && P.b != nullptr);
     // A^2 pass: B = gd I + ga A + gs A A^T takes A over the whole block. The
     // stored A is exactly symmetric (the Gram writes both triangles from the
     // same values), so the four accumulator rows r .. r+3 of a lane's column
