@@ -1,5 +1,5 @@
 """mu_muon_step_noalloc (the entry point for callers that cannot allocate)
-against mu_muon_step, through the C ABI: three calls in a row on one GPU, each
+against mu_muon_step, through the C ABI: four calls in a row on one GPU, each
 smaller than the one before, each compared bit for bit with mu_muon_step on
 clones of the same inputs (same kernels, so the results must be identical),
 and one matrix of each call against the oracle. The scratch array keeps the
@@ -27,6 +27,7 @@ def _gpu():
 # (shape, heads) lists, largest first; dtype and Newton-Schulz precision
 CALLS = [
     ([((32768, 256), 256), ((768, 2304), 1)], torch.bfloat16, "bf16"),   # fused short blocks + a tiled matrix
+    ([((1024, 2048), 1)], torch.bfloat16, "bf16"),                         # Gram-side steps
     ([((768, 768), 1), ((2304, 768), 1), ((300, 77), 1)], torch.bfloat16, "bf16"),
     ([((128, 256), 1)], torch.float32, "f32"),
 ]
