@@ -42,7 +42,7 @@ def nso():
 
 
 CASES = [(1e-25, 0.0), (1e-25, 1e-7), (1e18, 1e-7), (1e18, 0.0), (1e-33, 0.0)]
-SHAPES = [(300, 520), (520, 300), (768, 2304)]
+SHAPES = [(300, 520), (520, 300), (768, 2304), (1024, 2048)]   # the last takes Gram-side steps in bf16
 
 
 @pytest.mark.parametrize("scale,eps", CASES)

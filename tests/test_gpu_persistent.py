@@ -102,3 +102,40 @@ def test_persistent_128_tiles_match_one_workgroup_per_tile(monkeypatch):
     for i in range(len(shapes)):
         assert torch.equal(o_pers[i], o_tile[i]), i
         assert torch.equal(w_pers[i], w_tile[i]), i
+
+
+def test_persistent_gram_side_launches_match_one_workgroup_per_tile(monkeypatch):
+    """Gram-side blocks in persistent launches: 16 blocks of 4096 x 8192 (eight
+    wide, eight tall) give 16 x 136 = 2176 upper tiles per m x m product set and
+    per first Gram, and 8192 restart tiles, all above 8 x 256 slots."""
+    import newton_schulz_orthogonalized_amd as nso
+    from newton_schulz_orthogonalized_amd import _lib as L
+    props = torch.cuda.get_device_properties(0)
+    shapes = [(4096, 8192) if i % 2 else (8192, 4096) for i in range(16)]
+    if 16 * 136 < 8 * props.multi_processor_count:
+        pytest.skip("fewer tiles than the persistent threshold on this device")
+    print("[persistent] 16 x (4096, 8192) / (8192, 4096), Gram-side steps", flush=True)
+    ins = [make_matrix_inputs(sh, 47000 + i, torch.bfloat16, 1e-3, 0.02, 1e-3) for i, sh in enumerate(shapes)]
+    w0 = [w.clone() for w, _, _ in ins]
+    m0 = [m.clone() for _, _, m in ins]
+    oo = [torch.zeros(sh, dtype=torch.float32, device="cuda") for sh in shapes]
+
+    def run(persist):
+        monkeypatch.setenv("MU_PERSIST", "1" if persist else "0")
+        for (w, _, m), a, b in zip(ins, w0, m0):
+            w.copy_(a)
+            m.copy_(b)
+        L.mu_profile_enable(True)
+        try:
+            nso.muon_step([x[0] for x in ins], [x[1] for x in ins], [x[2] for x in ins], lr=0.02,
+                          weight_decay=0.01, ortho_outs=oo)
+            torch.cuda.synchronize()
+        finally:
+            L.mu_profile_enable(False)
+        return [w.clone() for w, _, _ in ins], [o.clone() for o in oo]
+
+    w_tile, o_tile = run(False)
+    w_pers, o_pers = run(True)
+    for i in range(len(shapes)):
+        assert torch.equal(o_pers[i], o_tile[i]), i
+        assert torch.equal(w_pers[i], w_tile[i]), i
