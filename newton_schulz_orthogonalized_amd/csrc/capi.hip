@@ -188,7 +188,7 @@ struct Group {
 // Llama-3-8B-shaped 21.56 -> 20.61, Llama-1B-shaped 2.00 -> 1.92 (windows of
 // 8; the contiguous split on the sorted order: 3.76), GPT-2-small-shaped
 // 0.101 -> 0.081 (windows of 4; of 8: 0.094).
-constexpr int GW_SMALL = 4, GW_MID = 8;
+constexpr int GW_SMALL = 4, GW_MID = 8, GW_SQ = 32;
 constexpr int MI355X_CUS = 256;   // compute units of the one chip this library targets
 int gram_window_for(const std::vector<ProbPlan>& probs, int first, int count, int tiles) {
     double all = 0, long_k = 0;
@@ -1043,7 +1043,9 @@ int launch_sequence(const Plan& pl, char* ws, const mu_muon_hparams* hp, int src
             a.cb = co[k].b;
             a.tmap = (const TileEntry*)(ws + (two ? g.sq2_tmap : g.sq_tmap));
             a.total_tiles = two ? g.sq2_prefix.back() : g.sq_prefix.back();
-            a.xcd_window = a.total_tiles < 4 * MI355X_CUS ? GW_SMALL : GW_MID;   // K = mp: short
+            // windows of 32 tiles per XCD (same process, 8B-shaped set, ms per
+            // m x m launch: 8 -> 6.99, 16 -> 6.86, 32 -> 6.84, 64 -> 6.89)
+            a.xcd_window = a.total_tiles < 4 * MI355X_CUS ? GW_SMALL : GW_SQ;
             return a;
         };
         rc = go(gram(GM_GRAM_DUAL, 0, 1, 0), MU_K_GRAM, fg, 0.0, "gram launch");
