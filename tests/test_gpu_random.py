@@ -45,11 +45,15 @@ def _draw(seed):
     return specs
 
 
+# seed 5 adds wide and tall blocks that take Gram-side steps (m >= 1024, n > m)
+GRAM_SIDE = [((1024, 1536), 1), ((1536, 1024), 1), ((1000, 1500), 1)]
+
+
 @pytest.mark.parametrize("seed,prec,sched", [(0, "bf16", 0), (1, "f32", 0), (2, "bf16", 1), (3, "f32", 2),
-                                             (4, "bf16", 2)])
+                                             (4, "bf16", 2), (5, "bf16", 0)])
 def test_random_list(seed, prec, sched):
     import newton_schulz_orthogonalized_amd as nso
-    specs = _draw(1000 + seed)
+    specs = _draw(1000 + seed) + (GRAM_SIDE if seed == 5 else [])
     coeffs = SCHEDULES[sched]
     print(f"[random list] seed={seed} prec={prec} schedule={sched} specs={specs}", flush=True)
     dt = torch.bfloat16 if prec == "bf16" else torch.float32
