@@ -9,6 +9,14 @@
 // in the Gram epilogue (cubic steps) or in an A A^T pass (quintic steps), so
 // the apply is a plain product.
 //
+// Wide blocks with Gram-side steps (planned in capi.hip) run their first steps
+// as m x m products instead: every iterate is X_k = Q_k X_0 with Q_k and
+// A_k = X_k X_k^T polynomials in A_0, so S_k = B_k B_k, A_{k+1} = S_k A_k and
+// Q_{k+1} = B_k Q_k are products of commuting symmetric matrices. They run on
+// the Gram kernel with two operands (the pair product: upper tiles, mirrored),
+// after a first Gram that also keeps A_0 and the unfolded B_0 (the dual Gram);
+// the restart X_R = Q_R X_0 is a plain apply.
+//
 // All products are grouped GEMMs over every (matrix, head) problem of a call:
 // one launch per mode covers all problems, each workgroup reads its problem
 // and tile coordinates from the call's tile map (built once per call from the
