@@ -128,3 +128,37 @@ def test_repeated_calls_replay_bit_for_bit():
         torch.cuda.synchronize()
         outs.append(out.clone())
     assert torch.equal(outs[0], outs[1]) and torch.equal(outs[1], outs[2])
+
+
+@pytest.mark.parametrize("cautious", [False, True])
+def test_float32_parameters_scale_and_cautious_decay(cautious):
+    """Gram-side blocks with float32 parameters (bf16 Newton-Schulz), a
+    per-matrix scale of 2 and, optionally, cautious weight decay: the last
+    apply's float32 update instance after the restart. O, M and the float32
+    update W1 - W0 against the oracle."""
+    shapes = [(1024, 2048), (2048, 1024)]
+    ws, gs, ms, oo, keep = [], [], [], [], []
+    for i, sh in enumerate(shapes):
+        w, g, m = make_matrix_inputs(sh, 31700 + 10 * i, torch.float32, 1.0, 1.0, 1.0)
+        keep.append((to_np(w), to_np(g), to_np(m)))
+        ws.append(w); gs.append(g); ms.append(m)
+        oo.append(torch.zeros(sh, dtype=torch.float32, device="cuda"))
+    nso().muon_step(ws, gs, ms, lr=0.05, weight_decay=0.3, scales=[2.0, 2.0], ortho_outs=oo, precision="bf16",
+                    cautious_wd=cautious)
+    torch.cuda.synchronize()
+    for i, sh in enumerate(shapes):
+        w0, g0, m0 = keep[i]
+        ref = O.muon_step_ref(w0, g0, m0, lr=0.05, weight_decay=0.3, scale=2.0, cautious=cautious)
+        o = to_np(oo[i])
+        err = O.rel_fro(o, ref["o"])
+        print(f"[gram-side f32 params] {sh} cautious={cautious}: O relF {err:.3e}", flush=True)
+        assert err <= BF16_TOL
+        assert O.rel_fro(to_np(ms[i]), ref["m"]) <= MOM_TOL
+        # the update with the GPU's own O, element by element (cautious: the same sign rule)
+        u = 0.05 * 2.0 * o
+        decay = 0.05 * 0.3 * np.where(cautious & (w0 * u < 0), 0.0, 1.0)
+        want = w0 - decay * w0 - u
+        assert np.allclose(to_np(ws[i]), want, rtol=1e-5, atol=1e-6)
+        # and against the oracle's W: the difference is lr scale (O - O_ref) away from the decay
+        dw, dref = to_np(ws[i]) - w0, ref["w"] - w0
+        assert O.rel_fro(dw, dref) <= BF16_TOL
