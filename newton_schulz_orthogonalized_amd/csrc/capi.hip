@@ -143,7 +143,10 @@ struct ProbPlan {
 // 3 (R - 1)(m^2 n - m^3) for every n > m. Only large blocks (mp >= GS_MIN_M)
 // take them: the extra launches cost small sets more than they save
 // (GPT-2-shaped set with m = 768 included: 1.366 -> 1.459 ms per step, with
-// the earlier form of these steps). MU_GRAMSIDE=0 turns them off.
+// the earlier form of these steps), and on short blocks the rounding of the
+// m x m products weighs more (emulation, rank-one-dominated inputs: 128 x 4096
+// 1.95-2.01e-2 against 1.38-1.42e-2 for plain steps; 512 x 2048 1.27-1.42e-2
+// against 1.37-1.43e-2). MU_GRAMSIDE=0 turns them off.
 constexpr int GS_MIN_M = 1024;
 constexpr int GS_MAX_RESTART = 4;
 bool gramside_enabled() {
