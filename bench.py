@@ -63,7 +63,9 @@ def parse():
     return ap.parse_args()
 
 
-KERNEL_SOURCES = ("ns_gemm.hip", "elementwise.hip", "common.hpp", "launch.hpp")
+# the library's sources that decide what runs on the GPU: the kernels and the
+# host planner (tile groups, schedules, launch shapes)
+KERNEL_SOURCES = ("ns_gemm.hip", "elementwise.hip", "common.hpp", "launch.hpp", "capi.hip")
 # the sources each profiled kernel class is built from
 KERNEL_FILES = {"apply": ("ns_gemm.hip", "common.hpp", "launch.hpp"),
                 "gram": ("ns_gemm.hip", "common.hpp", "launch.hpp")}
