@@ -269,7 +269,8 @@ def cpu_baseline(ps, set_index, ns_steps, coeffs):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; multi-GPU runs are not supported",
+        print(json.dumps({"error": "the benchmark times one GPU: the library has no multi-GPU path "
+                                   "(each GPU would run its own share of the matrices)",
                           "n_gpus": args.gpus}))
         sys.exit(2)
     import torch
