@@ -162,3 +162,44 @@ def test_float32_parameters_scale_and_cautious_decay(cautious):
         # and against the oracle's W: the difference is lr scale (O - O_ref) away from the decay
         dw, dref = to_np(ws[i]) - w0, ref["w"] - w0
         assert O.rel_fro(dw, dref) <= BF16_TOL
+
+
+# seeds whose draws give 3, 4, 5, 6 and 7 steps (restart after 2, 3, 4, 4 and 4
+# Gram-side steps), two to four Gram-side blocks each, and heads in two of them
+@pytest.mark.parametrize("seed", [26, 1, 25, 20, 11])
+def test_random_lists_with_gram_side_blocks(seed):
+    """Seeded random lists in which most blocks take Gram-side steps (wide or
+    tall, with or without heads, ragged sides), with 3 to 7 cubic steps and
+    per-step coefficients drawn per call, so the restart falls at every
+    position it can take; plain blocks ride along. O (whole matrix and every
+    256 x 256 tile) and M against the oracle."""
+    rng = np.random.default_rng(32000 + seed)
+    sides = [256, 777, 1000, 1024, 1100, 1280, 1536, 2048, 2300, 3000]
+    specs = []
+    while len(specs) < int(rng.integers(3, 6)):
+        r, c = (int(x) for x in rng.choice(sides, 2))
+        if r * c > 2_400_000:
+            continue
+        specs.append(((r, c), 2 if r % 2 == 0 and r >= 2048 and rng.random() < 0.5 else 1))
+    steps = int(rng.integers(3, 8))
+    co = [(1.5 + 0.02 * int(rng.integers(0, 5)), -0.5 + 0.01 * int(rng.integers(0, 3)), 0.0) for _ in range(steps)]
+    nest = bool(seed % 2 == 0)
+    print(f"[gram-side random] seed={seed} steps={steps} nesterov={nest} specs={specs}", flush=True)
+    ws, gs, ms, oo, keep = [], [], [], [], []
+    for i, (sh, _) in enumerate(specs):
+        w, g, m = make_matrix_inputs(sh, 32100 + 100 * seed + 10 * i, torch.bfloat16, 1e-3, 0.02, 1e-3)
+        keep.append((to_np(w), to_np(g), to_np(m)))
+        ws.append(w); gs.append(g); ms.append(m)
+        oo.append(torch.zeros(sh, dtype=torch.float32, device="cuda"))
+    nso().muon_step(ws, gs, ms, lr=0.02, weight_decay=0.01, nesterov=nest, heads=[h for _, h in specs],
+                    ns_steps=steps, coeffs=co, ortho_outs=oo)
+    torch.cuda.synchronize()
+    for i, (sh, heads) in enumerate(specs):
+        w0, g0, m0 = keep[i]
+        ref = O.muon_step_ref(w0, g0, m0, lr=0.02, weight_decay=0.01, nesterov=nest, heads=heads, coeffs=co)
+        o = to_np(oo[i])
+        err, terr = O.rel_fro(o, ref["o"]), tile_rel_fro(o, ref["o"])
+        print(f"[gram-side random]   {sh} heads={heads}: O relF {err:.3e}, worst tile {terr:.3e}", flush=True)
+        assert np.isfinite(o).all()
+        assert err <= BF16_TOL and terr <= BF16_TOL, (sh, heads)
+        assert O.rel_fro(to_np(ms[i]), ref["m"]) <= MOM_TOL, (sh, heads)
