@@ -1657,7 +1657,7 @@ int mu_adamw_step(const mu_tensor* ts, int32_t n, const mu_adamw_hparams* hp, vo
     if (!ws) return fail(MU_ERR_WORKSPACE, "workspace is null (need %zu bytes)", need);
     if (!aligned(ws, ALIGN)) return fail(MU_ERR_WORKSPACE, "workspace must be 256-byte aligned");
     if (ws_bytes < need) return fail(MU_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, need);
-    if (prefix.back() > 0x7fffffffLL) return fail(MU_ERR_INVALID_ARG, "too many elements for one launch");
+    if (prefix.back() > 0x7ffffff8LL) return fail(MU_ERR_INVALID_ARG, "too many elements for one launch");
 
     std::vector<char> table(sizeof(AdamWDesc) * n + sizeof(int64_t) * (n + 1));
     std::memcpy(table.data(), d.data(), sizeof(AdamWDesc) * n);

@@ -402,6 +402,22 @@ __global__ __launch_bounds__(NTHR) void k_finish(FinishArgs A) {
 // prefix[i] <= c < prefix[i+1] and k = c - prefix[i]. Each thread handles two
 // groups of 8 consecutive elements (16-byte bf16 / 32-byte fp32 accesses).
 // ---------------------------------------------------------------------------
+// One AdamW element in fp32, in the order of the formula, each operation
+// rounded once: contraction into fused multiply-adds is off here, because the
+// compiler fuses differently where the gradient arrives as a bf16 scalar (a
+// float32 ulp apart in a quarter of the moments), and every path of k_adamw
+// (band tile or contiguous chunk, vector or scalar accesses) must give an
+// element the same result.
+__device__ __forceinline__ void adamw1(float& p, float g, float& m, float& v, const AdamWArgs& A, float lr,
+                                       float decay) {
+#pragma clang fp contract(off)
+    m = A.beta1 * m + (1.f - A.beta1) * g;
+    v = A.beta2 * v + (1.f - A.beta2) * g * g;
+    const float mhat = m / A.bc1;
+    const float vhat = v / A.bc2;
+    p = (p - decay * p) - lr * mhat / (sqrtf(vhat) + A.eps);
+}
+
 template <typename TP>
 __device__ inline void adamw8(const AdamWDesc& D, int64_t i0, int cnt, const AdamWArgs& A) {
     MU_GLOBAL TP* p = (MU_GLOBAL TP*)D.param + i0;
@@ -432,16 +448,9 @@ __device__ inline void adamw8(const AdamWDesc& D, int64_t i0, int cnt, const Ada
             else { pv[e] = gv[e] = mv[e] = vv[e] = 0.f; }
         }
     }
-    const float b1 = A.beta1, b2 = A.beta2, omb1 = 1.f - b1, omb2 = 1.f - b2;
-    const float decay = D.lr * D.wd;
+    const float lr = D.lr, decay = D.lr * D.wd;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        mv[e] = b1 * mv[e] + omb1 * gv[e];
-        vv[e] = b2 * vv[e] + omb2 * gv[e] * gv[e];
-        const float mhat = mv[e] / A.bc1;
-        const float vhat = vv[e] / A.bc2;
-        pv[e] = (pv[e] - decay * pv[e]) - D.lr * mhat / (sqrtf(vhat) + A.eps);
-    }
+    for (int e = 0; e < 8; ++e) adamw1(pv[e], gv[e], mv[e], vv[e], A, lr, decay);
     if (full) {
         if constexpr (sizeof(TP) == 2) {
             bf16x8 a;
@@ -472,71 +481,110 @@ __device__ inline int find_tensor(const int64_t* prefix, int n, int64_t c) {
     return lo;
 }
 
-// One AdamW element in fp32, in the order of the formula.
-__device__ __forceinline__ void adamw1(float& p, float g, float& m, float& v, const AdamWArgs& A, float lr,
-                                       float decay) {
-    m = A.beta1 * m + (1.f - A.beta1) * g;
-    v = A.beta2 * v + (1.f - A.beta2) * g * g;
-    const float mhat = m / A.bc1;
-    const float vhat = v / A.bc2;
-    p = (p - decay * p) - lr * mhat / (sqrtf(vhat) + A.eps);
-}
 
-// Whole chunk of a bf16 tensor whose buffers allow 16-byte accesses: each
-// thread owns ADAMW_CHUNK / (256 * 8) runs of 8 elements; every load of all of
-// them is issued before any arithmetic.
-__device__ __forceinline__ void adamw_chunk_bf16(const AdamWDesc& D, int64_t base, const AdamWArgs& A) {
-    constexpr int RUNS = ADAMW_CHUNK / (NTHR * 8);
-    bf16x8 pq[RUNS], gq[RUNS];
-    f32x4 mq[RUNS][2], vq[RUNS][2];
+// Chunk layout. A tensor is cut into bands of ADAMW_BAND_ROWS rows of
+// ADAMW_BAND_W elements (a band is a contiguous run of 65536 elements), and a
+// band into ADAMW_BAND_W / ADAMW_TILE_C tiles of ADAMW_BAND_ROWS x
+// ADAMW_TILE_C elements, one chunk (workgroup) each, taken column-fastest. A
+// workgroup thus streams 16 pieces of 512 elements (1 KB of a bf16 parameter,
+// 2 KB of a moment) 8 KB / 16 KB apart rather than one contiguous 8192-element
+// run, which spreads each workgroup's requests over more memory channels.
+// Measured on the 8B-shaped AdamW layout (bf16 parameter and gradient, float32
+// moments, 2^30 elements), every variant in one process, two processes:
+//   contiguous 8192-element chunks                       5.28-5.30 TB/s
+//   16 x 512 tiles, 4096-wide view (this layout)         5.80-5.82
+//   8 x 512 tiles, 8192-wide view (4096-element chunks)  5.83-5.85
+//   16 x 256 tiles, 4096-wide view                       5.73-5.76
+//   8 x 512 tiles, 4096-wide view                        5.57-5.59
+//   4 x 1024 tiles, 16384-wide view                      5.52-5.54
+//   plain 16-byte copy                                   5.62-5.63
+// The 8192-element chunk is kept: the best layout was within 0.5 % of it.
+// What is left of a tensor after its last whole band (and every chunk of a
+// tensor whose buffers do not allow vector accesses) is taken in contiguous
+// chunks of ADAMW_CHUNK elements.
+constexpr int ADAMW_BAND_ROWS = 16, ADAMW_BAND_W = 4096, ADAMW_TILE_C = 512;
+constexpr int64_t ADAMW_BAND = (int64_t)ADAMW_BAND_ROWS * ADAMW_BAND_W;
+constexpr int ADAMW_TILES_PER_BAND = ADAMW_BAND_W / ADAMW_TILE_C;
+static_assert(ADAMW_BAND_ROWS * ADAMW_TILE_C == ADAMW_CHUNK, "a band tile is one chunk");
+static_assert(ADAMW_BAND % ADAMW_CHUNK == 0, "bands end on chunk boundaries");
+
+// One band tile of a tensor whose four buffers are 16-byte aligned: each
+// thread owns 4 consecutive elements in each of ADAMW_BAND_ROWS / 2 rows, and
+// issues every load before any arithmetic.
+template <typename TP>
+__device__ __forceinline__ void adamw_band_tile(const AdamWDesc& D, int64_t q, const AdamWArgs& A) {
+    constexpr int TPR = ADAMW_TILE_C / 4;       // threads per tile row
+    constexpr int RSTEP = NTHR / TPR;           // rows between a thread's rows
+    constexpr int RUNS = ADAMW_BAND_ROWS / RSTEP;
+    static_assert(NTHR % TPR == 0 && ADAMW_BAND_ROWS % RSTEP == 0, "tile rows split evenly over the threads");
+    const int64_t band = q / ADAMW_TILES_PER_BAND;
+    const int tj = (int)(q - band * ADAMW_TILES_PER_BAND);
+    const int rr = threadIdx.x / TPR, cc = (threadIdx.x % TPR) * 4;
+    const int64_t base = band * ADAMW_BAND + (int64_t)rr * ADAMW_BAND_W + tj * ADAMW_TILE_C + cc;
+    const MU_GLOBAL TP* pp = (const MU_GLOBAL TP*)D.param;
+    const MU_GLOBAL TP* gg = (const MU_GLOBAL TP*)D.grad;
+    float pv[RUNS][4], gv[RUNS][4];
+    f32x4 mq[RUNS], vq[RUNS];
 #pragma unroll
     for (int k = 0; k < RUNS; ++k) {
-        const int64_t i0 = base + (int64_t)k * NTHR * 8 + threadIdx.x * 8;
-        pq[k] = *(const MU_GLOBAL bf16x8*)((const bf16*)D.param + i0);
-        // the gradient is read once and never written: a non-temporal load
-        // (A/B on the 8B-shaped AdamW set, same process: +0.8 to +1.2 %)
-        gq[k] = __builtin_nontemporal_load((const MU_GLOBAL bf16x8*)((const bf16*)D.grad + i0));
-        mq[k][0] = *(const MU_GLOBAL f32x4*)(D.m + i0);
-        mq[k][1] = *(const MU_GLOBAL f32x4*)(D.m + i0 + 4);
-        vq[k][0] = *(const MU_GLOBAL f32x4*)(D.v + i0);
-        vq[k][1] = *(const MU_GLOBAL f32x4*)(D.v + i0 + 4);
+        const int64_t i0 = base + (int64_t)k * RSTEP * ADAMW_BAND_W;
+        if constexpr (sizeof(TP) == 2) {
+            const bf16x4 a = *(const MU_GLOBAL bf16x4*)(pp + i0);
+            // the gradient is read once and never written: a non-temporal load
+            // (A/B on the 8B-shaped AdamW set, same process: +0.8 to +1.2 %)
+            const bf16x4 b = __builtin_nontemporal_load((const MU_GLOBAL bf16x4*)(gg + i0));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { pv[k][e] = (float)a[e]; gv[k][e] = (float)b[e]; }
+        } else {
+            const f32x4 a = *(const MU_GLOBAL f32x4*)(pp + i0);
+            const f32x4 b = __builtin_nontemporal_load((const MU_GLOBAL f32x4*)(gg + i0));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { pv[k][e] = a[e]; gv[k][e] = b[e]; }
+        }
+        mq[k] = *(const MU_GLOBAL f32x4*)(D.m + i0);
+        vq[k] = *(const MU_GLOBAL f32x4*)(D.v + i0);
     }
     const float lr = D.lr, decay = D.lr * D.wd;
 #pragma unroll
     for (int k = 0; k < RUNS; ++k) {
-        const int64_t i0 = base + (int64_t)k * NTHR * 8 + threadIdx.x * 8;
-        bf16x8 po;
+        const int64_t i0 = base + (int64_t)k * RSTEP * ADAMW_BAND_W;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            float p = (float)pq[k][e], m = mq[k][e >> 2][e & 3], v = vq[k][e >> 2][e & 3];
-            adamw1(p, (float)gq[k][e], m, v, A, lr, decay);
-            po[e] = (bf16)p;
-            mq[k][e >> 2][e & 3] = m;
-            vq[k][e >> 2][e & 3] = v;
+        for (int e = 0; e < 4; ++e) {
+            float m = mq[k][e], v = vq[k][e];
+            adamw1(pv[k][e], gv[k][e], m, v, A, lr, decay);
+            mq[k][e] = m;
+            vq[k][e] = v;
         }
-        *(MU_GLOBAL bf16x8*)((bf16*)D.param + i0) = po;
-        *(MU_GLOBAL f32x4*)(D.m + i0) = mq[k][0];
-        *(MU_GLOBAL f32x4*)(D.m + i0 + 4) = mq[k][1];
-        *(MU_GLOBAL f32x4*)(D.v + i0) = vq[k][0];
-        *(MU_GLOBAL f32x4*)(D.v + i0 + 4) = vq[k][1];
+        if constexpr (sizeof(TP) == 2) {
+            bf16x4 po;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) po[e] = (bf16)pv[k][e];
+            *(MU_GLOBAL bf16x4*)((MU_GLOBAL TP*)D.param + i0) = po;
+        } else {
+            *(MU_GLOBAL f32x4*)((MU_GLOBAL TP*)D.param + i0) = f32x4{pv[k][0], pv[k][1], pv[k][2], pv[k][3]};
+        }
+        *(MU_GLOBAL f32x4*)(D.m + i0) = mq[k];
+        *(MU_GLOBAL f32x4*)(D.v + i0) = vq[k];
     }
 }
 
-// Chunks go to workgroups in order, so at any time the XCDs stream one
-// neighbourhood of each array together. Giving each XCD a contiguous eighth
-// instead (as k_prep does) was 2.3-2.6 % slower on two boxes (5.15 -> 5.27
-// and 5.78 -> 5.93 TB/s on a 2^30-element bf16 set; a kernel with the same
-// seven streams and no arithmetic reached 5.98 TB/s on the second box).
+// Chunk c of the call: chunk q of tensor i. The grid is a multiple of 8 and
+// xcd_remap gives each XCD one contiguous run of chunks. With the band layout
+// that measured faster, and steadier, than consecutive chunks dealt
+// round-robin over the XCDs: 16 x 256 tiles 5.73-5.76 against 5.65-5.66
+// TB/s, 8 x 512 tiles in an 8192-wide view 5.83-5.85 against 5.71 and 5.31.
 __global__ __launch_bounds__(NTHR) void k_adamw(AdamWArgs A) {
-    const int64_t c = blockIdx.x;
+    const int64_t c = xcd_remap(blockIdx.x, gridDim.x);
     if (c >= A.total_chunks) return;
     const int i = __builtin_amdgcn_readfirstlane(find_tensor(A.prefix, A.n, c));
     const AdamWDesc D = A.descs[i];   // by value: held in registers, never re-read after a store
-    const int64_t base = (c - A.prefix[i]) * ADAMW_CHUNK;
-    if (D.dtype == DT_BF16 && D.vec && base + ADAMW_CHUNK <= D.numel) {
-        adamw_chunk_bf16(D, base, A);
+    const int64_t q = c - A.prefix[i];
+    if (D.vec && q < D.numel / ADAMW_BAND * (ADAMW_BAND / ADAMW_CHUNK)) {
+        if (D.dtype == DT_BF16) adamw_band_tile<bf16>(D, q, A);
+        else adamw_band_tile<float>(D, q, A);
         return;
     }
+    const int64_t base = q * ADAMW_CHUNK;
 #pragma unroll
     for (int pass = 0; pass < ADAMW_CHUNK / (NTHR * 8); ++pass) {
         const int64_t i0 = base + (int64_t)pass * NTHR * 8 + threadIdx.x * 8;
@@ -668,7 +716,7 @@ hipError_t launch_finish(const FinishArgs& a, hipStream_t s) {
 
 hipError_t launch_adamw(const AdamWArgs& a, hipStream_t s) {
     if (a.total_chunks <= 0) return hipSuccess;
-    hipLaunchKernelGGL(k_adamw, dim3((unsigned)a.total_chunks), dim3(NTHR), 0, s, a);
+    hipLaunchKernelGGL(k_adamw, dim3(grid8(a.total_chunks)), dim3(NTHR), 0, s, a);
     return hipGetLastError();
 }
 

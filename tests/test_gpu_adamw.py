@@ -10,7 +10,9 @@ from workloads import as_dtype, host_normal
 
 pytestmark = pytest.mark.gpu
 
-SIZES = [1, 7, 8, 9, 4095, 4096, 4097, 10000, 70001]
+# around the chunk (8192 elements) and the band of the tiled layout (65536
+# elements): whole bands, bands plus whole and ragged chunks
+SIZES = [1, 7, 8, 9, 4095, 4096, 4097, 10000, 65536, 70001, 131072 + 12293, 3 * 65536 + 1]
 
 
 def f32(x):
@@ -96,3 +98,38 @@ def test_adamw_rejects_step_zero():
     with pytest.raises(_lib.MuonError):
         nso.adamw_step([p], [p.clone()], [p.clone()], [p.clone()], lr=0.1, weight_decay=0.0, step=0)
     assert torch.all(p == 1)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_adamw_unaligned_views_take_the_contiguous_path(dtype):
+    """Buffers that are not 16-byte aligned (views one element into a larger
+    allocation) are taken in contiguous chunks; the same values, aligned, go
+    through the band tiles. Both must equal the oracle, and each other bit for bit."""
+    import newton_schulz_orthogonalized_amd as nso
+    n = 2 * 65536 + 8192 + 37
+    p0 = as_dtype(host_normal(n, 23001, 0.5), dtype)
+    g0 = as_dtype(host_normal(n, 23002, 1e-2), dtype)
+    m0 = as_dtype(host_normal(n, 23003, 1e-2), torch.float32)
+    v0 = as_dtype(host_normal(n, 23004, 1e-2) ** 2, torch.float32)
+    outs = []
+    for off in (0, 1):
+        bufs = [torch.zeros(n + 1, dtype=t.dtype, device="cuda") for t in (p0, g0, m0, v0)]
+        views = [b[off:off + n] for b in bufs]
+        for vw, t in zip(views, (p0, g0, m0, v0)):
+            vw.copy_(t.cuda())
+        nso.adamw_step([views[0]], [views[1]], [views[2]], [views[3]], lr=0.03, weight_decay=0.01, beta1=0.9,
+                       beta2=0.95, eps=1e-8, step=7)
+        torch.cuda.synchronize()
+        outs.append([to_np(vw) for vw in (views[0], views[2], views[3])])
+    for a, b in zip(outs[0], outs[1]):
+        assert np.array_equal(a, b)
+    ins = tuple(to_np(t) for t in (p0, g0, m0, v0))
+    pr, mr, vr = O.adamw_ref(*ins, lr=f32(0.03), weight_decay=f32(0.01), beta1=f32(0.9), beta2=f32(0.95),
+                             eps=f32(1e-8), step=7)
+    p, m, v = outs[0]
+    check_states(m, v, mr, vr, ins)
+    if dtype == torch.float32:
+        assert O.rel_fro(p - ins[0], pr - ins[0]) <= 1e-4
+    else:
+        tol = 0.5 * bf16_ulp(pr) + 8 * U32 * (np.abs(ins[0]) + np.abs(pr - ins[0]))
+        assert np.all(np.abs(p - pr) <= tol)
