@@ -1587,7 +1587,7 @@ int mu_qk_clip(const mu_qk_pair* pairs, int32_t n, float tau, void* ws, size_t w
     if (!ws) return fail(MU_ERR_WORKSPACE, "workspace is null (need %zu bytes)", need);
     if (!aligned(ws, ALIGN)) return fail(MU_ERR_WORKSPACE, "workspace must be 256-byte aligned");
     if (ws_bytes < need) return fail(MU_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, need);
-    if (prefix.back() > 0x7fffffffLL || segs.size() > 0x7fffffffu)
+    if (prefix.back() > 0x7ffffff8LL || segs.size() > 0x7fffffffu)
         return fail(MU_ERR_INVALID_ARG, "too many elements for one launch");
 
     std::vector<char> table(qk_table_bytes((int64_t)segs.size()));

@@ -86,3 +86,15 @@ def test_llama_8b_attention_layers():
         ml = np.where(rng.random(32) < 0.5, rng.uniform(101.0, 500.0, 32), rng.uniform(1.0, 100.0, 32))
         specs.append((4096, 1024, 4096, 32, 8, list(ml)))
     _run(specs, torch.bfloat16, 100.0, 5300)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_band_tiles_tails_and_unaligned_heads(dtype):
+    """Head blocks longer than one band of the tiled layout (131072 elements):
+    33 x 4099 per head, so a band plus a ragged tail, and the second head of
+    each matrix starts off 16-byte alignment (contiguous path); 36 x 4096 per
+    head, a band plus two whole chunks, aligned."""
+    print(f"[qk_clip] band tiles dtype={dtype}", flush=True)
+    specs = [(66, 33, 4099, 2, 1, [150.0, 300.0]),
+             (72, 36, 4096, 2, 1, [120.0, 90.0])]
+    _run(specs, dtype, 100.0, 5400)
