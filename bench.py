@@ -86,15 +86,25 @@ def source_digest(files=KERNEL_SOURCES) -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_from_profiles(kernel: str):
+def run_key(args) -> dict:
+    """What decides a run's launches besides the sources: the parameter set and
+    the Newton-Schulz schedule."""
+    return {"workload": args.config, "coeffs": args.coeffs, "ns_steps": args.ns_steps, "precision": args.precision,
+            "gramside": os.environ.get("MU_GRAMSIDE", "1")[:1] != "0"}
+
+
+def traffic_from_profiles(kernel: str, run: dict):
     """HBM bytes per launch from committed counter summaries, if they were taken
-    on the current sources of that kernel; else None."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_llama_8b.json")
+    on the current sources of that kernel and on a run of the same parameter set
+    and schedule; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{run['workload']}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         d = json.load(f)
     if d.get("kernel_source_digest") != source_digest(KERNEL_FILES[kernel]):
+        return None
+    if d.get("run") != run:
         return None
     return d.get("bytes_per_launch")
 
@@ -394,7 +404,7 @@ def main():
                 "frac": achieved / PEAK_HBM_GBS}
     roof["kernel"] = dom
     roof["ms_per_launch"] = d["ms"] / max(1, d["launches"])
-    roof["traffic"] = traffic_from_profiles(dom)
+    roof["traffic"] = traffic_from_profiles(dom, run_key(args))
 
     out = {
         "metric": METRIC, "value": ms_step, "unit": "ms", "n_gpus": 1, "steps": args.steps,

@@ -1,7 +1,8 @@
 """The benchmark's host-side contract, on the CPU: it refuses more than one
 GPU with a message, and the HBM-traffic figure it reports comes from the
 committed counter summary only while the apply kernel's sources are the ones
-that summary was taken on (comments and formatting aside)."""
+that summary was taken on (comments and formatting aside) and only for the
+parameter set and schedule it was taken on."""
 
 import json
 import os
@@ -51,13 +52,17 @@ def test_traffic_figure_follows_the_apply_sources(tree):
         recorded = json.load(f)
     if recorded["kernel_source_digest"] != bench.source_digest(bench.KERNEL_FILES["apply"]):
         pytest.skip("the committed traffic summary predates the current apply sources")
-    assert bench.traffic_from_profiles("apply") == pytest.approx(recorded["bytes_per_launch"])
+    run = recorded["run"]
+    assert bench.traffic_from_profiles("apply", run) == pytest.approx(recorded["bytes_per_launch"])
+    # another parameter set or schedule has other launches: no figure
+    for k, v in (("workload", "gpt2_small"), ("coeffs", "quintic"), ("ns_steps", 6), ("gramside", False)):
+        assert bench.traffic_from_profiles("apply", dict(run, **{k: v})) is None
     # a change to a file the apply kernel is built from drops the figure ...
     p = tree / "common.hpp"
     p.write_text(p.read_text() + "\nconstexpr int UNUSED_FOR_TEST = 1;\n")
-    assert bench.traffic_from_profiles("apply") is None
+    assert bench.traffic_from_profiles("apply", run) is None
     # ... a change to a file it is not built from does not
     p.write_text(p.read_text().replace("\nconstexpr int UNUSED_FOR_TEST = 1;\n", ""))
     e = tree / "elementwise.hip"
     e.write_text(e.read_text() + "\n// unrelated\nstatic int unrelated_for_test;\n")
-    assert bench.traffic_from_profiles("apply") == pytest.approx(recorded["bytes_per_launch"])
+    assert bench.traffic_from_profiles("apply", run) == pytest.approx(recorded["bytes_per_launch"])
