@@ -1192,11 +1192,13 @@ __global__ __launch_bounds__(NTHR) void k_gemm_f32(GemmArgs A) {
 // 16-byte chunk of the K-blocked copy, written to LDS straight from registers
 // with no float staging (288 KB of LDS traffic per block, against 480 KB for
 // B X with B read from LDS and X' staged as floats). The loads of block j+1
-// stay in flight through block j's whole epilogue, store and Gram: the
-// barrier after the copy waits for LDS writes only. Per-head set, same
-// process: 1.465 -> 1.399 ms per launch, results bit for bit the same. (Two
-// workgroups per compute unit, with 64-column blocks in 80 KB of LDS, ran 6 %
-// slower.)
+// are issued before block j's apply; the barrier after the copy waits for LDS
+// writes only, but the compiler drains the direct loads before the first
+// write of X'_j into the staging buffer (it cannot tell the two LDS buffers
+// apart), so the loads overlap the apply and not the store or the Gram.
+// Per-head set, same process: 1.465 -> 1.399 ms per launch, results bit for
+// bit the same. (Two workgroups per compute unit, with 64-column blocks in
+// 80 KB of LDS, ran 6 % slower.)
 // 4 waves in 2 x 2: the apply 64 x 64 of X'^T (64 AGPRs), the Gram 64 x 64 of
 // A' (64 AGPRs).
 // ---------------------------------------------------------------------------
