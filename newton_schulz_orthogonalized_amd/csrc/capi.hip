@@ -146,7 +146,11 @@ struct ProbPlan {
 // the earlier form of these steps), and on short blocks the rounding of the
 // m x m products weighs more (emulation, rank-one-dominated inputs: 128 x 4096
 // 1.95-2.01e-2 against 1.38-1.42e-2 for plain steps; 512 x 2048 1.27-1.42e-2
-// against 1.37-1.43e-2). MU_GRAMSIDE=0 turns them off.
+// against 1.37-1.43e-2). With the threshold at 768 and the symmetric form the
+// GPT-2-shaped set ran 1.465 -> 1.402 ms per step, but on the GPU a rank-one-
+// dominated 768 x 3072 block reached 1.9e-2 (worst 256 x 256 tile 2.6e-2)
+// against 1.3-1.5e-2 with plain steps, past the bf16 bound; it stays at 1024.
+// MU_GRAMSIDE=0 turns them off.
 constexpr int GS_MIN_M = 1024;
 constexpr int GS_MAX_RESTART = 4;
 bool gramside_enabled() {
