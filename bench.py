@@ -66,9 +66,10 @@ def parse():
 # the library's sources that decide what runs on the GPU: the kernels and the
 # host planner (tile groups, schedules, launch shapes)
 KERNEL_SOURCES = ("ns_gemm.hip", "elementwise.hip", "common.hpp", "launch.hpp", "capi.hip")
-# the sources each profiled kernel class is built from
-KERNEL_FILES = {"apply": ("ns_gemm.hip", "common.hpp", "launch.hpp"),
-                "gram": ("ns_gemm.hip", "common.hpp", "launch.hpp")}
+# the sources each profiled kernel class is built from, with the host planner
+# that decides its launches (tile groups, schedule, persistent mode)
+KERNEL_FILES = {"apply": ("ns_gemm.hip", "common.hpp", "launch.hpp", "capi.hip"),
+                "gram": ("ns_gemm.hip", "common.hpp", "launch.hpp", "capi.hip")}
 
 
 def source_digest(files=KERNEL_SOURCES) -> str:

@@ -134,10 +134,15 @@ struct ProbPlan {
 // formed once (the restart), after which the remaining steps run as usual
 // from an exactly formed X_R and its own Gram. In exact arithmetic every X_k
 // is the same matrix; in bf16 the restart bounds the drift between the
-// carried A_k and Q_k, and no later than step 4, as the error of the result
-// then stays at or below that of the plain steps (CPU emulation of both in
-// bf16 against float64 on Gaussian, power-law and rank-one-dominated inputs;
-// without a restart, rank-one-dominated inputs went past 2e-2). Flops per
+// carried A_k and Q_k, and no later than step 3. Rank-one-dominated inputs
+// decide where: on the GPU, 96 blocks of 1024 x 1536 .. 1024 x 14336, 2048 x
+// 4096, 2048 x 8192 and 4096 x 1024 (rank one plus 1 % and 0.1 % noise, rank
+// four plus 1 %, four seeds each) against the float64 oracle gave a worst
+// 256 x 256 tile error of 3.1e-2 with the restart at step 4 (six blocks past
+// the 2e-2 bound, all with 0.1 % noise), 1.53e-2 at step 3, 1.17e-2 at step
+// 2 and 1.56e-2 with plain steps (the 8B-shaped set: 214, 246 and 278 ms per
+// step, about 318 ms plain). Without a restart, rank-one-dominated inputs
+// went past 2e-2 in a CPU emulation of the iteration in bf16. Flops per
 // block, cubic steps S, restart R: plain 3 S m^2 n; Gram-side
 // m^2 n + (3 R - 3) m^3 + 2 m^2 n + 3 (S - R) m^2 n, fewer by
 // 3 (R - 1)(m^2 n - m^3) for every n > m. Only large blocks (mp >= GS_MIN_M)
@@ -152,7 +157,7 @@ struct ProbPlan {
 // against 1.3-1.5e-2 with plain steps, past the bf16 bound; it stays at 1024.
 // MU_GRAMSIDE=0 turns them off.
 constexpr int GS_MIN_M = 1024;
-constexpr int GS_MAX_RESTART = 4;
+constexpr int GS_MAX_RESTART = 3;
 bool gramside_enabled() {
     const char* e = std::getenv("MU_GRAMSIDE");
     return !(e && e[0] == '0');
