@@ -99,6 +99,16 @@ def test_rank_one_with_small_noise(shape, seed):
     _ortho_check(as_dtype(x, torch.bfloat16), 5, label="rank-1 + 0.1 % noise")
 
 
+def test_rank_one_with_small_noise_8b_mlp_shape():
+    """The 8B set's MLP shape: with a restart at step 4 this block reached a
+    worst 256 x 256 tile error of 2.8e-2; at step 3 it measures 1.2e-2 (worst
+    tile 1.4e-2), within the bf16 bound."""
+    m, n, seed, eps = 4096, 14336, 2, 1e-3
+    base = 70000 + 100 * seed + m + 3 * n + int(1 / eps)
+    x = np.outer(host_normal(m, base), host_normal(n, base + 1)) + eps * host_normal((m, n), base + 2)
+    _ortho_check(as_dtype(x, torch.bfloat16), 5, label="8B MLP shape, rank-1 + 0.1 % noise")
+
+
 def test_muon_step_mixed_list_on_and_off():
     """One Muon call over Gram-side blocks and plain ones (square, short, tall),
     with and without Gram-side steps: both against the oracle's O, M and W."""
